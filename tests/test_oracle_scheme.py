@@ -1,0 +1,177 @@
+"""Pins for the oracle's key switching and the operations built on it.
+
+Checks against what the mathematics fixes, never against the oracle itself:
+  * with error-free keys, KS(d) decrypts to d*s' up to the ModDown rounding
+    only: |k0 + k1*s - d*s'| <= (K/2)*(1 + h) per coefficient;
+  * decrypt(rotate_k(ct)) = slots shifted left by k (C1 tolerance 2^-12,
+    C3 parameters 2^-20), Rot_a(Rot_b) = Rot_(a+b), accumulate = ct + Rot;
+  * mul/relinearise/rescale decrypts to the slot-wise product;
+  * the BSGS matvec equals the float64 map y_o[s] = sum_c sum_t
+    D_{o,c,t}[s] * x_c[(s+t) mod n];
+  * rotate-and-sum over all power-of-two offsets gives the slot sum in every slot.
+"""
+import numpy as np
+import pytest
+
+import ckks_synth as S
+from helpers import (config_params, encrypt_slots, galois_key, params, rel_err, relin_key, secret)
+
+
+def centered_max(orc, P, limbs_ntt, level):
+    coeff = orc.ntt_params(P, limbs_ntt, inverse=True)
+    x = orc.crt_centered(coeff, P.q[: level + 1])
+    return max(abs(int(v)) for v in x)
+
+
+@pytest.mark.parametrize("level", [23, 13, 4])
+def test_keyswitch_noise_free_bound(orc, level):
+    P = config_params(orc, "C3", log_n=9)
+    h = 64
+    s, s_ntt = secret(orc, P, 5, h)
+    g = P.galois(3)
+    evk = galois_key(orc, P, s_ntt, g, 5, "ks", zero_error=True)
+    d = S.uniform_limbs(S.stream(level, "ks/d"), P.q[: level + 1], P.N)
+    k = orc.keyswitch(P, level, d, evk)
+    nq = level + 1
+    mods = P.q[:nq]
+    s_from = orc.automorph_ntt(s_ntt, P.log_n, g)[:nq]
+    # e = k0 + k1*s - d*s'
+    t1 = np.array([[int(a) * int(b) % m for a, b in zip(k[1, i], s_ntt[i])] for i, m in enumerate(mods)], dtype=np.uint64)
+    t2 = np.array([[int(a) * int(b) % m for a, b in zip(d[i], s_from[i])] for i, m in enumerate(mods)], dtype=np.uint64)
+    e = np.array([[(int(a) + int(b) - int(c)) % m for a, b, c in zip(k[0, i], t1[i], t2[i])]
+                  for i, m in enumerate(mods)], dtype=np.uint64)
+    assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h)
+
+
+def test_relin_key_noise_free_bound(orc):
+    P = config_params(orc, "C3", log_n=9)
+    level, h = 23, 64
+    s, s_ntt = secret(orc, P, 6, h)
+    rlk = relin_key(orc, P, s_ntt, 6, zero_error=True)
+    d = S.uniform_limbs(S.stream(1, "rl/d"), P.q, P.N)
+    k = orc.keyswitch(P, level, d, rlk)
+    mods = P.q
+    e = np.array([[(int(k0) + int(k1) * int(sv) - int(dv) * int(sv) * int(sv)) % m
+                   for k0, k1, sv, dv in zip(k[0, i], k[1, i], s_ntt[i], d[i])]
+                  for i, m in enumerate(mods)], dtype=np.uint64)
+    assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h)
+
+
+def c1_setup(orc, seed=1):
+    c = S.CONFIGS["C1"]
+    P = config_params(orc, "C1")
+    s, s_ntt = secret(orc, P, seed, c["h"])
+    z = S.uniform_slots(S.stream(seed, "msg"), P.N // 2, complex_values=True)
+    level = P.L - 1
+    ct = encrypt_slots(orc, P, s_ntt, z, c["scale"], level, seed, "ct")
+    return P, s_ntt, z, ct, level, c["scale"]
+
+
+@pytest.mark.parametrize("k", [1, 7])
+def test_c1_rotation_decrypts_to_shift(orc, k):
+    P, s_ntt, z, ct, level, scale = c1_setup(orc)
+    g = P.galois(k)
+    evk = galois_key(orc, P, s_ntt, g, 1, "gk%d" % k)
+    r = orc.rotate(P, level, ct, g, evk)
+    assert rel_err(orc.decrypt(P, level, r, s_ntt, scale), np.roll(z, -k)) < 2 ** -12
+
+
+def test_rotation_composition_and_accumulate(orc):
+    P, s_ntt, z, ct, level, scale = c1_setup(orc, seed=2)
+    g1, g6, g7 = P.galois(1), P.galois(6), P.galois(7)
+    k1 = galois_key(orc, P, s_ntt, g1, 2, "k1")
+    k6 = galois_key(orc, P, s_ntt, g6, 2, "k6")
+    r = orc.rotate(P, level, orc.rotate(P, level, ct, g6, k6), g1, k1)
+    assert rel_err(orc.decrypt(P, level, r, s_ntt, scale), np.roll(z, -7)) < 2 ** -11
+    acc = orc.rotate(P, level, ct, g1, k1, flags=orc.ROT_ACCUMULATE)
+    assert rel_err(orc.decrypt(P, level, acc, s_ntt, scale), z + np.roll(z, -1)) < 2 ** -11
+    # g = 1 is the identity
+    same = orc.rotate(P, level, ct, 1, k1)
+    assert np.array_equal(same, ct)
+
+
+@pytest.mark.slow
+def test_c3_parameters_rotation(orc):
+    c = S.CONFIGS["C3"]
+    P = config_params(orc, "C3")
+    s, s_ntt = secret(orc, P, 3, c["h"])
+    z = S.uniform_slots(S.stream(3, "msg"), P.N // 2, complex_values=False)
+    level = P.L - 1
+    ct = encrypt_slots(orc, P, s_ntt, z, c["scale"], level, 3, "ct")
+    k = 20001
+    g = P.galois(k)
+    evk = galois_key(orc, P, s_ntt, g, 3, "gk")
+    r = orc.rotate(P, level, ct, g, evk)
+    assert rel_err(orc.decrypt(P, level, r, s_ntt, c["scale"]), np.roll(z, -k)) < 2 ** -20
+
+
+@pytest.mark.parametrize("log_n", [10, 12])
+def test_mul_relin_rescale_decrypts_to_product(orc, log_n):
+    c = S.CONFIGS["C5"]
+    P = config_params(orc, "C5", log_n=log_n)
+    s, s_ntt = secret(orc, P, 4, c["h"])
+    level = P.L - 1
+    n = P.N // 2
+    za = S.uniform_slots(S.stream(4, "za"), n, complex_values=False)
+    zb = S.uniform_slots(S.stream(4, "zb"), n, complex_values=False)
+    scale = c["scale"]
+    a = encrypt_slots(orc, P, s_ntt, za, scale, level, 4, "a")
+    b = encrypt_slots(orc, P, s_ntt, zb, scale, level, 4, "b")
+    rlk = relin_key(orc, P, s_ntt, 4)
+    pre = orc.mul_relin_rescale(P, level, a[None], b[None], rlk, flags=orc.NO_RESCALE)[0]
+    assert rel_err(orc.decrypt(P, level, pre, s_ntt, scale * scale), za * zb) < 2 ** -20
+    post = orc.mul_relin_rescale(P, level, a[None], b[None], rlk)[0]
+    assert post.shape == (2, level, P.N)
+    assert np.array_equal(post, orc.rescale(P, level, pre))
+    assert rel_err(orc.decrypt(P, level - 1, post, s_ntt, scale * scale / P.q[level]), za * zb) < 2 ** -12
+
+
+def test_ptmatvec_matches_float_map(orc):
+    P = config_params(orc, "C4", log_n=10)
+    n = P.N // 2
+    level, n_in, n_out, n1, n2 = 12, 2, 2, 4, 4
+    s, s_ntt = secret(orc, P, 9, 64)
+    scale = 2.0 ** 40
+    rng = S.stream(9, "pmv/x")
+    xs = [S.uniform_slots(rng, n, complex_values=False) for _ in range(n_in)]
+    x = np.stack([encrypt_slots(orc, P, s_ntt, xs[c], scale, level, 9, "x%d" % c) for c in range(n_in)])
+    D = S.normal_values(S.stream(9, "pmv/D"), (n_out, n_in, n1 * n2, n), 0.02)
+    diags = np.empty((n_out, n_in, n2, n1, level + 1, P.N), dtype=np.uint64)
+    for o in range(n_out):
+        for c in range(n_in):
+            for g in range(n2):
+                for b in range(n1):
+                    pre = np.roll(D[o, c, n1 * g + b], n1 * g)  # Rot_{-n1 g}
+                    diags[o, c, g, b] = orc.encode(P, pre, scale, level)
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [galois_key(orc, P, s_ntt, g, 9, "kb%d" % i) for i, g in enumerate(gb)]
+    kg = [galois_key(orc, P, s_ntt, g, 9, "kg%d" % i) for i, g in enumerate(gg)]
+    y_pre = orc.ptmatvec(P, level, x, diags, gb, kb, gg, kg, flags=orc.NO_RESCALE)
+    y = orc.ptmatvec(P, level, x, diags, gb, kb, gg, kg)
+    for o in range(n_out):
+        ref = np.zeros(n)
+        for c in range(n_in):
+            for t in range(n1 * n2):
+                ref += D[o, c, t] * np.roll(xs[c].real, -t)
+        assert rel_err(orc.decrypt(P, level, y_pre[o], s_ntt, scale * scale).real, ref) < 2 ** -20
+        assert np.array_equal(y[o], orc.rescale(P, level, y_pre[o]))
+        assert rel_err(orc.decrypt(P, level - 1, y[o], s_ntt, scale * scale / P.q[level]).real, ref) < 2 ** -10
+    # sampling a sub-range gives the same words
+    y1 = orc.ptmatvec(P, level, x, diags, gb, kb, gg, kg, o_range=(1, 2))
+    assert np.array_equal(y1[1], y[1])
+
+
+def test_rotate_and_sum_gives_slot_sum(orc):
+    P = config_params(orc, "C5", log_n=10)
+    n = P.N // 2
+    s, s_ntt = secret(orc, P, 8, 64)
+    level, scale = 22, 2.0 ** 40
+    z = S.uniform_slots(S.stream(8, "rs"), n, complex_values=False)
+    ct = encrypt_slots(orc, P, s_ntt, z, scale, level, 8, "ct")
+    steps = n.bit_length() - 1
+    for k in range(steps):
+        g = P.galois(1 << k)
+        ct = orc.rotate(P, level, ct, g, galois_key(orc, P, s_ntt, g, 8, "r%d" % k), flags=orc.ROT_ACCUMULATE)
+    dec = orc.decrypt(P, level, ct, s_ntt, scale).real
+    assert np.max(np.abs(dec - z.sum())) / np.sum(np.abs(z)) < 2 ** -20
