@@ -1,0 +1,182 @@
+/*
+ * ckks.h -- C ABI of the MI355X (gfx950) RNS-CKKS rotation hot-path library
+ * (libckks_mi355x.so).
+ *
+ * What it computes.  The AEGIS pages on gist.science ("Problem" section,
+ * challenges 2 and 3; "Methodology", communication hiding) state that
+ * encrypted Transformer inference runs CKKS over a residue number system and
+ * that key switching and rotation, needed by every matrix product and
+ * non-linear layer, dominate the work; the FFN layer does local polynomial
+ * multiplication and attention computes Q x K^T ("Methodology", items 2 and
+ * 3).  The pages give no formula, so every call follows the standard full-RNS
+ * CKKS construction with hybrid key switching (Cheon-Kim-Kim-Song 2017;
+ * Cheon-Han-Kim-Kim-Song 2018; Han-Ki 2020; fast basis conversion of
+ * Bajard-Eynard-Hasan-Zucca 2016; diagonal matvec of Halevi-Shoup 2014).
+ *
+ * Conventions shared by every call
+ *   Words      uint64, one residue per word, fully reduced to [0, m) on entry
+ *              and on exit.  Inputs with a word >= its modulus are undefined.
+ *   Basis      q_0 .. q_{L-1} (ciphertext primes), then p_0 .. p_{K-1}
+ *              (special primes).  A level-l polynomial holds limbs q_0..q_l.
+ *   Limb       N consecutive words (one residue polynomial); arrays are
+ *              limb-major: [..][limb][N].
+ *   NTT form   word j of a limb is the polynomial evaluated at
+ *              psi^(2*brv(j)+1) (bit-reversed evaluation order), psi the
+ *              limb's 2N-th root of unity (by default the smallest primitive
+ *              one).  Ciphertexts, keys and plaintexts are in NTT form.
+ *   Ciphertext [2][l+1][N]: component 0 = c0, component 1 = c1; decryption
+ *              is c0 + c1*s.
+ *   Switch key [dnum][2][L+K][N]: digit j, component 0 = b, 1 = a, with
+ *              b_j + a_j*s = e_j + [P]_{m_t} * s' on the limbs t of digit j
+ *              (digit j = q_{j*alpha} .. q_{(j+1)*alpha-1}, alpha =
+ *              ceil(L/dnum)) and b_j + a_j*s = e_j elsewhere; P = prod p_k.
+ *              At level l the same key is used with limbs l+1..L-1 skipped.
+ *   Galois     elements are odd integers in [1, 2N); X -> X^g.  The library
+ *              has no slot convention: a left rotation by k slots in the
+ *              usual encoding is g = 5^k mod 2N.
+ *   Memory     d_* arguments are device pointers (HIP), owned by the caller,
+ *              not retained after the call's stream work completes.  Host
+ *              arrays (galois element lists, key pointer lists) are read
+ *              before the call returns.
+ *   Streams    every compute call enqueues on `stream` and returns; outputs
+ *              are valid after the stream is synchronised.  A context is not
+ *              thread-safe: use one context per host thread / stream.
+ *   Aliasing   ckks_ntt works in place; every other call requires its
+ *              outputs not to overlap its inputs.
+ *   Errors     every call returns CKKS_OK (0) or a negative CKKS_E* code; a
+ *              detail string is kept per host thread (ckks_last_error).  No
+ *              C++ exception crosses this interface.  On error no output is
+ *              written unless the code is CKKS_EHIP (a failed launch may
+ *              leave outputs partially written).
+ */
+#ifndef CKKS_MI355X_H
+#define CKKS_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* ckks_stream_t; /* a hipStream_t; NULL = the null stream */
+
+enum {
+  CKKS_OK = 0,
+  CKKS_EINVAL = -1,    /* null pointer, bad count, even or out-of-range Galois element */
+  CKKS_ERANGE = -2,    /* level out of range, rescale at level 0, limb range outside the basis */
+  CKKS_ENOMEM = -3,    /* device or host allocation failed */
+  CKKS_EHIP = -4,      /* HIP launch or API failure */
+  CKKS_EPARAM = -5,    /* invalid parameter set */
+  CKKS_EINTERNAL = -6  /* internal error */
+};
+
+/* flags */
+#define CKKS_ROT_ACCUMULATE 1u /* ckks_rotate: out = in + Rot(in) */
+#define CKKS_NO_RESCALE 2u     /* ckks_mul_relin_rescale / ckks_ptmatvec: keep level l */
+
+typedef struct ckks_ctx ckks_ctx;
+
+typedef struct {
+  uint32_t log_n;      /* N = 2^log_n, 10 <= log_n <= 16 */
+  uint32_t n_q;        /* L: ciphertext primes, 1..64 */
+  uint32_t n_p;        /* K: special primes, 0..16; when K > 0, K == ceil(L/dnum) */
+  uint32_t dnum;       /* gadget digits, 1..L; when K > 0, ceil(L/dnum) <= 16 */
+  const uint64_t* q;   /* host [n_q]: distinct primes, each = 1 mod 2N, < 2^62 */
+  const uint64_t* p;   /* host [n_p]: distinct primes, each = 1 mod 2N, < 2^62 */
+  const uint64_t* psi; /* host [n_q+n_p] primitive 2N-th roots, or NULL = smallest ones */
+} ckks_params;
+
+/* ---- host-only set-up (no GPU needed) ---------------------------------- */
+
+/* The `count` largest primes below 2^bits that are 1 mod 2^(log_n+1), in
+ * descending order, written to out[count] (host).  bits in [log_n+2, 62].
+ * Parameter set-up for the benchmark parameter reading (largest NTT-friendly
+ * primes); CKKS_EPARAM if fewer exist. */
+int ckks_find_primes(uint32_t log_n, uint32_t bits, uint32_t count, uint64_t* out);
+
+/* Checks a parameter set: sizes, primality (deterministic Miller-Rabin),
+ * q = 1 mod 2N, distinctness, the K == ceil(L/dnum) rule and, when given,
+ * that each psi is a primitive 2N-th root.  Returns CKKS_OK or CKKS_EPARAM. */
+int ckks_params_validate(const ckks_params* params);
+
+const char* ckks_strerror(int status);
+const char* ckks_last_error(void); /* detail of this thread's last failure ("" if none) */
+
+/* ---- context ------------------------------------------------------------- */
+
+/* Validates params, selects HIP device `hip_device`, and uploads the
+ * per-prime twiddle tables and basis-conversion constants.  *out owns that
+ * device memory plus a workspace grown on demand. */
+int ckks_ctx_create(const ckks_params* params, int hip_device, ckks_ctx** out);
+int ckks_ctx_destroy(ckks_ctx* ctx);
+/* The roots in use (n_q+n_p values, host). */
+int ckks_ctx_psi(const ckks_ctx* ctx, uint64_t* out);
+
+/* ---- hot path ------------------------------------------------------------ */
+
+/* Negacyclic NTT (inverse = 0) or inverse NTT with the 1/N factor
+ * (inverse = 1), in place, on d_data = [npoly][n_limb][N]; limb i of every
+ * polynomial uses basis prime limb_begin + i.  Forward maps coefficient form
+ * to NTT form (bit-reversed evaluation order), inverse maps back.
+ * CKKS_ERANGE if limb_begin + n_limb exceeds L+K. */
+int ckks_ntt(ckks_ctx* ctx, uint64_t* d_data, int npoly, int limb_begin, int n_limb, int inverse,
+             ckks_stream_t stream);
+
+/* Galois automorphism X -> X^g on d_in = [npoly][level+1][N] (limbs
+ * q_0..q_level) into d_out (same shape).  domain 0: NTT form (a permutation
+ * of words); domain 1: coefficient form (a signed permutation). */
+int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npoly, int level, uint32_t galois_elt,
+                   int domain, ckks_stream_t stream);
+
+/* Hybrid key switch of d_poly ([level+1][N], NTT form) with the switch key
+ * d_evk ([dnum][2][L+K][N]) into d_out ([2][level+1][N], NTT form):
+ * per active digit, ModUp (unsigned fast basis conversion to the other limbs
+ * and the special primes), NTT, inner product with the key digit, then
+ * ModDown (centered conversion of the special part, multiply by P^-1).
+ * Requires K > 0. */
+int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk, uint64_t* d_out, int level,
+                   ckks_stream_t stream);
+
+/* Batched homomorphic rotation: for b < batch, ciphertext b of d_ct_in
+ * ([batch][2][level+1][N]) is mapped by Galois element galois_elts[b]
+ * (host array) and key-switched back with the switch key d_evks[b] (host
+ * array of device pointers, each [dnum][2][L+K][N], the key for
+ * tau_g(s) -> s): out = (tau_g(c0) + k0, k1), (k0, k1) = KS(tau_g(c1)).
+ * galois element 1 is the identity (copy, no key read; its key pointer may
+ * be NULL).  With CKKS_ROT_ACCUMULATE, out = in + Rot(in). */
+int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream);
+
+/* Rescale (divide by q_level, rounding to nearest) of d_in
+ * ([batch][2][level+1][N]) into d_out ([batch][2][level][N]).
+ * CKKS_ERANGE at level 0. */
+int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch, int level, ckks_stream_t stream);
+
+/* Batched ciphertext product: tensor (d0 = a0 b0, d1 = a0 b1 + a1 b0,
+ * d2 = a1 b1), relinearisation with d_rlk (switch key s^2 -> s):
+ * (d0, d1) + KS(d2), then rescale.  d_a, d_b: [batch][2][level+1][N];
+ * d_out: [batch][2][level][N], or [batch][2][level+1][N] with
+ * CKKS_NO_RESCALE.  Requires K > 0; CKKS_ERANGE when rescaling at level 0. */
+int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d_b, const uint64_t* d_rlk,
+                           uint64_t* d_out, int batch, int level, unsigned flags, ckks_stream_t stream);
+
+/* Baby-step / giant-step ciphertext x plaintext matrix-vector product.
+ *   d_x      [n_in][2][level+1][N] input ciphertexts
+ *   d_diags  [n_out][n_in][n2][n1][level+1][N] plaintexts (NTT form); entry
+ *            (o, c, g, b) is the diagonal for offset n1*g + b, already
+ *            rotated by the inverse of giant step g
+ *   baby     n1-1 Galois elements / switch keys for the baby steps 1..n1-1
+ *   giant    n2-1 Galois elements / switch keys for the giant steps 1..n2-1
+ *   d_y      [n_out][2][level][N] (level+1 with CKKS_NO_RESCALE)
+ * y_o = sum_g Rot_g( sum_c sum_b diag(o,c,g,b) * Rot_b(x_c) ), then rescale.
+ * The baby-step rotations are computed once and shared by all outputs. */
+int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
+                  const uint32_t* baby_galois, const uint64_t* const* d_evk_baby, const uint32_t* giant_galois,
+                  const uint64_t* const* d_evk_giant, uint64_t* d_y, int level, unsigned flags,
+                  ckks_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKKS_MI355X_H */

@@ -1,0 +1,103 @@
+// Argument blocks and launchers of the non-NTT kernels.  Strides are in
+// 64-bit words; `*_bstride` is the distance between consecutive batch items.
+#pragma once
+#include "internal.h"
+
+namespace ckks {
+
+constexpr int kMaxChunk = 8;  // batch items per launch of the key-switch pipeline
+
+struct ModUpArgs {
+  const uint64_t* x;    // coefficient form (no 1/N), [level+1][N] per item
+  uint64_t* out;        // [beta][next][N] per item
+  uint64_t x_bstride, out_bstride;
+  const uint64_t* tables;
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, next, L;
+  int lo[64], hi[64];
+  uint64_t offset[64];
+};
+
+struct IPArgs {
+  const uint64_t* d;    // NTT-form input, [level+1][N] per item
+  const uint64_t* ext;  // NTT-form ModUp output, [beta][next][N] per item
+  uint64_t* acc;        // [2][next][N] per item
+  uint64_t d_bstride, ext_bstride, acc_bstride;
+  const uint64_t* evk[kMaxChunk];  // [dnum][2][L+K][N]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, next, beta, alpha, L, K;
+};
+
+struct ModDownArgs {
+  const uint64_t* acc;  // [2][next][N] per item; special limbs in coefficient form (no 1/N)
+  uint64_t* w;          // [2][level+1][N] per item (coefficient form)
+  uint64_t acc_bstride, w_bstride;
+  const uint64_t* phinv;  // [K][2]
+  const uint64_t* conv;   // [K][L]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, next, L, K;
+};
+
+struct CombineArgs {
+  const uint64_t* acc;  // [2][next][N] per item (NTT form)
+  const uint64_t* w;    // [2][level+1][N] per item (NTT form)
+  const uint64_t* add[2];    // optional [level+1][N] per item per component
+  const uint64_t* accum;     // optional [2][level+1][N] per item
+  uint64_t* out;             // [2][out_comp_limbs][N] per item
+  uint64_t acc_bstride, w_bstride, add_bstride, accum_bstride, out_bstride;
+  uint32_t add_g[kMaxChunk];  // gather `add` through X -> X^g (0 = none)
+  const uint64_t* pinv;       // [L][2]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, next, out_comp_limbs, log_n;
+};
+
+struct RescaleArgs {
+  const uint64_t* ct;  // [2][level+1][N] per item
+  const uint64_t* v;   // [2][N] per item: iNTT of limb `level`
+  uint64_t* w;         // [2][level][N] per item
+  uint64_t* out;       // [2][level][N] per item
+  uint64_t ct_bstride, v_bstride, w_bstride, out_bstride;
+  const uint64_t* tab;  // rescale constants [L][L][4]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, L;
+};
+
+struct TensorArgs {
+  const uint64_t *a, *b;  // [2][level+1][N] per item
+  uint64_t* out;          // [3][level+1][N] per item
+  uint64_t in_bstride, out_bstride;
+  const PrimeConst* prime;
+  uint32_t n;
+  int level;
+};
+
+struct PtMacArgs {
+  const uint64_t* diags;  // [n_out][n_in][n2][n1][level+1][N]
+  const uint64_t* baby;   // [n1][n_in][2][level+1][N]
+  uint64_t* out;          // [n_out][n2][2][level+1][N]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, n_in, n1, n2;
+};
+
+int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl, uint64_t pstride,
+                         uint32_t g);
+int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl,
+                           uint64_t pstride, uint32_t ginv);
+int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch);
+int launch_inner_product(Ctx* c, hipStream_t s, IPArgs& a, int batch);
+int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch);
+int launch_combine(Ctx* c, hipStream_t s, CombineArgs& a, int batch);
+int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
+int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
+int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);
+int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
+int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
+               int ncomp, uint64_t bstride);
+
+}  // namespace ckks

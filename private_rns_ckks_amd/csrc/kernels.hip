@@ -1,0 +1,319 @@
+// Non-NTT kernels of the hot path: Galois automorphism, ModUp and ModDown
+// basis conversion, the key-switch inner product, the final combination
+// steps, rescale, ciphertext tensor product and the plaintext MAC.
+//
+// All kernels are elementwise over the N coefficients of a limb: one thread
+// per coefficient, blockIdx.x over coefficient tiles of 256, blockIdx.y over
+// limbs (or digits / components), blockIdx.z over batch items.  Limb-major
+// layout makes every load and store a contiguous 64-bit access per lane.
+#include "arith.h"
+#include "kernels.h"
+
+namespace ckks {
+
+namespace {
+
+// Index in the NTT-form input whose word lands at position j after X -> X^g:
+// word j holds a(psi^(2brv(j)+1)); the image holds a(psi^(g(2brv(j)+1))).
+__device__ __forceinline__ uint32_t automorph_src(uint32_t j, uint32_t g, int log_n) {
+  const uint32_t mask2n = (2u << log_n) - 1;
+  const uint32_t e = 2 * (__brev(j) >> (32 - log_n)) + 1;
+  const uint32_t eg = (e * g) & mask2n;
+  return __brev((eg - 1) >> 1) >> (32 - log_n);
+}
+
+__global__ void automorph_ntt_kernel(const uint64_t* in, uint64_t* out, uint64_t pstride, uint32_t g, int log_n) {
+  const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t base = blockIdx.z * pstride + ((uint64_t)blockIdx.y << log_n);
+  out[base + j] = in[base + automorph_src(j, g, log_n)];
+}
+
+// Coefficient form: output coefficient r takes input coefficient u = r/g mod 2N,
+// negated when u >= N (X^N = -1).
+__global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64_t pstride, uint32_t ginv, int log_n,
+                                       const PrimeConst* pc) {
+  const uint32_t r = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t n = 1u << log_n;
+  const uint64_t base = blockIdx.z * pstride + ((uint64_t)blockIdx.y << log_n);
+  const uint32_t u = (r * ginv) & (2 * n - 1);
+  const uint64_t q = pc[blockIdx.y].q;
+  if (u < n) {
+    out[base + r] = in[base + u];
+  } else {
+    const uint64_t v = in[base + u - n];
+    out[base + r] = v ? q - v : 0;
+  }
+}
+
+// ModUp for digit blockIdx.y of batch item blockIdx.z.
+// x: coefficient form WITHOUT the 1/N factor (folded into the constants),
+// [level+1][N] per item.  out: [beta][next][N] per item; columns inside the
+// digit are left untouched.
+__global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int j = blockIdx.y;
+  const int lo = a.lo[j], hi = a.hi[j], na = hi - lo;
+  const uint64_t* tab = a.tables + a.offset[j];
+  const uint64_t* x = a.x + blockIdx.z * a.x_bstride + c;
+  uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
+  uint64_t y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < na) {
+      const uint64_t q = a.prime[lo + i].q;
+      y[i] = reduce_2q(mul_shoup(x[(uint64_t)(lo + i) * a.n], tab[2 * i], tab[2 * i + 1], q), q);
+    }
+  }
+  const uint64_t* conv = tab + 2 * na;
+  for (int t = 0; t < a.next; ++t) {
+    if (t >= lo && t < hi) continue;
+    const PrimeConst pc = a.prime[t <= a.level ? t : a.L + (t - a.level - 1)];
+    U128 acc = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < na) mac(acc, y[i], conv[i * a.next + t]);
+    out[(uint64_t)t * a.n] = reduce128(acc, pc.q, pc.r64, pc.r64p, pc.inv1);
+  }
+}
+
+// Inner product with the key digits for extended limb t = blockIdx.y:
+// acc_b[t] = sum_j d_j[t] * evk_j.b[t], acc_a[t] likewise, where d_j[t] is the
+// NTT-form input itself for limbs inside digit j and the NTT-form ModUp output
+// otherwise.
+__global__ __launch_bounds__(256) void inner_product_kernel(IPArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = blockIdx.y;
+  const int item = blockIdx.z;
+  const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
+  const PrimeConst pc = a.prime[keyl];
+  const uint64_t* evk = a.evk[item];
+  const uint64_t LKN = (uint64_t)(a.L + a.K) * a.n;
+  U128 ab = {0, 0}, aa = {0, 0};
+  for (int j = 0; j < a.beta; ++j) {
+    const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
+    const uint64_t d = in_digit ? a.d[item * a.d_bstride + (uint64_t)t * a.n + c]
+                                : a.ext[item * a.ext_bstride + ((uint64_t)j * a.next + t) * a.n + c];
+    const uint64_t kb = evk[(2 * j) * LKN + (uint64_t)keyl * a.n + c];
+    const uint64_t ka = evk[(2 * j + 1) * LKN + (uint64_t)keyl * a.n + c];
+    mac(ab, d, kb);
+    mac(aa, d, ka);
+  }
+  uint64_t* out = a.acc + item * a.acc_bstride + (uint64_t)t * a.n + c;
+  out[0] = reduce128(ab, pc.q, pc.r64, pc.r64p, pc.inv1);
+  out[(uint64_t)a.next * a.n] = reduce128(aa, pc.q, pc.r64, pc.r64p, pc.inv1);
+}
+
+// ModDown conversion for component blockIdx.y of item blockIdx.z.
+// z_k: special limbs of acc in coefficient form without 1/N.
+// y_k = z_k * [phat_k^-1 N^-1]_{p_k}; negative when y_k > (p_k-1)/2 (centered lift).
+// w_i = sum_k y_k * [1/p_k]_{q_i} - (#negative) mod q_i  (= centered conversion times P^-1).
+__global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int comp = blockIdx.y;
+  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)comp * a.next * a.n + c;
+  uint64_t y[16];
+  uint32_t neg = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k < a.K) {
+      const uint64_t p = a.prime[a.L + k].q;
+      uint64_t v = acc[(uint64_t)(a.level + 1 + k) * a.n];
+      v = reduce_2q(mul_shoup(v, a.phinv[2 * k], a.phinv[2 * k + 1], p), p);
+      neg += v > (p - 1) / 2 ? 1u : 0u;
+      y[k] = v;
+    }
+  }
+  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * (a.level + 1) * a.n + c;
+  for (int i = 0; i <= a.level; ++i) {
+    const PrimeConst pc = a.prime[i];
+    U128 s = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < a.K) mac(s, y[k], a.conv[k * a.L + i]);
+    const uint64_t r = reduce128(s, pc.q, pc.r64, pc.r64p, pc.inv1);
+    w[(uint64_t)i * a.n] = sub_mod(r, neg, pc.q);
+  }
+}
+
+// out[comp][i] = acc[comp][i] * P^-1 - w[comp][i]  (+ add[comp][i] gathered
+// through X -> X^g when add_g != 0)  (+ accum[comp][i]).
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y;
+  const int item = blockIdx.z;
+  const PrimeConst pc = a.prime[i];
+  const uint64_t q = pc.q;
+  for (int comp = 0; comp < 2; ++comp) {
+    const uint64_t av = a.acc[item * a.acc_bstride + ((uint64_t)comp * a.next + i) * a.n + c];
+    const uint64_t wv = a.w[item * a.w_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c];
+    uint64_t r = sub_mod(reduce_2q(mul_shoup(av, a.pinv[2 * i], a.pinv[2 * i + 1], q), q), wv, q);
+    if (a.add[comp]) {
+      const uint32_t g = a.add_g[item];
+      const uint32_t src = g ? automorph_src(c, g, a.log_n) : c;
+      r = add_mod(r, a.add[comp][item * a.add_bstride + (uint64_t)i * a.n + src], q);
+    }
+    if (a.accum) r = add_mod(r, a.accum[item * a.accum_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c], q);
+    a.out[item * a.out_bstride + ((uint64_t)comp * a.out_comp_limbs + i) * a.n + c] = r;
+  }
+}
+
+// Rescale, step 1: v = iNTT(c[l]) (canonical, 1/N applied) for both components;
+// w_i = (vbar mod q_i) * [q_l^-1]_{q_i}, vbar the centered lift of v.
+__global__ __launch_bounds__(256) void rescale_prep_kernel(RescaleArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int comp = blockIdx.y;
+  const uint64_t v = a.v[blockIdx.z * a.v_bstride + (uint64_t)comp * a.n + c];
+  const uint64_t ql = a.prime[a.level].q;
+  const bool neg = v > (ql - 1) / 2;
+  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * a.level * a.n + c;
+  for (int i = 0; i < a.level; ++i) {
+    const PrimeConst pc = a.prime[i];
+    const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
+    uint64_t t = v >= pc.q ? reduce64(v, pc.q, pc.inv1) : v;
+    if (neg) t = sub_mod(t, rs[2], pc.q);
+    w[(uint64_t)i * a.n] = reduce_2q(mul_shoup(t, rs[0], rs[1], pc.q), pc.q);
+  }
+}
+
+// Rescale, step 2: out_i = c_i * [q_l^-1]_{q_i} - NTT(w)_i.
+__global__ __launch_bounds__(256) void rescale_combine_kernel(RescaleArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y;
+  const PrimeConst pc = a.prime[i];
+  const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
+  for (int comp = 0; comp < 2; ++comp) {
+    const uint64_t cv = a.ct[blockIdx.z * a.ct_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c];
+    const uint64_t wv = a.w[blockIdx.z * a.w_bstride + ((uint64_t)comp * a.level + i) * a.n + c];
+    a.out[blockIdx.z * a.out_bstride + ((uint64_t)comp * a.level + i) * a.n + c] =
+        sub_mod(reduce_2q(mul_shoup(cv, rs[0], rs[1], pc.q), pc.q), wv, pc.q);
+  }
+}
+
+// d0 = a0 b0, d1 = a0 b1 + a1 b0, d2 = a1 b1 on limb blockIdx.y.
+__global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y;
+  const PrimeConst pc = a.prime[i];
+  const uint64_t lim = (uint64_t)(a.level + 1) * a.n;
+  const uint64_t off = (uint64_t)i * a.n + c;
+  const uint64_t* x = a.a + blockIdx.z * a.in_bstride;
+  const uint64_t* y = a.b + blockIdx.z * a.in_bstride;
+  uint64_t* d = a.out + blockIdx.z * a.out_bstride;
+  const uint64_t a0 = x[off], a1 = x[lim + off], b0 = y[off], b1 = y[lim + off];
+  d[off] = mul_mod(a0, b0, pc.q, pc.r64, pc.r64p, pc.inv1);
+  U128 m = {0, 0};
+  mac(m, a0, b1);
+  mac(m, a1, b0);
+  d[lim + off] = reduce128(m, pc.q, pc.r64, pc.r64p, pc.inv1);
+  d[2 * lim + off] = mul_mod(a1, b1, pc.q, pc.r64, pc.r64p, pc.inv1);
+}
+
+// BSGS inner sums: inner[o][g][comp][i] = sum_c sum_b diag[o][c][g][b][i] * baby[b][c][comp][i].
+// blockIdx.y = limb i, blockIdx.z = o * n2 + g.
+__global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y;
+  const int o = blockIdx.z / a.n2, g = blockIdx.z % a.n2;
+  const PrimeConst pc = a.prime[i];
+  const uint64_t limbs = (uint64_t)(a.level + 1);
+  const uint64_t off = (uint64_t)i * a.n + c;
+  U128 s0 = {0, 0}, s1 = {0, 0};
+  for (int ci = 0; ci < a.n_in; ++ci) {
+    for (int b = 0; b < a.n1; ++b) {
+      const uint64_t pt = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * limbs * a.n + off];
+      const uint64_t* ct = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * limbs * a.n;
+      mac(s0, pt, ct[off]);
+      mac(s1, pt, ct[limbs * a.n + off]);
+    }
+  }
+  uint64_t* out = a.out + (uint64_t)blockIdx.z * 2 * limbs * a.n;
+  out[off] = reduce128(s0, pc.q, pc.r64, pc.r64p, pc.inv1);
+  out[limbs * a.n + off] = reduce128(s1, pc.q, pc.r64, pc.r64p, pc.inv1);
+}
+
+// out = x + y on [nl] limbs per item (limb i uses prime i).
+__global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, uint64_t bstride, int nl,
+                           const PrimeConst* prime, int log_n) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y % nl;
+  const uint64_t off = blockIdx.z * bstride + ((uint64_t)blockIdx.y << log_n) + c;
+  out[off] = add_mod(x[off], y[off], prime[i].q);
+}
+
+}  // namespace
+
+#define LAUNCH_CHECK() CKKS_HIP_CHECK(hipGetLastError())
+
+int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl, uint64_t pstride,
+                         uint32_t g) {
+  hipLaunchKernelGGL(automorph_ntt_kernel, dim3(c->N / 256, nl, npoly), dim3(256), 0, s, in, out, pstride, g,
+                     (int)c->log_n);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl,
+                           uint64_t pstride, uint32_t ginv) {
+  hipLaunchKernelGGL(automorph_coeff_kernel, dim3(c->N / 256, nl, npoly), dim3(256), 0, s, in, out, pstride, ginv,
+                     (int)c->log_n, c->d_prime);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch) {
+  hipLaunchKernelGGL(modup_kernel, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_inner_product(Ctx* c, hipStream_t s, IPArgs& a, int batch) {
+  hipLaunchKernelGGL(inner_product_kernel, dim3(c->N / 256, a.next, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
+  hipLaunchKernelGGL(moddown_conv_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_combine(Ctx* c, hipStream_t s, CombineArgs& a, int batch) {
+  hipLaunchKernelGGL(combine_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
+  hipLaunchKernelGGL(rescale_prep_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
+  hipLaunchKernelGGL(rescale_combine_kernel, dim3(c->N / 256, a.level, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
+  hipLaunchKernelGGL(tensor_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
+  hipLaunchKernelGGL(ptmac_kernel, dim3(c->N / 256, a.level + 1, n_out * a.n2), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
+               int ncomp, uint64_t bstride) {
+  hipLaunchKernelGGL(add_kernel, dim3(c->N / 256, nl * ncomp, npoly), dim3(256), 0, s, x, y, out, bstride, nl,
+                     c->d_prime, (int)c->log_n);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+}  // namespace ckks

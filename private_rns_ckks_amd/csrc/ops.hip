@@ -1,0 +1,515 @@
+// Host orchestration of the hot path and the C ABI compute entry points.
+//
+// Hybrid key switch of one polynomial d at level l (per batch item):
+//   1. (rotation only) T = tau_g(c1) in NTT form (a permutation of words)
+//   2. C = iNTT(T) without the 1/N factor (folded into the ModUp constants)
+//   3. ModUp: for each digit j, unsigned fast basis conversion of the digit's
+//      limbs of C to every other limb of the extended basis q_0..q_l, p_*
+//   4. forward NTT of the converted limbs
+//   5. inner product with the key digits (digit limbs use T directly), one
+//      128-bit accumulation and one reduction per output word
+//   6. iNTT of the special-prime limbs of both accumulators (no 1/N)
+//   7. ModDown conversion: centered lift, times P^-1 folded into the constants
+//   8. forward NTT of the converted limbs
+//   9. out = acc * P^-1 - w (+ tau_g(c0), + the input for accumulation)
+// Batch items are processed in chunks so the intermediates of a chunk stay
+// resident in the last-level cache (the 256 MiB Infinity Cache) between the
+// steps instead of round-tripping through HBM for the whole batch.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+
+namespace ckks {
+
+namespace {
+
+int g_chunk_default() {
+  static int v = [] {
+    const char* e = getenv("CKKS_CHUNK");
+    int x = e ? atoi(e) : 4;
+    return std::max(1, std::min(x, kMaxChunk));
+  }();
+  return v;
+}
+
+struct KSItem {
+  const uint64_t* d;       // NTT-form input polynomial [level+1][N]
+  uint32_t g;              // automorphism applied to d before switching (0 = none)
+  const uint64_t* evk;     // [dnum][2][L+K][N]
+  const uint64_t* add[2];  // added to output component (gathered through add_g when add_g != 0)
+  uint32_t add_g;
+  const uint64_t* accum;   // [2][level+1][N] added to the output, or NULL
+  uint64_t* out;           // [2][out_comp_limbs][N]
+};
+
+// Workspace words per item for the key-switch pipeline at `level`.
+size_t ks_ws_words(const Ctx* c, int level) {
+  const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
+  return n * (nq /*T*/ + nq /*C*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
+}
+
+// Run the key-switch pipeline on up to kMaxChunk items whose external buffers
+// share one stride (item i at base + i*stride), with `ws` as scratch.
+int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
+             uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
+  const uint32_t N = c->N;
+  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
+  const uint64_t per = ks_ws_words(c, level);
+  uint64_t* T = ws;
+  uint64_t* C = T + (uint64_t)nq * N;
+  uint64_t* E = C + (uint64_t)nq * N;
+  uint64_t* A = E + (uint64_t)beta * next * N;
+  uint64_t* W = A + (uint64_t)2 * next * N;
+  int rc;
+  // 1. automorphism of the input (rotation)
+  const uint64_t* Tsrc = it[0].d;
+  uint64_t T_stride = d_stride;
+  if (it[0].g) {
+    for (int i = 0; i < n_items; ++i)
+      if ((rc = launch_automorph_ntt(c, s, it[i].d, T + i * per, 1, nq, 0, it[i].g))) return rc;
+    Tsrc = T;
+    T_stride = per;
+  }
+  // 2. iNTT to coefficient form (no 1/N)
+  NttJobs jobs;
+  for (int i = 0; i < nq; ++i) jobs.add(i, i, i);
+  if ((rc = ntt_run(c, s, Tsrc, C, T_stride, per, n_items, jobs, true, false))) return rc;
+  // 3. ModUp
+  ModUpArgs mu;
+  memset(&mu, 0, sizeof(mu));
+  mu.x = C;
+  mu.out = E;
+  mu.x_bstride = per;
+  mu.out_bstride = per;
+  mu.tables = c->d_modup;
+  mu.prime = c->d_prime;
+  mu.n = N;
+  mu.level = level;
+  mu.next = next;
+  mu.L = (int)c->L;
+  for (int j = 0; j < beta; ++j) {
+    const ModUpEntry& en = c->modup[level][j];
+    mu.lo[j] = en.lo;
+    mu.hi[j] = en.hi;
+    mu.offset[j] = en.offset;
+  }
+  if ((rc = launch_modup(c, s, mu, beta, n_items))) return rc;
+  // 4. NTT of the converted limbs
+  jobs.n = 0;
+  for (int j = 0; j < beta; ++j)
+    for (int t = 0; t < next; ++t) {
+      if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
+      jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
+    }
+  if ((rc = ntt_run(c, s, E, E, per, per, n_items, jobs, false, false))) return rc;
+  // 5. inner product
+  IPArgs ip;
+  memset(&ip, 0, sizeof(ip));
+  ip.d = Tsrc;
+  ip.ext = E;
+  ip.acc = A;
+  ip.d_bstride = T_stride;
+  ip.ext_bstride = per;
+  ip.acc_bstride = per;
+  for (int i = 0; i < n_items; ++i) ip.evk[i] = it[i].evk;
+  ip.prime = c->d_prime;
+  ip.n = N;
+  ip.level = level;
+  ip.next = next;
+  ip.beta = beta;
+  ip.alpha = (int)c->alpha;
+  ip.L = (int)c->L;
+  ip.K = (int)c->K;
+  if ((rc = launch_inner_product(c, s, ip, n_items))) return rc;
+  // 6. iNTT of the special limbs (no 1/N)
+  jobs.n = 0;
+  for (int comp = 0; comp < 2; ++comp)
+    for (int k = 0; k < (int)c->K; ++k) jobs.add(comp * next + nq + k, comp * next + nq + k, (int)c->L + k);
+  if ((rc = ntt_run(c, s, A, A, per, per, n_items, jobs, true, false))) return rc;
+  // 7. ModDown conversion
+  ModDownArgs md;
+  memset(&md, 0, sizeof(md));
+  md.acc = A;
+  md.w = W;
+  md.acc_bstride = per;
+  md.w_bstride = per;
+  md.phinv = c->d_moddown + c->md.phinv;
+  md.conv = c->d_moddown + c->md.conv;
+  md.prime = c->d_prime;
+  md.n = N;
+  md.level = level;
+  md.next = next;
+  md.L = (int)c->L;
+  md.K = (int)c->K;
+  if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
+  // 8. NTT of the converted limbs
+  jobs.n = 0;
+  for (int comp = 0; comp < 2; ++comp)
+    for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
+  if ((rc = ntt_run(c, s, W, W, per, per, n_items, jobs, false, false))) return rc;
+  // 9. combine
+  CombineArgs cb;
+  memset(&cb, 0, sizeof(cb));
+  cb.acc = A;
+  cb.w = W;
+  cb.acc_bstride = per;
+  cb.w_bstride = per;
+  cb.add[0] = it[0].add[0];
+  cb.add[1] = it[0].add[1];
+  cb.add_bstride = add_stride;
+  for (int i = 0; i < n_items; ++i) cb.add_g[i] = it[i].add_g;
+  cb.accum = it[0].accum;
+  cb.accum_bstride = accum_stride;
+  cb.out = it[0].out;
+  cb.out_bstride = out_stride;
+  cb.out_comp_limbs = out_comp_limbs;
+  cb.pinv = c->d_moddown + c->md.pinv;
+  cb.prime = c->d_prime;
+  cb.n = N;
+  cb.level = level;
+  cb.next = next;
+  cb.log_n = (int)c->log_n;
+  return launch_combine(c, s, cb, n_items);
+}
+
+uint32_t inv_mod_2n(uint32_t g, uint32_t two_n) {
+  uint32_t x = g;  // Newton iteration for the inverse of an odd number modulo a power of two
+  for (int i = 0; i < 5; ++i) x *= 2 - g * x;
+  return x & (two_n - 1);
+}
+
+int check_level(const Ctx* c, int level) {
+  if (level < 0 || level >= (int)c->L) return set_error(CKKS_ERANGE, "level out of range");
+  return CKKS_OK;
+}
+
+int check_galois(const Ctx* c, uint32_t g) {
+  if (!(g & 1) || g >= 2 * c->N) return set_error(CKKS_EINVAL, "galois element must be odd and below 2N");
+  return CKKS_OK;
+}
+
+// Rescale of `batch` items: in [2][level+1][N] at in + b*in_stride -> out [2][level][N].
+int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride, uint64_t* out, uint64_t out_stride,
+                  int batch, int level, uint64_t* ws, uint64_t ws_words) {
+  const uint32_t N = c->N;
+  const uint64_t per = (uint64_t)N * (2 + 2 * level);
+  const int chunk = (int)std::max<uint64_t>(1, std::min<uint64_t>(kMaxChunk, ws_words / per));
+  for (int b0 = 0; b0 < batch; b0 += chunk) {
+    const int n = std::min(chunk, batch - b0);
+    uint64_t* V = ws;
+    uint64_t* W = ws + 2ull * N;
+    NttJobs jobs;
+    for (int comp = 0; comp < 2; ++comp) jobs.add(comp * (level + 1) + level, comp, level);
+    int rc = ntt_run(c, s, in + b0 * in_stride, V, in_stride, per, n, jobs, true, true);
+    if (rc) return rc;
+    RescaleArgs ra;
+    memset(&ra, 0, sizeof(ra));
+    ra.ct = in + b0 * in_stride;
+    ra.v = V;
+    ra.w = W;
+    ra.out = out + b0 * out_stride;
+    ra.ct_bstride = in_stride;
+    ra.v_bstride = per;
+    ra.w_bstride = per;
+    ra.out_bstride = out_stride;
+    ra.tab = c->d_rescale;
+    ra.prime = c->d_prime;
+    ra.n = N;
+    ra.level = level;
+    ra.L = (int)c->L;
+    if ((rc = launch_rescale_prep(c, s, ra, n))) return rc;
+    jobs.n = 0;
+    for (int comp = 0; comp < 2; ++comp)
+      for (int i = 0; i < level; ++i) jobs.add(comp * level + i, comp * level + i, i);
+    if ((rc = ntt_run(c, s, W, W, per, per, n, jobs, false, false))) return rc;
+    if ((rc = launch_rescale_combine(c, s, ra, n))) return rc;
+  }
+  return CKKS_OK;
+}
+
+// Batched rotation with contiguous input/output (item b at base + b*stride).
+int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint64_t stride, int batch, int level,
+                 const uint32_t* g, const uint64_t* const* evk, unsigned flags) {
+  const int nq = level + 1;
+  const uint64_t ct_words = 2ull * nq * c->N;
+  const uint64_t per = ks_ws_words(c, level);
+  const int chunk = g_chunk_default();
+  int rc = ensure_workspace(c, per * chunk);
+  if (rc) return rc;
+  std::vector<int> idx;
+  for (int b = 0; b < batch; ++b) {
+    if (g[b] == 1) {
+      if (flags & CKKS_ROT_ACCUMULATE) {
+        if ((rc = launch_add(c, s, in + b * stride, in + b * stride, out + b * stride, 1, nq, 2, 0))) return rc;
+      } else {
+        CKKS_HIP_CHECK(hipMemcpyAsync(out + b * stride, in + b * stride, ct_words * 8, hipMemcpyDeviceToDevice, s));
+      }
+    } else {
+      idx.push_back(b);
+    }
+  }
+  // consecutive runs of non-identity items share a stride
+  size_t p = 0;
+  while (p < idx.size()) {
+    size_t q = p + 1;
+    while (q < idx.size() && q - p < (size_t)chunk && idx[q] == idx[q - 1] + 1) ++q;
+    KSItem items[kMaxChunk];
+    for (size_t k = p; k < q; ++k) {
+      const int b = idx[k];
+      KSItem& it = items[k - p];
+      it.d = in + b * stride + (uint64_t)nq * c->N;  // c1
+      it.g = g[b];
+      it.evk = evk[b];
+      it.add[0] = in + b * stride;  // c0, gathered through g
+      it.add[1] = nullptr;
+      it.add_g = g[b];
+      it.accum = (flags & CKKS_ROT_ACCUMULATE) ? in + b * stride : nullptr;
+      it.out = out + b * stride;
+    }
+    if ((rc = ks_chunk(c, s, level, (int)(q - p), items, stride, stride, stride, stride, nq, c->ws))) return rc;
+    p = q;
+  }
+  return CKKS_OK;
+}
+
+}  // namespace
+}  // namespace ckks
+
+using namespace ckks;
+
+#define CTX_OR_FAIL(ctx)                                             \
+  if (!(ctx)) return set_error(CKKS_EINVAL, "ctx is NULL");         \
+  if (hipSetDevice((ctx)->device) != hipSuccess) return set_error(CKKS_EHIP, "hipSetDevice failed")
+
+extern "C" {
+
+int ckks_ntt(ckks_ctx* ctx, uint64_t* d_data, int npoly, int limb_begin, int n_limb, int inverse,
+             ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_data || npoly < 0 || n_limb < 0) return set_error(CKKS_EINVAL, "bad data pointer or count");
+  if (limb_begin < 0 || limb_begin + n_limb > (int)(ctx->L + ctx->K)) return set_error(CKKS_ERANGE, "limb range outside the basis");
+  if (npoly == 0 || n_limb == 0) return CKKS_OK;
+  if (npoly > 65535) return set_error(CKKS_EINVAL, "npoly too large");
+  NttJobs jobs;
+  for (int i0 = 0; i0 < n_limb; i0 += kMaxJobs) {
+    jobs.n = 0;
+    const int nl = std::min(kMaxJobs, n_limb - i0);
+    for (int i = 0; i < nl; ++i) jobs.add(i0 + i, i0 + i, limb_begin + i0 + i);
+    int rc = ntt_run(ctx, stream, d_data, d_data, (uint64_t)n_limb * ctx->N, (uint64_t)n_limb * ctx->N, npoly, jobs,
+                     inverse != 0, true);
+    if (rc) return rc;
+  }
+  return CKKS_OK;
+}
+
+int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npoly, int level, uint32_t galois_elt,
+                   int domain, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_in || !d_out || npoly < 0) return set_error(CKKS_EINVAL, "bad pointer or count");
+  int rc = check_level(ctx, level);
+  if (rc || (rc = check_galois(ctx, galois_elt))) return rc;
+  if (domain != 0 && domain != 1) return set_error(CKKS_EINVAL, "domain must be 0 (NTT) or 1 (coefficient)");
+  if (npoly == 0) return CKKS_OK;
+  const uint64_t pstride = (uint64_t)(level + 1) * ctx->N;
+  if (domain == 0) return launch_automorph_ntt(ctx, stream, d_in, d_out, npoly, level + 1, pstride, galois_elt);
+  return launch_automorph_coeff(ctx, stream, d_in, d_out, npoly, level + 1, pstride,
+                                inv_mod_2n(galois_elt, 2 * ctx->N));
+}
+
+int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk, uint64_t* d_out, int level,
+                   ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_poly || !d_evk || !d_out) return set_error(CKKS_EINVAL, "NULL pointer");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "key switching needs special primes");
+  if ((rc = ensure_workspace(ctx, ks_ws_words(ctx, level)))) return rc;
+  KSItem it;
+  memset(&it, 0, sizeof(it));
+  it.d = d_poly;
+  it.evk = d_evk;
+  it.out = d_out;
+  return ks_chunk(ctx, stream, level, 1, &it, 0, 0, 0, 0, level + 1, ctx->ws);
+}
+
+int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_ct_in || !d_ct_out || batch < 0 || (batch > 0 && (!galois_elts || !d_evks)))
+    return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (flags & ~CKKS_ROT_ACCUMULATE) return set_error(CKKS_EINVAL, "unknown flag");
+  for (int b = 0; b < batch; ++b) {
+    if ((rc = check_galois(ctx, galois_elts[b]))) return rc;
+    if (galois_elts[b] != 1 && !d_evks[b]) return set_error(CKKS_EINVAL, "NULL key pointer");
+  }
+  if (batch > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
+  return rotate_batch(ctx, stream, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
+                      flags);
+}
+
+int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch, int level, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_in || !d_out || batch < 0) return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
+  const uint64_t per = (uint64_t)ctx->N * (2 + 2 * level);
+  if ((rc = ensure_workspace(ctx, per * std::min(batch, kMaxChunk)))) return rc;
+  return rescale_batch(ctx, stream, d_in, 2ull * (level + 1) * ctx->N, d_out, 2ull * level * ctx->N, batch, level,
+                       ctx->ws, ctx->ws_words);
+}
+
+int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d_b, const uint64_t* d_rlk,
+                           uint64_t* d_out, int batch, int level, unsigned flags, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_a || !d_b || !d_rlk || !d_out || batch < 0) return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (flags & ~CKKS_NO_RESCALE) return set_error(CKKS_EINVAL, "unknown flag");
+  const bool rescale = !(flags & CKKS_NO_RESCALE);
+  if (rescale && level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation needs special primes");
+  if (batch == 0) return CKKS_OK;
+  const uint32_t N = ctx->N;
+  const int nq = level + 1;
+  const uint64_t ct = 2ull * nq * N;
+  const int chunk = g_chunk_default();
+  const uint64_t ks = ks_ws_words(ctx, level);
+  // per chunk: tensor output [3][nq][N] per item, relinearised [2][nq][N] per item, then key-switch scratch
+  const uint64_t tens = 3ull * nq * N, rel = ct;
+  const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
+  const uint64_t need = chunk * (tens + rel + std::max(ks, rs_per));
+  if ((rc = ensure_workspace(ctx, need))) return rc;
+  uint64_t* D = ctx->ws;
+  uint64_t* R = D + chunk * tens;
+  uint64_t* S = R + chunk * rel;
+  for (int b0 = 0; b0 < batch; b0 += chunk) {
+    const int n = std::min(chunk, batch - b0);
+    TensorArgs ta;
+    ta.a = d_a + b0 * ct;
+    ta.b = d_b + b0 * ct;
+    ta.out = D;
+    ta.in_bstride = ct;
+    ta.out_bstride = tens;
+    ta.prime = ctx->d_prime;
+    ta.n = N;
+    ta.level = level;
+    if ((rc = launch_tensor(ctx, stream, ta, n))) return rc;
+    KSItem items[kMaxChunk];
+    for (int i = 0; i < n; ++i) {
+      KSItem& it = items[i];
+      it.d = D + i * tens + 2ull * nq * N;
+      it.g = 0;
+      it.evk = d_rlk;
+      it.add[0] = D + i * tens;
+      it.add[1] = D + i * tens + (uint64_t)nq * N;
+      it.add_g = 0;
+      it.accum = nullptr;
+      it.out = rescale ? R + i * rel : d_out + (b0 + i) * ct;
+    }
+    if ((rc = ks_chunk(ctx, stream, level, n, items, tens, tens, 0, rel, nq, S))) return rc;
+    if (rescale) {
+      if ((rc = rescale_batch(ctx, stream, R, rel, d_out + (b0)*2ull * level * N, 2ull * level * N, n, level, S,
+                              chunk * std::max(ks, rs_per))))
+        return rc;
+    }
+  }
+  return CKKS_OK;
+}
+
+int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
+                  const uint32_t* baby_galois, const uint64_t* const* d_evk_baby, const uint32_t* giant_galois,
+                  const uint64_t* const* d_evk_giant, uint64_t* d_y, int level, unsigned flags,
+                  ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_x || !d_diags || !d_y || n_in < 1 || n_out < 1 || n1 < 1 || n2 < 1)
+    return set_error(CKKS_EINVAL, "NULL pointer or bad size");
+  if ((n1 > 1 && (!baby_galois || !d_evk_baby)) || (n2 > 1 && (!giant_galois || !d_evk_giant)))
+    return set_error(CKKS_EINVAL, "missing rotation keys");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (flags & ~CKKS_NO_RESCALE) return set_error(CKKS_EINVAL, "unknown flag");
+  const bool rescale = !(flags & CKKS_NO_RESCALE);
+  if (rescale && level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
+  for (int b = 1; b < n1; ++b)
+    if ((rc = check_galois(ctx, baby_galois[b - 1]))) return rc;
+  for (int g = 1; g < n2; ++g)
+    if ((rc = check_galois(ctx, giant_galois[g - 1]))) return rc;
+  const uint32_t N = ctx->N;
+  const int nq = level + 1;
+  const uint64_t ct = 2ull * nq * N;
+  // baby [n1][n_in] ciphertexts, inner [n_out][n2], rotated [n_out][n2], sum [n_out]
+  uint64_t *baby = nullptr, *inner = nullptr, *rot = nullptr;
+  auto cleanup = [&]() {
+    if (baby) (void)hipFree(baby);
+    if (inner) (void)hipFree(inner);
+    if (rot) (void)hipFree(rot);
+  };
+  if (hipMalloc((void**)&baby, ct * n1 * n_in * 8) != hipSuccess ||
+      hipMalloc((void**)&inner, ct * n_out * n2 * 8) != hipSuccess ||
+      hipMalloc((void**)&rot, ct * n_out * n2 * 8) != hipSuccess) {
+    (void)hipGetLastError();
+    cleanup();
+    return set_error(CKKS_ENOMEM, "ptmatvec buffers");
+  }
+  rc = CKKS_OK;
+  do {
+    if (hipMemcpyAsync(baby, d_x, ct * n_in * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+      rc = set_error(CKKS_EHIP, "copy");
+      break;
+    }
+    std::vector<uint32_t> gs(n_in);
+    std::vector<const uint64_t*> ks(n_in);
+    for (int b = 1; b < n1 && !rc; ++b) {
+      for (int c = 0; c < n_in; ++c) {
+        gs[c] = baby_galois[b - 1];
+        ks[c] = d_evk_baby[b - 1];
+      }
+      rc = rotate_batch(ctx, stream, d_x, baby + (uint64_t)b * n_in * ct, ct, n_in, level, gs.data(), ks.data(), 0);
+    }
+    if (rc) break;
+    PtMacArgs pm;
+    pm.diags = d_diags;
+    pm.baby = baby;
+    pm.out = inner;
+    pm.prime = ctx->d_prime;
+    pm.n = N;
+    pm.level = level;
+    pm.n_in = n_in;
+    pm.n1 = n1;
+    pm.n2 = n2;
+    if ((rc = launch_ptmac(ctx, stream, pm, n_out))) break;
+    std::vector<uint32_t> gg(n_out * n2);
+    std::vector<const uint64_t*> kg(n_out * n2);
+    for (int o = 0; o < n_out; ++o)
+      for (int g = 0; g < n2; ++g) {
+        gg[o * n2 + g] = g == 0 ? 1u : giant_galois[g - 1];
+        kg[o * n2 + g] = g == 0 ? nullptr : d_evk_giant[g - 1];
+      }
+    if ((rc = rotate_batch(ctx, stream, inner, rot, ct, n_out * n2, level, gg.data(), kg.data(), 0))) break;
+    // sum over giant steps into rot[o][0]
+    for (int g = 1; g < n2 && !rc; ++g)
+      rc = launch_add(ctx, stream, rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
+    if (rc) break;
+    if (rescale) {
+      const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
+      if ((rc = ensure_workspace(ctx, rs_per * std::min(n_out, kMaxChunk)))) break;
+      rc = rescale_batch(ctx, stream, rot, ct * n2, d_y, 2ull * level * N, n_out, level, ctx->ws, ctx->ws_words);
+    } else {
+      for (int o = 0; o < n_out && !rc; ++o)
+        if (hipMemcpyAsync(d_y + o * ct, rot + o * n2 * ct, ct * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+          rc = set_error(CKKS_EHIP, "copy");
+    }
+  } while (0);
+  if (hipStreamSynchronize(stream) != hipSuccess && !rc) rc = set_error(CKKS_EHIP, "stream sync");
+  cleanup();
+  return rc;
+}
+
+}  // extern "C"

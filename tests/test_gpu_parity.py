@@ -1,0 +1,251 @@
+"""Bit-exact parity of the HIP library against the CPU oracle, through the C
+interface, on seeded inputs: every output word must be equal.
+
+Sizes span several NTT tiles and, where the shape allows, ragged counts
+(odd batch sizes, partial last digits at lower levels, level 0, identity
+Galois elements mixed into a batch)."""
+import numpy as np
+import pytest
+
+import ckks_synth as S
+from gpu_util import announce, config_pair, empty_dev, make_pair, to_dev, to_host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    torch_cuda()
+    import private_rns_ckks_amd as L
+
+    return L
+
+
+@pytest.fixture(scope="module")
+def c1(lib, orc):
+    return config_pair(lib, orc, "C1")
+
+
+@pytest.fixture(scope="module")
+def c3small(lib, orc):
+    # C3 primes and digit structure at N = 2^12
+    return config_pair(lib, orc, "C3", log_n=12)
+
+
+# ---------------------------------------------------------------- NTT
+
+@pytest.mark.parametrize("log_n", [10, 11, 12, 13, 14, 15, 16])
+def test_ntt_parity_sizes(lib, orc, log_n):
+    announce("ntt log_n=%d" % log_n)
+    ctx, P = make_pair(lib, orc, log_n, 3, 54, 2, 60, 2)
+    npoly, nl = 3, 5
+    x = S.uniform_limbs(S.stream(log_n, "gpu/ntt"), P.mods, P.N, lead=(npoly,))
+    d = to_dev(x)
+    lib.ckks_ntt(ctx, d, npoly, 0, nl, 0)
+    f = to_host(d)
+    assert np.array_equal(f, orc.ntt_params(P, x))
+    lib.ckks_ntt(ctx, d, npoly, 0, nl, 1)
+    assert np.array_equal(to_host(d), x)
+    # inverse on an independent input
+    d2 = to_dev(x)
+    lib.ckks_ntt(ctx, d2, npoly, 0, nl, 1)
+    assert np.array_equal(to_host(d2), orc.ntt_params(P, x, inverse=True))
+
+
+def test_ntt_limb_offset_and_edges(lib, orc, c3small):
+    ctx, P = c3small
+    announce("ntt limb_begin / edge values")
+    x = S.uniform_limbs(S.stream(2, "gpu/ntt2"), P.mods[20:30], P.N, lead=(2,))
+    x[0, 0, :7] = 0
+    x[1, 3, :7] = np.uint64(P.mods[23] - 1)
+    d = to_dev(x)
+    lib.ckks_ntt(ctx, d, 2, 20, 10, 0)
+    ref = orc.ntt(x, P.mods[20:30], P.psi[20:30], P.log_n)
+    assert np.array_equal(to_host(d), ref)
+    z = to_dev(np.zeros((1, 1, P.N), dtype=np.uint64))
+    lib.ckks_ntt(ctx, z, 1, 31, 1, 0)
+    assert not to_host(z).any()
+    lib.ckks_ntt(ctx, d, 0, 0, 3, 0)  # empty batch is a no-op
+    with pytest.raises(lib.CKKSError) as e:
+        lib.ckks_ntt(ctx, d, 1, 30, 3, 0)
+    assert e.value.code == lib.CKKS_ERANGE
+
+
+def test_ntt_c2_full(lib, orc):
+    """C2 at full size: 16 polynomials x 24 limbs x 2^16 words, forward then inverse."""
+    announce("ntt C2 full")
+    ctx, P = config_pair(lib, orc, "C2")
+    x = S.uniform_limbs(S.stream(2, "C2/x"), P.q, P.N, lead=(16,))
+    d = to_dev(x)
+    lib.ckks_ntt(ctx, d, 16, 0, 24, 0)
+    f = to_host(d)
+    ref = orc.ntt_params(P, x)
+    assert np.array_equal(f, ref)
+    lib.ckks_ntt(ctx, d, 16, 0, 24, 1)
+    assert np.array_equal(to_host(d), x)
+
+
+# ---------------------------------------------------------------- automorphism
+
+@pytest.mark.parametrize("domain", [0, 1])
+def test_automorph_parity(lib, orc, c3small, domain):
+    ctx, P = c3small
+    level = 23
+    announce("automorph domain=%d" % domain)
+    x = S.uniform_limbs(S.stream(domain, "gpu/aut"), P.q, P.N, lead=(2,))
+    dx = to_dev(x)
+    out = empty_dev(x.shape)
+    for g in [5, P.galois(7), 2 * P.N - 1, 1, P.galois(1234)]:
+        lib.ckks_automorph(ctx, dx, out, 2, level, g, domain)
+        got = to_host(out)
+        if domain == 0:
+            ref = orc.automorph_ntt(x, P.log_n, g)
+        else:
+            ref = orc.automorph_coeff(x, P.q, P.log_n, g)
+        assert np.array_equal(got, ref), g
+    with pytest.raises(lib.CKKSError) as e:
+        lib.ckks_automorph(ctx, dx, out, 2, level, 4, domain)
+    assert e.value.code == lib.CKKS_EINVAL
+
+
+# ---------------------------------------------------------------- key switching
+
+@pytest.mark.parametrize("level", [23, 16, 12, 7, 0])
+def test_keyswitch_parity(lib, orc, c3small, level):
+    ctx, P = c3small
+    announce("keyswitch level=%d" % level)
+    d = S.uniform_limbs(S.stream(level, "gpu/ks/d"), P.q[: level + 1], P.N)
+    evk = S.uniform_limbs(S.stream(level, "gpu/ks/k"), P.mods, P.N, lead=(P.dnum, 2))
+    out = empty_dev((2, level + 1, P.N))
+    lib.ckks_keyswitch(ctx, to_dev(d), to_dev(evk), out, level)
+    assert np.array_equal(to_host(out), orc.keyswitch(P, level, d, evk))
+
+
+def test_keyswitch_parity_c1(lib, orc, c1):
+    ctx, P = c1
+    for level in (3, 1, 0):
+        announce("keyswitch C1 level=%d" % level)
+        d = S.uniform_limbs(S.stream(level, "gpu/ks1/d"), P.q[: level + 1], P.N)
+        evk = S.uniform_limbs(S.stream(level, "gpu/ks1/k"), P.mods, P.N, lead=(P.dnum, 2))
+        out = empty_dev((2, level + 1, P.N))
+        lib.ckks_keyswitch(ctx, to_dev(d), to_dev(evk), out, level)
+        assert np.array_equal(to_host(out), orc.keyswitch(P, level, d, evk))
+
+
+# ---------------------------------------------------------------- rotation
+
+def test_rotate_c1_encrypted(lib, orc, c1):
+    """C1: real encryption, rotate by 1 and by 7; words equal the oracle's and decrypt to the shift."""
+    from helpers import encrypt_slots, galois_key, rel_err, secret
+
+    ctx, P = c1
+    c = S.CONFIGS["C1"]
+    announce("rotate C1")
+    s, s_ntt = secret(orc, P, 1, c["h"])
+    z = S.uniform_slots(S.stream(1, "msg"), P.N // 2, complex_values=True)
+    level = P.L - 1
+    ct = encrypt_slots(orc, P, s_ntt, z, c["scale"], level, 1, "ct")
+    for k in c["rotations"]:
+        g = P.galois(k)
+        evk = galois_key(orc, P, s_ntt, g, 1, "gk%d" % k)
+        out = empty_dev(ct.shape)
+        lib.ckks_rotate(ctx, to_dev(ct), out, 1, level, [g], [to_dev(evk)])
+        got = to_host(out)
+        assert np.array_equal(got, orc.rotate(P, level, ct, g, evk))
+        assert rel_err(orc.decrypt(P, level, got, s_ntt, c["scale"]), np.roll(z, -k)) < 2 ** -12
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_rotate_batch_mixed(lib, orc, c3small, flags):
+    ctx, P = c3small
+    level = 22
+    B = 7
+    announce("rotate batch mixed flags=%d" % flags)
+    cts = S.uniform_limbs(S.stream(flags, "gpu/rot/ct"), P.q[: level + 1], P.N, lead=(B, 2))
+    gs = [P.galois(k) for k in (1, 3, 0, 100, 2047, 5, 0)]
+    keys_h = [S.uniform_limbs(S.stream(b, "gpu/rot/k"), P.mods, P.N, lead=(P.dnum, 2)) for b in range(B)]
+    keys = [to_dev(k) for k in keys_h]
+    out = empty_dev(cts.shape)
+    lib.ckks_rotate(ctx, to_dev(cts), out, B, level, gs, keys, flags)
+    got = to_host(out)
+    ref = orc.rotate_batch(P, level, cts, gs, keys_h, flags)
+    assert np.array_equal(got, ref)
+
+
+def test_rotate_errors(lib, orc, c3small):
+    ctx, P = c3small
+    x = empty_dev((1, 2, 24, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    for args, code in [((1, 24, [5], [k]), lib.CKKS_ERANGE), ((1, 23, [6], [k]), lib.CKKS_EINVAL),
+                       ((1, 23, [2 * P.N + 1], [k]), lib.CKKS_EINVAL), ((1, -1, [5], [k]), lib.CKKS_ERANGE),
+                       ((1, 23, [5], [None]), lib.CKKS_EINVAL)]:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_rotate(ctx, x, x, *args)
+        assert e.value.code == code
+
+
+# ---------------------------------------------------------------- rescale, multiply
+
+@pytest.mark.parametrize("level", [23, 1])
+def test_rescale_parity(lib, orc, c3small, level):
+    ctx, P = c3small
+    announce("rescale level=%d" % level)
+    B = 3
+    cts = S.uniform_limbs(S.stream(level, "gpu/rs"), P.q[: level + 1], P.N, lead=(B, 2))
+    out = empty_dev((B, 2, level, P.N))
+    lib.ckks_rescale(ctx, to_dev(cts), out, B, level)
+    got = to_host(out)
+    for b in range(B):
+        assert np.array_equal(got[b], orc.rescale(P, level, cts[b]))
+    with pytest.raises(lib.CKKSError) as e:
+        lib.ckks_rescale(ctx, to_dev(cts), out, B, 0)
+    assert e.value.code == lib.CKKS_ERANGE
+
+
+@pytest.mark.parametrize("flags", [0, 2])
+def test_mul_relin_rescale_parity(lib, orc, c3small, flags):
+    ctx, P = c3small
+    level = 23
+    B = 5
+    announce("mul_relin_rescale flags=%d" % flags)
+    a = S.uniform_limbs(S.stream(1, "gpu/mrr/a"), P.q, P.N, lead=(B, 2))
+    b = S.uniform_limbs(S.stream(1, "gpu/mrr/b"), P.q, P.N, lead=(B, 2))
+    rlk = S.uniform_limbs(S.stream(1, "gpu/mrr/k"), P.mods, P.N, lead=(P.dnum, 2))
+    lo = level + 1 if flags else level
+    out = empty_dev((B, 2, lo, P.N))
+    lib.ckks_mul_relin_rescale(ctx, to_dev(a), to_dev(b), to_dev(rlk), out, B, level, flags)
+    assert np.array_equal(to_host(out), orc.mul_relin_rescale(P, level, a, b, rlk, flags))
+
+
+def test_ptmatvec_parity(lib, orc, c3small):
+    ctx, P = c3small
+    level, n_in, n_out, n1, n2 = 12, 2, 3, 4, 3
+    announce("ptmatvec small")
+    x = S.uniform_limbs(S.stream(4, "gpu/pmv/x"), P.q[: level + 1], P.N, lead=(n_in, 2))
+    diags = S.uniform_limbs(S.stream(4, "gpu/pmv/d"), P.q[: level + 1], P.N, lead=(n_out, n_in, n2, n1))
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [S.uniform_limbs(S.stream(i, "gpu/pmv/kb"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n1 - 1)]
+    kg = [S.uniform_limbs(S.stream(i, "gpu/pmv/kg"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n2 - 1)]
+    for flags in (0, 2):
+        lo = level + 1 if flags else level
+        y = empty_dev((n_out, 2, lo, P.N))
+        lib.ckks_ptmatvec(ctx, to_dev(x), n_in, to_dev(diags), n_out, n1, n2, gb, [to_dev(k) for k in kb], gg,
+                          [to_dev(k) for k in kg], y, level, flags)
+        ref = orc.ptmatvec(P, level, x, diags, gb, kb, gg, kg, flags)
+        assert np.array_equal(to_host(y), ref)
+
+
+def test_repeatable(lib, orc, c3small):
+    """Same call twice gives identical words (no races between tiles)."""
+    ctx, P = c3small
+    level = 23
+    announce("repeatable")
+    cts = S.uniform_limbs(S.stream(9, "gpu/rep"), P.q, P.N, lead=(4, 2))
+    keys = [to_dev(S.uniform_limbs(S.stream(b, "gpu/rep/k"), P.mods, P.N, lead=(P.dnum, 2))) for b in range(4)]
+    gs = [P.galois(k) for k in (1, 2, 3, 4)]
+    d = to_dev(cts)
+    o1, o2 = empty_dev(cts.shape), empty_dev(cts.shape)
+    lib.ckks_rotate(ctx, d, o1, 4, level, gs, keys)
+    lib.ckks_rotate(ctx, d, o2, 4, level, gs, keys)
+    assert np.array_equal(to_host(o1), to_host(o2))
