@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Headline benchmark: batched homomorphic rotation (hybrid key switching) on
+one MI355X.
+
+Workload (the HRot throughput recipe): N = 2^16, L = 24 ciphertext primes of
+54 bits, K = 8 special primes of 60 bits, dnum = 3, level 23; a batch of 32
+ciphertexts, each rotated by its own offset (32 distinct offsets drawn from
+[1, 32767]) with its own Galois key.  One step = one ckks_rotate call on the
+batch.  Ciphertext and key words are seeded uniform residues: the rotation
+performs exactly the same operations on them as on real encryptions and keys
+(in RLWE both look uniform), and no scheme arithmetic is needed to make them.
+
+Also reported: the batched NTT (16 polynomials x 24 limbs x 2^16 words) in
+GB/s against the HBM peak, the roofline of the dominant kernel measured with
+HIP events on the library's stream during the timed region, and the CPU
+oracle timed on a bounded sample of the same batch.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "HRot (hybrid key-switch) ops/s at N=2^16,L=24,dnum=3; NTT GB/s vs HBM peak"
+HBM_PEAK_GBPS = 8000.0
+# int32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+BYTES_PER_HROT = 150_994_944  # ciphertext in (24 MiB) + key (96 MiB) + ciphertext out (24 MiB)
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
+    """The CPU oracle on a bounded sample of the batch (same words)."""
+    import oracle
+
+    P = oracle.Params(cfg["log_n"], q, p, cfg["dnum"])
+    level = cfg["L"] - 1
+    t0 = time.perf_counter()
+    oracle.rotate_batch(P, level, cts[:1], gs[:1], keys[:1])
+    t1 = time.perf_counter() - t0
+    k = max(1, min(len(gs) - 1, int(round(target_s / max(t1, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.rotate_batch(P, level, cts[1:1 + k], gs[1:1 + k], keys[1:1 + k])
+    dt = time.perf_counter() - t0
+    return {
+        "value": k / dt,
+        "unit": "HRot/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of the 32 rotations of the batch (items 1..%d), same words as the GPU run, "
+                  "plain __int128 %% oracle with OpenMP over limbs/coefficients; %.1f s" % (k, k, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-ntt", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rotation batches shard by ciphertext with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ckks_synth as S
+    import private_rns_ckks_amd as lib
+
+    cfg = S.CONFIGS["C3"]
+    N, L, K, dnum = 1 << cfg["log_n"], cfg["L"], cfg["K"], cfg["dnum"]
+    level, B = L - 1, cfg["batch"]
+    torch.cuda.set_device(0)
+    q = lib.ckks_find_primes(cfg["log_n"], cfg["q_bits"], L)
+    p = lib.ckks_find_primes(cfg["log_n"], cfg["p_bits"], K)
+    ctx = lib.Context(cfg["log_n"], q, p, dnum, device=0)
+
+    seed = 3
+    log("generating inputs")
+    cts = S.uniform_limbs(S.stream(seed, "bench/ct"), q, N, lead=(B, 2))
+    offsets = S.distinct_offsets(S.stream(seed, "bench/offsets"), B, *cfg["offset_range"])
+    gs = [pow(5, int(k), 2 * N) for k in offsets]
+    keys_h = [S.uniform_limbs(S.stream(seed, "bench/evk/%d" % b), q + p, N, lead=(dnum, 2)) for b in range(B)]
+    d_ct = torch.from_numpy(cts.view(np.int64)).cuda()
+    d_keys = [torch.from_numpy(k.view(np.int64)).cuda() for k in keys_h]
+    d_out = torch.empty_like(d_ct)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lib.ckks_rotate(ctx, d_ct, d_out, B, level, gs, d_keys, 0, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    trace = lib.KernelTrace(ctx, lib.DOMINANT_KERNEL)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    kstat = trace.read()
+    trace.close()
+    ms_step = ms / args.steps
+    value = B * args.steps / (ms / 1e3)
+    log("HRot/s %.1f  (%.3f ms per batch of %d)" % (value, ms_step, B))
+
+    # dominant kernel roofline, from the events recorded around each of its launches
+    roof = None
+    if kstat["launches"]:
+        avg_s = kstat["total_ms"] / kstat["launches"] / 1e3
+        per_launch = kstat["alg_units"] / kstat["launches"]
+        achieved = per_launch * kstat["ops_per_unit"] / avg_s / 1e12
+        roof = {
+            "kernel": kstat["name"],
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_PEAK_TOPS, 2),
+            "unit": "Tops/s",
+            "frac": round(achieved / VALU_PEAK_TOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_s * 1e6, 2),
+            "launches": kstat["launches"],
+            "work_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"], kstat["ops_per_unit"]),
+            "hbm_frac_step": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+
+    ntt = None
+    if not args.no_ntt:
+        ntt = ntt_bench(lib, S, torch, np, args)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(cfg, q, p, cts, gs, keys_h, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "HRot/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {
+            "workload": "HRot batch: N=2^16, L=24 x 54-bit + K=8 x 60-bit primes, dnum=3, level 23, "
+                        "32 ciphertexts with distinct offsets in [1,32767] and one Galois key each",
+            "batch": B, "N": N, "L": L, "K": K, "dnum": dnum, "level": level,
+        },
+        "roofline": roof,
+        "hbm_roofline_frac": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
+        "ntt": ntt,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    ctx.close()
+    return 0
+
+
+def ntt_bench(lib, S, torch, np, args):
+    """16 polynomials x 24 limbs x 2^16 words, forward and inverse, GB/s at 16 B per coefficient."""
+    cfg = S.CONFIGS["C2"]
+    N = 1 << cfg["log_n"]
+    q = lib.ckks_find_primes(cfg["log_n"], cfg["q_bits"], cfg["L"])
+    ctx = lib.Context(cfg["log_n"], q, [], 1, device=0)
+    x = S.uniform_limbs(S.stream(2, "bench/ntt"), q, N, lead=(cfg["npoly"],))
+    d = torch.from_numpy(x.view(np.int64)).cuda()
+    stream = torch.cuda.current_stream()
+    res = {}
+    nbytes = cfg["npoly"] * cfg["L"] * N * 16
+    for name, inv in (("fwd", 0), ("inv", 1)):
+        for _ in range(3):
+            lib.ckks_ntt(ctx, d, cfg["npoly"], 0, cfg["L"], inv, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            lib.ckks_ntt(ctx, d, cfg["npoly"], 0, cfg["L"], inv, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps / 1e3
+        res[name + "_GBps"] = round(nbytes / t / 1e9, 1)
+        res[name + "_us"] = round(t * 1e6, 1)
+        res[name + "_hbm_frac"] = round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)
+    res["shape"] = "16 x 24 x 2^16 u64, %d B per direction" % nbytes
+    log("NTT fwd %.1f GB/s, inv %.1f GB/s" % (res["fwd_GBps"], res["inv_GBps"]))
+    ctx.close()
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -112,6 +112,26 @@ int ckks_ctx_destroy(ckks_ctx* ctx);
 /* The roots in use (n_q+n_p values, host). */
 int ckks_ctx_psi(const ckks_ctx* ctx, uint64_t* out);
 
+/* ---- kernel timing trace (profiling aid) ------------------------------------ */
+
+typedef struct {
+  int32_t launches;  /* traced launches since ckks_trace_begin */
+  double total_ms;   /* sum of their durations (HIP events on the launch stream) */
+  double work_units; /* algorithmic work of those launches, in 64-bit modmul-class
+                        operations: one NTT butterfly, one 64x64-bit multiply-
+                        accumulate, one modular reduction or one constant
+                        multiplication each count 1 */
+} ckks_trace_stats;
+
+/* Start tracing the kernel family `kernel`: every later launch of it on any
+ * stream is bracketed by a HIP event pair on that stream.  Families:
+ * "ntt_pass", "automorph", "modup", "inner_product", "moddown_conv",
+ * "combine", "rescale", "tensor", "ptmac", "add".  NULL or "" stops tracing.
+ * Tracing adds two event records per traced launch and nothing else. */
+int ckks_trace_begin(ckks_ctx* ctx, const char* kernel);
+/* Waits for the recorded events, returns the totals and stops tracing. */
+int ckks_trace_end(ckks_ctx* ctx, ckks_trace_stats* out);
+
 /* ---- hot path ------------------------------------------------------------ */
 
 /* Negacyclic NTT (inverse = 0) or inverse NTT with the 1/N factor

@@ -96,6 +96,7 @@ def lib():
             "orc_make_switch_key": (None, [pp, u64p, u64p, u64p, i64p, u64p]),
             "orc_encrypt": (None, [pp, c_int, u64p, u64p, u64p, i64p, u64p]),
             "orc_decrypt_coeff": (None, [pp, c_int, u64p, u64p, u64p]),
+            "orc_num_threads": (c_int, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -127,6 +128,11 @@ def _ptr_array(arrs):
 # ---------------------------------------------------------------------------
 # Parameters
 # ---------------------------------------------------------------------------
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
+
 
 def is_prime(n: int) -> bool:
     return bool(lib().orc_is_prime(int(n)))

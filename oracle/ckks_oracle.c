@@ -763,3 +763,11 @@ void orc_decrypt_coeff(const orc_params *P, int level, const uint64_t *ct, const
     }
     orc_ntt_limbs(out, nq, P->log_n, P->mod, P->psi, 1);
 }
+
+/* Number of OpenMP threads the batched loops use (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

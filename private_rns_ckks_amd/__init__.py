@@ -31,8 +31,15 @@ EXPORTED = [
     "ckks_find_primes", "ckks_params_validate", "ckks_strerror", "ckks_last_error",
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
     "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rescale",
-    "ckks_mul_relin_rescale", "ckks_ptmatvec",
+    "ckks_mul_relin_rescale", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
 ]
+
+# Kernel family whose launches dominate a rotation batch (by rocprofv3 time).
+DOMINANT_KERNEL = "ntt_pass"
+# int32 VALU operations per 64-bit modmul-class operation: the 10 32x32-bit
+# partial products of a 64-bit Shoup (or Barrett) multiplication plus 6 int32
+# adds/subtracts to combine them and apply the quotient.
+OPS_PER_MODMUL = 16
 
 
 class CKKSError(RuntimeError):
@@ -40,6 +47,10 @@ class CKKSError(RuntimeError):
         self.code = code
         super().__init__("%s failed: %s (%d): %s" % (where, _lib.ckks_strerror(code).decode(), code,
                                                     _lib.ckks_last_error().decode()))
+
+
+class ckks_trace_stats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int32), ("total_ms", ctypes.c_double), ("work_units", ctypes.c_double)]
 
 
 class ckks_params(ctypes.Structure):
@@ -77,6 +88,8 @@ def _load():
         "ckks_rescale": (i, [vp, vp, vp, i, i, vp]),
         "ckks_mul_relin_rescale": (i, [vp, vp, vp, vp, vp, i, i, ctypes.c_uint, vp]),
         "ckks_ptmatvec": (i, [vp, vp, i, vp, i, i, i, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
+        "ckks_trace_begin": (i, [vp, ctypes.c_char_p]),
+        "ckks_trace_end": (i, [vp, ctypes.POINTER(ckks_trace_stats)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -218,3 +231,30 @@ def ckks_ptmatvec(ctx, d_x, n_in, d_diags, n_out, n1, n2, baby_galois, d_evk_bab
     _check(_lib.ckks_ptmatvec(ctx.handle, _ptr(d_x), n_in, _ptr(d_diags), n_out, n1, n2, gb, _ptr_list(d_evk_baby),
                               gg, _ptr_list(d_evk_giant), _ptr(d_y), level, flags, _stream(stream)),
            "ckks_ptmatvec")
+
+
+def ckks_trace_begin(ctx, kernel):
+    _check(_lib.ckks_trace_begin(ctx.handle, kernel.encode() if kernel else None), "ckks_trace_begin")
+
+
+def ckks_trace_end(ctx):
+    st = ckks_trace_stats()
+    _check(_lib.ckks_trace_end(ctx.handle, ctypes.byref(st)), "ckks_trace_end")
+    return {"launches": st.launches, "total_ms": st.total_ms, "work_units": st.work_units}
+
+
+class KernelTrace:
+    """Times every launch of one kernel family with HIP events (see ckks_trace_begin)."""
+
+    def __init__(self, ctx, kernel):
+        self.ctx, self.kernel = ctx, kernel
+        ckks_trace_begin(ctx, kernel)
+
+    def read(self):
+        st = ckks_trace_end(self.ctx)
+        st.update(name=self.kernel, alg_units=st["work_units"], ops_per_unit=OPS_PER_MODMUL,
+                  unit_name="modmul-class ops")
+        return st
+
+    def close(self):
+        pass

@@ -32,6 +32,28 @@ int ensure_workspace(Ctx* c, size_t words) {
   return CKKS_OK;
 }
 
+TraceScope::TraceScope(Ctx* c, hipStream_t s, const char* family, double units)
+    : c_(c), s_(s), on_(!c->trace.name.empty() && c->trace.name == family) {
+  if (!on_) return;
+  TraceState& t = c->trace;
+  while (t.pool.size() < t.used + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      on_ = false;
+      return;
+    }
+    t.pool.push_back(e);
+  }
+  (void)hipEventRecord(t.pool[t.used], s);
+  t.units += units;
+}
+
+TraceScope::~TraceScope() {
+  if (!on_) return;
+  (void)hipEventRecord(c_->trace.pool[c_->trace.used + 1], s_);
+  c_->trace.used += 2;
+}
+
 static int validate(const ckks_params* p) {
   using namespace host;
   if (!p) return set_error(CKKS_EPARAM, "params is NULL");
@@ -74,6 +96,7 @@ static int upload(void** dst, const void* src, size_t bytes) {
 static void destroy(Ctx* c) {
   if (!c) return;
   (void)hipSetDevice(c->device);
+  for (hipEvent_t e : c->trace.pool) (void)hipEventDestroy(e);
   void* bufs[] = {c->d_prime, c->d_tw_fwd, c->d_tw_inv, c->d_modup, c->d_moddown, c->d_rescale, c->ws};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
@@ -271,6 +294,32 @@ int ckks_ctx_create(const ckks_params* params, int hip_device, ckks_ctx** out) {
 int ckks_ctx_destroy(ckks_ctx* ctx) {
   if (!ctx) return set_error(CKKS_EINVAL, "ctx is NULL");
   destroy(ctx);
+  return CKKS_OK;
+}
+
+int ckks_trace_begin(ckks_ctx* ctx, const char* kernel) {
+  if (!ctx) return set_error(CKKS_EINVAL, "ctx is NULL");
+  ctx->trace.name = kernel ? kernel : "";
+  ctx->trace.used = 0;
+  ctx->trace.units = 0;
+  return CKKS_OK;
+}
+
+int ckks_trace_end(ckks_ctx* ctx, ckks_trace_stats* out) {
+  if (!ctx || !out) return set_error(CKKS_EINVAL, "NULL argument");
+  TraceState& t = ctx->trace;
+  out->launches = (int32_t)(t.used / 2);
+  out->total_ms = 0;
+  out->work_units = t.units;
+  for (size_t i = 0; i + 1 < t.used; i += 2) {
+    float ms = 0;
+    CKKS_HIP_CHECK(hipEventSynchronize(t.pool[i + 1]));
+    CKKS_HIP_CHECK(hipEventElapsedTime(&ms, t.pool[i], t.pool[i + 1]));
+    out->total_ms += ms;
+  }
+  t.name.clear();
+  t.used = 0;
+  t.units = 0;
   return CKKS_OK;
 }
 

@@ -40,6 +40,15 @@ struct ModDownLayout {
   size_t phinv, conv, pinv;
 };
 
+// Kernel timing trace (see ckks_trace_begin): HIP event pairs recorded on the
+// launch stream around every launch of one kernel family.
+struct TraceState {
+  std::string name;                // family being traced, "" = off
+  std::vector<hipEvent_t> pool;    // 2 events per traced launch
+  size_t used = 0;
+  double units = 0;                // algorithmic work units of the traced launches
+};
+
 struct Ctx {
   int device = 0;
   uint32_t log_n = 0, N = 0, L = 0, K = 0, dnum = 0, alpha = 0;
@@ -54,6 +63,7 @@ struct Ctx {
   uint64_t* d_rescale = nullptr;  // [L][L][4]: for level l, limb i < l: {ql^-1, Shoup, ql mod q_i, 0}
   uint64_t* ws = nullptr;         // workspace
   size_t ws_words = 0;
+  TraceState trace;
 
   int beta(int level) const { return (level + 1 + (int)alpha - 1) / (int)alpha; }
   // basis index of extended limb t at level l (q_0..q_l, then p_0..p_{K-1})
@@ -69,6 +79,19 @@ int set_error(int code, const std::string& msg);
   } while (0)
 
 int ensure_workspace(Ctx* c, size_t words);
+
+// Records the start event (if `family` is being traced) on construction and
+// the stop event on destruction; wrap exactly one kernel launch.
+class TraceScope {
+ public:
+  TraceScope(Ctx* c, hipStream_t s, const char* family, double units);
+  ~TraceScope();
+
+ private:
+  Ctx* c_;
+  hipStream_t s_;
+  bool on_;
+};
 
 // ---- NTT ----------------------------------------------------------------------
 constexpr int kMaxJobs = 160;

@@ -246,6 +246,7 @@ __global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, 
 
 int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl, uint64_t pstride,
                          uint32_t g) {
+  TraceScope ts(c, s, "automorph", 0);
   hipLaunchKernelGGL(automorph_ntt_kernel, dim3(c->N / 256, nl, npoly), dim3(256), 0, s, in, out, pstride, g,
                      (int)c->log_n);
   LAUNCH_CHECK();
@@ -254,6 +255,7 @@ int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* ou
 
 int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl,
                            uint64_t pstride, uint32_t ginv) {
+  TraceScope ts(c, s, "automorph", 0);
   hipLaunchKernelGGL(automorph_coeff_kernel, dim3(c->N / 256, nl, npoly), dim3(256), 0, s, in, out, pstride, ginv,
                      (int)c->log_n, c->d_prime);
   LAUNCH_CHECK();
@@ -261,48 +263,61 @@ int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* 
 }
 
 int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch) {
+  double units = 0;
+  for (int j = 0; j < beta; ++j) {
+    const int na = a.hi[j] - a.lo[j];
+    units += na + (double)(a.next - na) * (na + 1);
+  }
+  TraceScope ts(c, s, "modup", units * batch * c->N);
   hipLaunchKernelGGL(modup_kernel, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_inner_product(Ctx* c, hipStream_t s, IPArgs& a, int batch) {
+  TraceScope ts(c, s, "inner_product", (double)batch * a.next * 2 * (a.beta + 1) * c->N);
   hipLaunchKernelGGL(inner_product_kernel, dim3(c->N / 256, a.next, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
+  TraceScope ts(c, s, "moddown_conv", (double)batch * 2 * (a.K + (double)(a.level + 1) * (a.K + 1)) * c->N);
   hipLaunchKernelGGL(moddown_conv_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_combine(Ctx* c, hipStream_t s, CombineArgs& a, int batch) {
+  TraceScope ts(c, s, "combine", (double)batch * 2 * (a.level + 1) * c->N);
   hipLaunchKernelGGL(combine_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
+  TraceScope ts(c, s, "rescale", (double)batch * 2 * a.level * c->N);
   hipLaunchKernelGGL(rescale_prep_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
+  TraceScope ts(c, s, "rescale", (double)batch * 2 * a.level * c->N);
   hipLaunchKernelGGL(rescale_combine_kernel, dim3(c->N / 256, a.level, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
+  TraceScope ts(c, s, "tensor", (double)batch * (a.level + 1) * 7 * c->N);
   hipLaunchKernelGGL(tensor_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
+  TraceScope ts(c, s, "ptmac", (double)n_out * a.n2 * (a.level + 1) * 2 * (a.n_in * a.n1 + 1) * c->N);
   hipLaunchKernelGGL(ptmac_kernel, dim3(c->N / 256, a.level + 1, n_out * a.n2), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
@@ -310,6 +325,7 @@ int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
 
 int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
                int ncomp, uint64_t bstride) {
+  TraceScope ts(c, s, "add", 0);
   hipLaunchKernelGGL(add_kernel, dim3(c->N / 256, nl * ncomp, npoly), dim3(256), 0, s, x, y, out, bstride, nl,
                      c->d_prime, (int)c->log_n);
   LAUNCH_CHECK();

@@ -186,6 +186,8 @@ int launch_pass(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs, int lo
                   : (colfast ? pick<false, true>(logb) : pick<false, false>(logb));
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
   const uint32_t tiles = c->N / ((1u << logb) * kCols);
+  const double limbs = (double)njobs * batch;
+  TraceScope ts(c, s, "ntt_pass", limbs * (c->N / 2) * logb + ((inv && a.final_pass && a.scale) ? limbs * c->N : 0));
   hipLaunchKernelGGL(fn, dim3(tiles, njobs, batch), dim3(kThreads), 0, s, a);
   CKKS_HIP_CHECK(hipGetLastError());
   return CKKS_OK;
