@@ -81,8 +81,8 @@ typedef struct {
   uint32_t n_q;        /* L: ciphertext primes, 1..64 */
   uint32_t n_p;        /* K: special primes, 0..16; when K > 0, K == ceil(L/dnum) */
   uint32_t dnum;       /* gadget digits, 1..L; when K > 0, ceil(L/dnum) <= 16 */
-  const uint64_t* q;   /* host [n_q]: distinct primes, each = 1 mod 2N, < 2^62 */
-  const uint64_t* p;   /* host [n_p]: distinct primes, each = 1 mod 2N, < 2^62 */
+  const uint64_t* q;   /* host [n_q]: distinct primes, each = 1 mod 2N, < 2^60 */
+  const uint64_t* p;   /* host [n_p]: distinct primes, each = 1 mod 2N, < 2^60 */
   const uint64_t* psi; /* host [n_q+n_p] primitive 2N-th roots, or NULL = smallest ones */
 } ckks_params;
 

@@ -33,7 +33,40 @@ __device__ __forceinline__ uint64_t mul_shoup(uint64_t a, uint64_t w, uint64_t w
   return a * w - qh * q;
 }
 
+__device__ __forceinline__ uint64_t mad64(uint32_t a, uint32_t b, uint64_t c) { return (uint64_t)a * b + c; }
+
+// Shoup with an approximate quotient: the high product a*w' is taken from
+// the three upper 32x32 partial products only (the low one and the carries out
+// of the discarded low halves are dropped), so the quotient is at most 2 below
+// floor(a*w'/2^64) and the result lies in [0, 4q) for every a < 2^64.
+// 3 v_mad/v_mul_hi for the quotient instead of 4 plus carry handling.
+// The remainder a*w - qh*q is formed as lo64(a*w + qh*(2^64 - q)) with the two
+// low 32x32 products chained through one 64-bit accumulator and the four
+// cross products folded into its high word.
+__device__ __forceinline__ uint64_t mul_shoup_lazy(uint64_t a, uint64_t w, uint64_t wp, uint64_t q) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t p0 = (uint32_t)wp, p1 = (uint32_t)(wp >> 32);
+  // qh = a1 p1 + hi(a0 p1) + hi(a1 p0): drops a0 p0 and the low halves of the
+  // two middle products, so it is at most 2 below floor(a w' / 2^64)
+  const uint64_t s = (uint64_t)__umulhi(a0, p1) + (uint64_t)__umulhi(a1, p0);
+  const uint64_t qh = mad64(a1, p1, s);
+  const uint64_t nq = 0 - q;
+  const uint32_t q0 = (uint32_t)qh, q1 = (uint32_t)(qh >> 32);
+  const uint32_t w0 = (uint32_t)w, w1 = (uint32_t)(w >> 32);
+  const uint32_t n0 = (uint32_t)nq, n1 = (uint32_t)(nq >> 32);
+  uint64_t r = mad64(a0, w0, 0);
+  r = mad64(q0, n0, r);  // modulo 2^64
+  const uint32_t h = (uint32_t)(r >> 32) + a0 * w1 + a1 * w0 + q0 * n1 + q1 * n0;
+  return ((uint64_t)h << 32) | (uint32_t)r;
+}
+
 __device__ __forceinline__ uint64_t reduce_2q(uint64_t a, uint64_t q) { return a >= q ? a - q : a; }
+
+// [0, 4q) -> [0, q)
+__device__ __forceinline__ uint64_t reduce_4q(uint64_t a, uint64_t q) {
+  a = a >= 2 * q ? a - 2 * q : a;
+  return a >= q ? a - q : a;
+}
 
 // a mod q for any 64-bit a, given inv1 = floor(2^64 / q).
 __device__ __forceinline__ uint64_t reduce64(uint64_t a, uint64_t q, uint64_t inv1) {
@@ -64,6 +97,63 @@ __device__ __forceinline__ uint64_t reduce128(U128 x, uint64_t q, uint64_t r64, 
   uint64_t s = a + b;                             // [0, 4q), q < 2^62
   s = s >= 2 * q ? s - 2 * q : s;
   return reduce_2q(s, q);
+}
+
+// ---------------------------------------------------------------------------
+// Exact dot products of residues below 2^60 without carry chains.
+// Each operand is split into 30-bit halves (v = vh*2^30 + vl); a product then
+// has three column terms that are accumulated separately in 64-bit registers:
+//   a0 = sum vl*cl,  a1 = sum (vl*ch + vh*cl),  a2 = sum vh*ch,
+// every partial product is below 2^60, so up to 8 terms never overflow (a1
+// holds 2 products per term).  One v_mad_u64_u32 per partial product.
+struct Acc3 {
+  uint64_t a0, a1, a2;
+};
+
+__device__ __forceinline__ uint32_t lo30(uint64_t v) { return (uint32_t)v & 0x3fffffffu; }
+__device__ __forceinline__ uint32_t hi30(uint64_t v) { return (uint32_t)(v >> 30); }
+
+__device__ __forceinline__ void acc3_mac(Acc3& A, uint32_t xl, uint32_t xh, uint32_t cl, uint32_t ch) {
+  A.a0 = mad64(xl, cl, A.a0);
+  A.a1 = mad64(xl, ch, A.a1);
+  A.a1 = mad64(xh, cl, A.a1);
+  A.a2 = mad64(xh, ch, A.a2);
+}
+
+// a0 + a1*2^30 + a2*2^60 as a 128-bit value (a0 < 2^63, a1 < 2^64, a2 < 2^63).
+__device__ __forceinline__ U128 acc3_value(const Acc3& A) {
+  U128 r;
+  uint64_t t = A.a1 << 30;
+  uint64_t lo = A.a0 + t;
+  uint64_t hi = (A.a1 >> 34) + (lo < t ? 1 : 0);
+  t = A.a2 << 60;
+  r.lo = lo + t;
+  r.hi = hi + (A.a2 >> 4) + (r.lo < t ? 1 : 0);
+  return r;
+}
+
+// x mod q for x.hi < 2^64, using the approximate Shoup product for the high
+// word: hi*2^64 = hi*r64 (mod q).
+__device__ __forceinline__ uint64_t reduce128_lazy(U128 x, uint64_t q, uint64_t r64, uint64_t r64p, uint64_t inv1) {
+  const uint64_t a = mul_shoup_lazy(x.hi, r64, r64p, q);  // [0, 4q)
+  const uint64_t b = x.lo - mulhi64(x.lo, inv1) * q;      // [0, 2q)
+  uint64_t s = a + b;                                      // [0, 6q) < 2^63
+  s = s >= 4 * q ? s - 4 * q : s;
+  s = s >= 2 * q ? s - 2 * q : s;
+  return s >= q ? s - q : s;
+}
+
+// Running sum of products folded every 8 terms (the Acc3 capacity).
+struct DotMod {
+  Acc3 A;
+  int n;
+  uint64_t r;
+  __device__ __forceinline__ DotMod() : A{0, 0, 0}, n(0), r(0) {}
+};
+
+__device__ __forceinline__ uint64_t acc3_reduce(const Acc3& A, const uint64_t q, uint64_t r64, uint64_t r64p,
+                                                uint64_t inv1) {
+  return reduce128_lazy(acc3_value(A), q, r64, r64p, inv1);
 }
 
 __device__ __forceinline__ uint64_t add_mod(uint64_t a, uint64_t b, uint64_t q) {

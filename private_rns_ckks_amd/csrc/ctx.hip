@@ -70,7 +70,7 @@ static int validate(const ckks_params* p) {
   if (p->n_p) all.insert(all.end(), p->p, p->p + p->n_p);
   for (size_t i = 0; i < all.size(); ++i) {
     uint64_t m = all[i];
-    if (m >= (1ull << 62)) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not below 2^62");
+    if (m >= (1ull << 60)) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not below 2^60");
     if (m % two_n != 1) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not 1 mod 2N");
     if (!is_prime(m)) return set_error(CKKS_EPARAM, std::to_string(m) + " is not prime");
     for (size_t j = 0; j < i; ++j)

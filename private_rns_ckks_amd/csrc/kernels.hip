@@ -56,23 +56,41 @@ __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
   const uint64_t* tab = a.tables + a.offset[j];
   const uint64_t* x = a.x + blockIdx.z * a.x_bstride + c;
   uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
-  uint64_t y[16];
+  uint32_t yl[16], yh[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i < na) {
       const uint64_t q = a.prime[lo + i].q;
-      y[i] = reduce_2q(mul_shoup(x[(uint64_t)(lo + i) * a.n], tab[2 * i], tab[2 * i + 1], q), q);
+      const uint64_t y = reduce_4q(mul_shoup_lazy(x[(uint64_t)(lo + i) * a.n], tab[2 * i], tab[2 * i + 1], q), q);
+      yl[i] = lo30(y);
+      yh[i] = hi30(y);
     }
   }
   const uint64_t* conv = tab + 2 * na;
   for (int t = 0; t < a.next; ++t) {
     if (t >= lo && t < hi) continue;
     const PrimeConst pc = a.prime[t <= a.level ? t : a.L + (t - a.level - 1)];
-    U128 acc = {0, 0};
+    Acc3 A = {0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < na) mac(acc, y[i], conv[i * a.next + t]);
-    out[(uint64_t)t * a.n] = reduce128(acc, pc.q, pc.r64, pc.r64p, pc.inv1);
+    for (int i = 0; i < 8; ++i) {
+      if (i < na) {
+        const uint64_t cv = conv[i * a.next + t];
+        acc3_mac(A, yl[i], yh[i], lo30(cv), hi30(cv));
+      }
+    }
+    uint64_t r = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    if (na > 8) {
+      Acc3 B = {0, 0, 0};
+#pragma unroll
+      for (int i = 8; i < 16; ++i) {
+        if (i < na) {
+          const uint64_t cv = conv[i * a.next + t];
+          acc3_mac(B, yl[i], yh[i], lo30(cv), hi30(cv));
+        }
+      }
+      r = add_mod(r, acc3_reduce(B, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+    }
+    out[(uint64_t)t * a.n] = r;
   }
 }
 
@@ -88,19 +106,29 @@ __global__ __launch_bounds__(256) void inner_product_kernel(IPArgs a) {
   const PrimeConst pc = a.prime[keyl];
   const uint64_t* evk = a.evk[item];
   const uint64_t LKN = (uint64_t)(a.L + a.K) * a.n;
-  U128 ab = {0, 0}, aa = {0, 0};
+  Acc3 ab = {0, 0, 0}, aa = {0, 0, 0};
+  uint64_t rb = 0, ra = 0;
   for (int j = 0; j < a.beta; ++j) {
     const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
     const uint64_t d = in_digit ? a.d[item * a.d_bstride + (uint64_t)t * a.n + c]
                                 : a.ext[item * a.ext_bstride + ((uint64_t)j * a.next + t) * a.n + c];
     const uint64_t kb = evk[(2 * j) * LKN + (uint64_t)keyl * a.n + c];
     const uint64_t ka = evk[(2 * j + 1) * LKN + (uint64_t)keyl * a.n + c];
-    mac(ab, d, kb);
-    mac(aa, d, ka);
+    const uint32_t dl = lo30(d), dh = hi30(d);
+    acc3_mac(ab, dl, dh, lo30(kb), hi30(kb));
+    acc3_mac(aa, dl, dh, lo30(ka), hi30(ka));
+    if ((j & 7) == 7) {  // fold every 8 digits
+      rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      ab = {0, 0, 0};
+      aa = {0, 0, 0};
+    }
   }
+  rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+  ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
   uint64_t* out = a.acc + item * a.acc_bstride + (uint64_t)t * a.n + c;
-  out[0] = reduce128(ab, pc.q, pc.r64, pc.r64p, pc.inv1);
-  out[(uint64_t)a.next * a.n] = reduce128(aa, pc.q, pc.r64, pc.r64p, pc.inv1);
+  out[0] = rb;
+  out[(uint64_t)a.next * a.n] = ra;
 }
 
 // ModDown conversion for component blockIdx.y of item blockIdx.z.
@@ -111,26 +139,42 @@ __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int comp = blockIdx.y;
   const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)comp * a.next * a.n + c;
-  uint64_t y[16];
+  uint32_t yl[16], yh[16];
   uint32_t neg = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     if (k < a.K) {
       const uint64_t p = a.prime[a.L + k].q;
       uint64_t v = acc[(uint64_t)(a.level + 1 + k) * a.n];
-      v = reduce_2q(mul_shoup(v, a.phinv[2 * k], a.phinv[2 * k + 1], p), p);
+      v = reduce_4q(mul_shoup_lazy(v, a.phinv[2 * k], a.phinv[2 * k + 1], p), p);
       neg += v > (p - 1) / 2 ? 1u : 0u;
-      y[k] = v;
+      yl[k] = lo30(v);
+      yh[k] = hi30(v);
     }
   }
   uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * (a.level + 1) * a.n + c;
   for (int i = 0; i <= a.level; ++i) {
     const PrimeConst pc = a.prime[i];
-    U128 s = {0, 0};
+    Acc3 A = {0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k < a.K) mac(s, y[k], a.conv[k * a.L + i]);
-    const uint64_t r = reduce128(s, pc.q, pc.r64, pc.r64p, pc.inv1);
+    for (int k = 0; k < 8; ++k) {
+      if (k < a.K) {
+        const uint64_t cv = a.conv[k * a.L + i];
+        acc3_mac(A, yl[k], yh[k], lo30(cv), hi30(cv));
+      }
+    }
+    uint64_t r = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    if (a.K > 8) {
+      Acc3 B = {0, 0, 0};
+#pragma unroll
+      for (int k = 8; k < 16; ++k) {
+        if (k < a.K) {
+          const uint64_t cv = a.conv[k * a.L + i];
+          acc3_mac(B, yl[k], yh[k], lo30(cv), hi30(cv));
+        }
+      }
+      r = add_mod(r, acc3_reduce(B, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+    }
     w[(uint64_t)i * a.n] = sub_mod(r, neg, pc.q);
   }
 }
@@ -200,12 +244,16 @@ __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
   const uint64_t* y = a.b + blockIdx.z * a.in_bstride;
   uint64_t* d = a.out + blockIdx.z * a.out_bstride;
   const uint64_t a0 = x[off], a1 = x[lim + off], b0 = y[off], b1 = y[lim + off];
-  d[off] = mul_mod(a0, b0, pc.q, pc.r64, pc.r64p, pc.inv1);
-  U128 m = {0, 0};
-  mac(m, a0, b1);
-  mac(m, a1, b0);
-  d[lim + off] = reduce128(m, pc.q, pc.r64, pc.r64p, pc.inv1);
-  d[2 * lim + off] = mul_mod(a1, b1, pc.q, pc.r64, pc.r64p, pc.inv1);
+  const uint32_t a0l = lo30(a0), a0h = hi30(a0), a1l = lo30(a1), a1h = hi30(a1);
+  const uint32_t b0l = lo30(b0), b0h = hi30(b0), b1l = lo30(b1), b1h = hi30(b1);
+  Acc3 m0 = {0, 0, 0}, m1 = {0, 0, 0}, m2 = {0, 0, 0};
+  acc3_mac(m0, a0l, a0h, b0l, b0h);
+  acc3_mac(m1, a0l, a0h, b1l, b1h);
+  acc3_mac(m1, a1l, a1h, b0l, b0h);
+  acc3_mac(m2, a1l, a1h, b1l, b1h);
+  d[off] = acc3_reduce(m0, pc.q, pc.r64, pc.r64p, pc.inv1);
+  d[lim + off] = acc3_reduce(m1, pc.q, pc.r64, pc.r64p, pc.inv1);
+  d[2 * lim + off] = acc3_reduce(m2, pc.q, pc.r64, pc.r64p, pc.inv1);
 }
 
 // BSGS inner sums: inner[o][g][comp][i] = sum_c sum_b diag[o][c][g][b][i] * baby[b][c][comp][i].
@@ -217,18 +265,31 @@ __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
   const PrimeConst pc = a.prime[i];
   const uint64_t limbs = (uint64_t)(a.level + 1);
   const uint64_t off = (uint64_t)i * a.n + c;
-  U128 s0 = {0, 0}, s1 = {0, 0};
+  Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
+  uint64_t r0 = 0, r1 = 0;
+  int terms = 0;
   for (int ci = 0; ci < a.n_in; ++ci) {
     for (int b = 0; b < a.n1; ++b) {
       const uint64_t pt = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * limbs * a.n + off];
       const uint64_t* ct = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * limbs * a.n;
-      mac(s0, pt, ct[off]);
-      mac(s1, pt, ct[limbs * a.n + off]);
+      const uint64_t c0 = ct[off], c1 = ct[limbs * a.n + off];
+      const uint32_t pl = lo30(pt), ph = hi30(pt);
+      acc3_mac(s0, pl, ph, lo30(c0), hi30(c0));
+      acc3_mac(s1, pl, ph, lo30(c1), hi30(c1));
+      if (++terms == 8) {  // fold every 8 terms
+        r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        s0 = {0, 0, 0};
+        s1 = {0, 0, 0};
+        terms = 0;
+      }
     }
   }
+  r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+  r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
   uint64_t* out = a.out + (uint64_t)blockIdx.z * 2 * limbs * a.n;
-  out[off] = reduce128(s0, pc.q, pc.r64, pc.r64p, pc.inv1);
-  out[limbs * a.n + off] = reduce128(s1, pc.q, pc.r64, pc.r64p, pc.inv1);
+  out[off] = r0;
+  out[limbs * a.n + off] = r1;
 }
 
 // out = x + y on [nl] limbs per item (limb i uses prime i).
