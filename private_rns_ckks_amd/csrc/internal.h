@@ -118,6 +118,18 @@ struct NttJobs {
 // constant).  Outputs are fully reduced.  src may equal dst.
 int ntt_run(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, size_t src_bstride, size_t dst_bstride,
             int batch, const NttJobs& jobs, bool inverse, bool scale);
+// One pass only: forward first = column pass, forward second = row pass;
+// inverse first = row pass, inverse second = column pass.  The second pass
+// reduces to [0, q) (inverse: after the optional multiply, scale_mode as in
+// ntt_run_scaled).  src may equal dst.
+int ntt_pass_only(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, size_t src_bstride, size_t dst_bstride,
+                  int batch, const NttJobs& jobs, bool inverse, bool first, int scale_mode, const uint64_t* scale_tab,
+                  const uint32_t* scale_off);
+// As ntt_run; an inverse transform ends with a multiply by 1/N (scale_mode 1)
+// or by the per-job constant {w, w'} at scale_tab + scale_off[job] (mode 2).
+int ntt_run_scaled(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, size_t src_bstride, size_t dst_bstride,
+                   int batch, const NttJobs& jobs, bool inverse, int scale_mode, const uint64_t* scale_tab,
+                   const uint32_t* scale_off);
 
 }  // namespace ckks
 

@@ -6,9 +6,10 @@
 namespace ckks {
 
 constexpr int kMaxChunk = 8;  // batch items per launch of the key-switch pipeline
+constexpr int kMaxExt = 80;   // limbs of the extended basis: L (<= 64) + K (<= 16)
 
 struct ModUpArgs {
-  const uint64_t* x;    // coefficient form (no 1/N), [level+1][N] per item
+  const uint64_t* x;    // y_i = x_i [qhat_i^-1]_{q_i}, coefficient form, [level+1][N] per item
   uint64_t* out;        // [beta][next][N] per item
   uint64_t x_bstride, out_bstride;
   const uint64_t* tables;
@@ -31,10 +32,9 @@ struct IPArgs {
 };
 
 struct ModDownArgs {
-  const uint64_t* acc;  // [2][next][N] per item; special limbs in coefficient form (no 1/N)
+  const uint64_t* acc;  // [2][next][N] per item; special limbs hold y_k (coefficient form)
   uint64_t* w;          // [2][level+1][N] per item (coefficient form)
   uint64_t acc_bstride, w_bstride;
-  const uint64_t* phinv;  // [K][2]
   const uint64_t* conv;   // [K][L]
   const PrimeConst* prime;
   uint32_t n;
@@ -84,6 +84,24 @@ struct PtMacArgs {
   uint32_t n;
   int level, n_in, n1, n2;
 };
+
+struct KSItem {
+  const uint64_t* d;       // NTT-form input polynomial [level+1][N]
+  uint32_t g;              // automorphism applied to d before switching (0 = none)
+  const uint64_t* evk;     // [dnum][2][L+K][N]
+  const uint64_t* add[2];  // added to output component (gathered through add_g when add_g != 0)
+  uint32_t add_g;
+  const uint64_t* accum;   // [2][level+1][N] added to the output, or NULL
+  uint64_t* out;           // [2][out_comp_limbs][N]
+};
+
+// Key-switch workspace per item at `level` (words).
+size_t ks_ws_words(const Ctx* c, int level);
+
+// Hybrid key switch of up to kMaxChunk items whose external buffers share one
+// stride (item i at base + i*stride); `ws` provides ks_ws_words per item.
+int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
+             uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws);
 
 int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl, uint64_t pstride,
                          uint32_t g);

@@ -7,20 +7,12 @@
 // limbs (or digits / components), blockIdx.z over batch items.  Limb-major
 // layout makes every load and store a contiguous 64-bit access per lane.
 #include "arith.h"
+#include "automorph.h"
 #include "kernels.h"
 
 namespace ckks {
 
 namespace {
-
-// Index in the NTT-form input whose word lands at position j after X -> X^g:
-// word j holds a(psi^(2brv(j)+1)); the image holds a(psi^(g(2brv(j)+1))).
-__device__ __forceinline__ uint32_t automorph_src(uint32_t j, uint32_t g, int log_n) {
-  const uint32_t mask2n = (2u << log_n) - 1;
-  const uint32_t e = 2 * (__brev(j) >> (32 - log_n)) + 1;
-  const uint32_t eg = (e * g) & mask2n;
-  return __brev((eg - 1) >> 1) >> (32 - log_n);
-}
 
 __global__ void automorph_ntt_kernel(const uint64_t* in, uint64_t* out, uint64_t pstride, uint32_t g, int log_n) {
   const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -46,49 +38,60 @@ __global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64
 }
 
 // ModUp for digit blockIdx.y of batch item blockIdx.z.
-// x: coefficient form WITHOUT the 1/N factor (folded into the constants),
-// [level+1][N] per item.  out: [beta][next][N] per item; columns inside the
-// digit are left untouched.
+// x: the digit limbs already multiplied by [qhat_i^-1]_{q_i} (canonical y_i),
+// [level+1][N] per item.  out: [beta][next][N] per item; for every target limb
+// t outside the digit, out_t = sum_i y_i [qhat_i]_{m_t} mod m_t (exact).
+// The conversion constants and target moduli are staged in LDS once per
+// workgroup so the target loop reads them with broadcast LDS loads.
 __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ uint64_t s_conv[16 * kMaxExt];
+  __shared__ uint64_t s_pc[4 * kMaxExt];
   const int j = blockIdx.y;
   const int lo = a.lo[j], hi = a.hi[j], na = hi - lo;
-  const uint64_t* tab = a.tables + a.offset[j];
-  const uint64_t* x = a.x + blockIdx.z * a.x_bstride + c;
+  const uint64_t* conv = a.tables + a.offset[j] + 2 * na;
+  for (int k = threadIdx.x; k < na * a.next; k += blockDim.x) s_conv[k] = conv[k];
+  for (int t = threadIdx.x; t < a.next; t += blockDim.x) {
+    const PrimeConst& pc = a.prime[t <= a.level ? t : a.L + (t - a.level - 1)];
+    s_pc[4 * t] = pc.q;
+    s_pc[4 * t + 1] = pc.r64;
+    s_pc[4 * t + 2] = pc.r64p;
+    s_pc[4 * t + 3] = pc.inv1;
+  }
+  __syncthreads();
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t* x = a.x + blockIdx.z * a.x_bstride + (uint64_t)lo * a.n + c;
   uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
   uint32_t yl[16], yh[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i < na) {
-      const uint64_t q = a.prime[lo + i].q;
-      const uint64_t y = reduce_4q(mul_shoup_lazy(x[(uint64_t)(lo + i) * a.n], tab[2 * i], tab[2 * i + 1], q), q);
+      const uint64_t y = x[(uint64_t)i * a.n];
       yl[i] = lo30(y);
       yh[i] = hi30(y);
     }
   }
-  const uint64_t* conv = tab + 2 * na;
   for (int t = 0; t < a.next; ++t) {
     if (t >= lo && t < hi) continue;
-    const PrimeConst pc = a.prime[t <= a.level ? t : a.L + (t - a.level - 1)];
+    const uint64_t q = s_pc[4 * t], r64 = s_pc[4 * t + 1], r64p = s_pc[4 * t + 2], inv1 = s_pc[4 * t + 3];
     Acc3 A = {0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < na) {
-        const uint64_t cv = conv[i * a.next + t];
+        const uint64_t cv = s_conv[i * a.next + t];
         acc3_mac(A, yl[i], yh[i], lo30(cv), hi30(cv));
       }
     }
-    uint64_t r = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    uint64_t r = acc3_reduce(A, q, r64, r64p, inv1);
     if (na > 8) {
       Acc3 B = {0, 0, 0};
 #pragma unroll
       for (int i = 8; i < 16; ++i) {
         if (i < na) {
-          const uint64_t cv = conv[i * a.next + t];
+          const uint64_t cv = s_conv[i * a.next + t];
           acc3_mac(B, yl[i], yh[i], lo30(cv), hi30(cv));
         }
       }
-      r = add_mod(r, acc3_reduce(B, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r = add_mod(r, acc3_reduce(B, q, r64, r64p, inv1), q);
     }
     out[(uint64_t)t * a.n] = r;
   }
@@ -132,50 +135,61 @@ __global__ __launch_bounds__(256) void inner_product_kernel(IPArgs a) {
 }
 
 // ModDown conversion for component blockIdx.y of item blockIdx.z.
-// z_k: special limbs of acc in coefficient form without 1/N.
-// y_k = z_k * [phat_k^-1 N^-1]_{p_k}; negative when y_k > (p_k-1)/2 (centered lift).
-// w_i = sum_k y_k * [1/p_k]_{q_i} - (#negative) mod q_i  (= centered conversion times P^-1).
+// The special limbs of acc hold y_k = z_k [phat_k^-1]_{p_k} (canonical,
+// coefficient form).  Centred lift: y_k counts as negative when
+// y_k > (p_k-1)/2, and then sum_k ybar_k [phat_k P^-1]_{q_i} =
+// sum_k y_k [1/p_k]_{q_i} - #negative  (mod q_i).  w: [2][level+1][N] per item.
 __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
+  __shared__ uint64_t s_conv[16 * 64];
+  __shared__ uint64_t s_pc[4 * 64];
+  const int nq = a.level + 1;
+  for (int k = threadIdx.x; k < a.K * nq; k += blockDim.x) s_conv[k] = a.conv[(k / nq) * a.L + (k % nq)];
+  for (int i = threadIdx.x; i < nq; i += blockDim.x) {
+    const PrimeConst& pc = a.prime[i];
+    s_pc[4 * i] = pc.q;
+    s_pc[4 * i + 1] = pc.r64;
+    s_pc[4 * i + 2] = pc.r64p;
+    s_pc[4 * i + 3] = pc.inv1;
+  }
+  __syncthreads();
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int comp = blockIdx.y;
-  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)comp * a.next * a.n + c;
+  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.next + nq) * a.n + c;
   uint32_t yl[16], yh[16];
   uint32_t neg = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     if (k < a.K) {
-      const uint64_t p = a.prime[a.L + k].q;
-      uint64_t v = acc[(uint64_t)(a.level + 1 + k) * a.n];
-      v = reduce_4q(mul_shoup_lazy(v, a.phinv[2 * k], a.phinv[2 * k + 1], p), p);
-      neg += v > (p - 1) / 2 ? 1u : 0u;
+      const uint64_t v = acc[(uint64_t)k * a.n];
+      neg += v > (a.prime[a.L + k].q >> 1) ? 1u : 0u;
       yl[k] = lo30(v);
       yh[k] = hi30(v);
     }
   }
-  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * (a.level + 1) * a.n + c;
-  for (int i = 0; i <= a.level; ++i) {
-    const PrimeConst pc = a.prime[i];
+  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * nq * a.n + c;
+  for (int i = 0; i < nq; ++i) {
+    const uint64_t q = s_pc[4 * i], r64 = s_pc[4 * i + 1], r64p = s_pc[4 * i + 2], inv1 = s_pc[4 * i + 3];
     Acc3 A = {0, 0, 0};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (k < a.K) {
-        const uint64_t cv = a.conv[k * a.L + i];
+        const uint64_t cv = s_conv[k * nq + i];
         acc3_mac(A, yl[k], yh[k], lo30(cv), hi30(cv));
       }
     }
-    uint64_t r = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    uint64_t r = acc3_reduce(A, q, r64, r64p, inv1);
     if (a.K > 8) {
       Acc3 B = {0, 0, 0};
 #pragma unroll
       for (int k = 8; k < 16; ++k) {
         if (k < a.K) {
-          const uint64_t cv = a.conv[k * a.L + i];
+          const uint64_t cv = s_conv[k * nq + i];
           acc3_mac(B, yl[k], yh[k], lo30(cv), hi30(cv));
         }
       }
-      r = add_mod(r, acc3_reduce(B, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r = add_mod(r, acc3_reduce(B, q, r64, r64p, inv1), q);
     }
-    w[(uint64_t)i * a.n] = sub_mod(r, neg, pc.q);
+    w[(uint64_t)i * a.n] = sub_mod(r, neg, q);
   }
 }
 

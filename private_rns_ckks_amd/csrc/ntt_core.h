@@ -1,0 +1,269 @@
+// Core of the negacyclic NTT passes on gfx950, shared by the plain transform
+// and by the fused key-switch kernels.
+//
+// Transform (the reading used throughout): word j of the forward output is the
+// input polynomial evaluated at psi^(2*brv(j)+1).  The forward transform is a
+// chain of log N radix-2 Cooley-Tukey stages with the powers of psi merged
+// into the twiddles (stage S, butterfly block b uses psi^brv(2^S + b)); the
+// inverse is the Gentleman-Sande chain with psi^-brv(.) and a final 1/N.
+//
+// Decomposition.  A 2^16-word limb (512 KiB) does not fit the 160 KiB LDS of
+// a CU, so the stages are split into two passes over memory:
+//   column pass: the first LOGB stages of the forward transform only pair
+//                words whose index agrees modulo N/2^LOGB, so each column of
+//                2^LOGB words (stride N/2^LOGB) is independent;
+//   row pass:    the remaining stages act inside contiguous blocks.
+// The inverse runs the row pass first.  A workgroup owns a tile of 16 columns
+// (column pass: 16 adjacent words per row, 128-byte segments) or 16 blocks
+// (row pass) and runs its stages in two register rounds of radix 2^RA and
+// 2^RB: each thread holds 2^R words and applies R stages in registers, with
+// one LDS exchange between the rounds.  Loads and stores go straight between
+// registers and memory where the lanes of a wave touch adjacent words;
+// otherwise (first round of the inverse row pass, last round of the forward
+// row pass) they are staged through LDS.
+//
+// Element I/O is a template policy (see PlainIO; j = word index within the
+// limb), so a pass can gather its input (automorphism) or combine its output
+// with other data (key-switch epilogue) without a separate trip through
+// memory.
+//
+// Arithmetic: Shoup multiplication by the twiddle with an approximate
+// quotient (result in [0, 4q)).  Forward butterflies are fully lazy for
+// q < 2^57 (values grow by at most 4q per stage: 16 stages from [0, q) stay
+// below 65q < 2^64) and keep [0, 8q) otherwise; inverse butterflies keep
+// [0, 4q).  The last pass reduces to [0, q).
+#pragma once
+#include "arith.h"
+#include "internal.h"
+
+namespace ckks {
+namespace nttc {
+
+constexpr int kCols = 16;
+constexpr int kThreads = 256;
+
+// global word index (within the limb) of tile element (row, col)
+template <bool COLFAST>
+__device__ __forceinline__ uint32_t tile_index(uint32_t tile, uint32_t row, uint32_t col, int logb, int log_n) {
+  if (COLFAST) return tile * kCols + col + (row << (log_n - logb));
+  return ((tile * kCols + col) << logb) + row;
+}
+
+// LDS position of tile element (row, col).  Column pass: row-major with 16
+// padding words after every 2^RB rows; row pass: column-major with the low 4
+// row bits XOR-ed with the next 4 and 16 padding words per column.  Both make
+// the register rounds' 64-bit LDS accesses hit distinct bank pairs.
+template <bool COLFAST, int RB, int ROWS>
+__device__ __forceinline__ int lds_index(int row, int col) {
+  if (COLFAST) return row * kCols + col + (row >> RB) * 16;
+  return col * (ROWS + 16) + (row ^ ((row >> 4) & 15));
+}
+template <bool COLFAST, int RB, int ROWS>
+constexpr int lds_words() {
+  return COLFAST ? ROWS * kCols + (ROWS >> RB) * 16 : kCols * (ROWS + 16);
+}
+
+__device__ __forceinline__ void load_tw(const uint64_t* tw, uint32_t ti, uint64_t& w, uint64_t& wp) {
+  const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(tw + 2 * ti);
+  w = v.x;
+  wp = v.y;
+}
+
+template <bool LAZY>
+__device__ __forceinline__ void ct_butterfly(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q) {
+  const uint64_t four_q = 4 * q;
+  uint64_t u = x;
+  if (!LAZY) u = u >= four_q ? u - four_q : u;
+  const uint64_t t = mul_shoup_lazy(y, w, wp, q);  // [0, 4q)
+  x = u + t;
+  y = u + four_q - t;
+}
+
+__device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q) {
+  const uint64_t four_q = 4 * q;
+  const uint64_t s = x + y;
+  const uint64_t d = x + four_q - y;
+  x = s >= four_q ? s - four_q : s;
+  y = mul_shoup_lazy(d, w, wp, q);
+}
+
+// R stages in registers on the 2^R words x[] of one thread; the words are
+// rows base + (i << pos) of column col.  Global stage of sub-stage s is
+// s0 + logb - pos - R + s.
+template <int R, bool INV, bool LAZY, bool COLFAST>
+__device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int pos, int col, int logb, uint32_t tile,
+                                           uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
+  constexpr int E = 1 << R;
+#pragma unroll
+  for (int ss = 0; ss < R; ++ss) {
+    const int s = INV ? (R - 1 - ss) : ss;
+    const int half = E >> (s + 1);
+    const int S = s0 + logb - pos - R + s;
+#pragma unroll
+    for (int g = 0; g < (1 << s); ++g) {
+      const int i0 = g * 2 * half;
+      const uint32_t j = tile_index<COLFAST>(tile, base + (i0 << pos), col, logb, log_n);
+      uint64_t w, wp;
+      load_tw(tw, (1u << S) + (j >> (log_n - S)), w, wp);
+#pragma unroll
+      for (int m = 0; m < half; ++m) {
+        if (INV) gs_butterfly(x[i0 + m], x[i0 + m + half], w, wp, q);
+        else ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w, wp, q);
+      }
+    }
+  }
+}
+
+// Work item -> (column, base row) of a round covering row bits [pos, pos+R).
+// Column pass: columns vary fastest across lanes (adjacent words in memory);
+// row pass: the in-column index varies fastest.
+template <bool COLFAST, int R, int LOGB>
+__device__ __forceinline__ void item_coords(int item, int pos, int& col, int& base) {
+  constexpr int nb = 1 << (LOGB - R);
+  int b;
+  if (COLFAST) {
+    col = item % kCols;
+    b = item / kCols;
+  } else {
+    b = item % nb;
+    col = item / nb;
+  }
+  base = ((b >> pos) << (pos + R)) | (b & ((1 << pos) - 1));
+}
+
+// End-of-transform handling of the last pass.
+struct Finish {
+  int mode;        // 0: leave lazy (first pass), 1: reduce to [0,q), 2: inverse, times (w, wp) then reduce
+  uint64_t w, wp;  // mode 2 multiplier
+  uint64_t inv1;   // floor(2^64/q), forward reduction
+};
+
+template <int RA, int RB, bool INV, bool COLFAST, bool LAZY, class IO>
+__device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t tile, int log_n, uint32_t s0,
+                                          const uint64_t* tw, uint64_t q, const Finish& fin) {
+  constexpr int LOGB = RA + RB;
+  constexpr int ROWS = 1 << LOGB;
+  constexpr int TILE = ROWS * kCols;
+  const int tid = threadIdx.x;
+  // first round: forward = high bits (pos RB, RA stages); inverse = low bits (pos 0, RB stages)
+  constexpr int R1 = INV ? RB : RA;
+  constexpr int R2 = INV ? RA : RB;
+  const int pos1 = INV ? 0 : RB;
+  const int pos2 = INV ? RB : 0;
+  constexpr bool stage_in = INV && !COLFAST;   // inverse row pass: first round strided in memory
+  constexpr bool stage_out = !INV && !COLFAST; // forward row pass: last round strided in memory
+  constexpr int PER = TILE / kThreads;  // words per thread in the staging loops
+  if (stage_in) {
+    // all loads first, then the LDS and side stores: keeps the loads in flight together
+    uint64_t v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      v[k] = io.load(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      lds[lds_index<COLFAST, RB, ROWS>(row, col)] = v[k];
+      io.after_load(tile_index<COLFAST>(tile, row, col, LOGB, log_n), v[k]);
+    }
+    __syncthreads();
+  }
+  if (tid < kCols * (ROWS >> R1)) {
+    int col, base;
+    item_coords<COLFAST, R1, LOGB>(tid, pos1, col, base);
+    uint64_t x[1 << R1];
+#pragma unroll
+    for (int i = 0; i < (1 << R1); ++i) {
+      const int row = base + (i << pos1);
+      x[i] = stage_in ? lds[lds_index<COLFAST, RB, ROWS>(row, col)]
+                      : io.load(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
+    }
+    round_regs<R1, INV, LAZY, COLFAST>(x, base, pos1, col, LOGB, tile, s0, log_n, tw, q);
+    // each thread writes back exactly the words it read: no hazard with other threads
+#pragma unroll
+    for (int i = 0; i < (1 << R1); ++i) lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos1), col)] = x[i];
+  }
+  __syncthreads();
+  if (tid < kCols * (ROWS >> R2)) {
+    int col, base;
+    item_coords<COLFAST, R2, LOGB>(tid, pos2, col, base);
+    uint64_t x[1 << R2];
+#pragma unroll
+    for (int i = 0; i < (1 << R2); ++i) x[i] = lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)];
+    round_regs<R2, INV, LAZY, COLFAST>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
+    if (fin.mode == 1) {
+      if (INV) {
+#pragma unroll
+        for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_4q(x[i], q);
+      } else {
+#pragma unroll
+        for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);
+      }
+    } else if (fin.mode == 2) {
+#pragma unroll
+      for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_4q(mul_shoup_lazy(x[i], fin.w, fin.wp, q), q);
+    }
+    if (stage_out) {
+#pragma unroll
+      for (int i = 0; i < (1 << R2); ++i) lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)] = x[i];
+    } else {
+      typename IO::Ops ops[1 << R2];
+#pragma unroll
+      for (int i = 0; i < (1 << R2); ++i) ops[i] = io.fetch(tile_index<COLFAST>(tile, base + (i << pos2), col, LOGB, log_n));
+#pragma unroll
+      for (int i = 0; i < (1 << R2); ++i)
+        io.store(tile_index<COLFAST>(tile, base + (i << pos2), col, LOGB, log_n), x[i], ops[i]);
+    }
+  }
+  if (stage_out) {
+    __syncthreads();
+    // fetch every operand of the epilogue before the first store
+    typename IO::Ops ops[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      ops[k] = io.fetch(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      io.store(tile_index<COLFAST>(tile, row, col, LOGB, log_n), lds[lds_index<COLFAST, RB, ROWS>(row, col)], ops[k]);
+    }
+  }
+}
+
+// Dispatch on the butterfly form (lazy forward for small primes).
+template <int RA, int RB, bool INV, bool COLFAST, class IO>
+__device__ __forceinline__ void run_pass(const IO& io, uint64_t* lds, uint32_t tile, int log_n, uint32_t s0,
+                                         const uint64_t* tw, uint64_t q, const Finish& fin) {
+  if (!INV && q < (1ull << 57))
+    pass_body<RA, RB, INV, COLFAST, true>(io, lds, tile, log_n, s0, tw, q, fin);
+  else
+    pass_body<RA, RB, INV, COLFAST, false>(io, lds, tile, log_n, s0, tw, q, fin);
+}
+
+// Pass geometry for N = 2^log_n: the column pass covers the first logb_col
+// stages of the forward transform.
+__host__ __device__ inline int logb_col(int log_n) { return (log_n + 1) / 2; }
+__host__ __device__ inline int logb_row(int log_n) { return log_n - logb_col(log_n); }
+inline uint32_t pass_tiles(uint32_t n, int logb) { return n / ((1u << logb) * kCols); }
+
+// Element I/O policy.  load(j) supplies input word j; after_load(j, v) runs
+// once per word after all loads of a staging loop (side outputs); fetch(j)
+// reads whatever the store of word j needs and store(j, v, ops) writes the
+// result -- every fetch of a loop is issued before its first store.
+struct NoOps {};
+
+struct PlainIO {
+  typedef NoOps Ops;
+  const uint64_t* src;
+  uint64_t* dst;
+  __device__ __forceinline__ uint64_t load(uint32_t j) const { return src[j]; }
+  __device__ __forceinline__ void after_load(uint32_t, uint64_t) const {}
+  __device__ __forceinline__ Ops fetch(uint32_t) const { return Ops(); }
+  __device__ __forceinline__ void store(uint32_t j, uint64_t v, const Ops&) const { dst[j] = v; }
+};
+
+}  // namespace nttc
+}  // namespace ckks

@@ -1,20 +1,8 @@
 // Host orchestration of the hot path and the C ABI compute entry points.
-//
-// Hybrid key switch of one polynomial d at level l (per batch item):
-//   1. (rotation only) T = tau_g(c1) in NTT form (a permutation of words)
-//   2. C = iNTT(T) without the 1/N factor (folded into the ModUp constants)
-//   3. ModUp: for each digit j, unsigned fast basis conversion of the digit's
-//      limbs of C to every other limb of the extended basis q_0..q_l, p_*
-//   4. forward NTT of the converted limbs
-//   5. inner product with the key digits (digit limbs use T directly), one
-//      128-bit accumulation and one reduction per output word
-//   6. iNTT of the special-prime limbs of both accumulators (no 1/N)
-//   7. ModDown conversion: centered lift, times P^-1 folded into the constants
-//   8. forward NTT of the converted limbs
-//   9. out = acc * P^-1 - w (+ tau_g(c0), + the input for accumulation)
-// Batch items are processed in chunks so the intermediates of a chunk stay
-// resident in the last-level cache (the 256 MiB Infinity Cache) between the
-// steps instead of round-tripping through HBM for the whole batch.
+// The key-switch pipeline itself is in keyswitch.hip.  Batch items are
+// processed in chunks (CKKS_CHUNK, default 4, at most 8) so that one launch
+// covers several ciphertexts: enough workgroups to fill 256 CUs while the
+// chunk's intermediates stay within the 256 MiB last-level cache.
 #include <string.h>
 
 #include <algorithm>
@@ -33,146 +21,6 @@ int g_chunk_default() {
     return std::max(1, std::min(x, kMaxChunk));
   }();
   return v;
-}
-
-struct KSItem {
-  const uint64_t* d;       // NTT-form input polynomial [level+1][N]
-  uint32_t g;              // automorphism applied to d before switching (0 = none)
-  const uint64_t* evk;     // [dnum][2][L+K][N]
-  const uint64_t* add[2];  // added to output component (gathered through add_g when add_g != 0)
-  uint32_t add_g;
-  const uint64_t* accum;   // [2][level+1][N] added to the output, or NULL
-  uint64_t* out;           // [2][out_comp_limbs][N]
-};
-
-// Workspace words per item for the key-switch pipeline at `level`.
-size_t ks_ws_words(const Ctx* c, int level) {
-  const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
-  return n * (nq /*T*/ + nq /*C*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
-}
-
-// Run the key-switch pipeline on up to kMaxChunk items whose external buffers
-// share one stride (item i at base + i*stride), with `ws` as scratch.
-int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
-             uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
-  const uint32_t N = c->N;
-  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
-  const uint64_t per = ks_ws_words(c, level);
-  uint64_t* T = ws;
-  uint64_t* C = T + (uint64_t)nq * N;
-  uint64_t* E = C + (uint64_t)nq * N;
-  uint64_t* A = E + (uint64_t)beta * next * N;
-  uint64_t* W = A + (uint64_t)2 * next * N;
-  int rc;
-  // 1. automorphism of the input (rotation)
-  const uint64_t* Tsrc = it[0].d;
-  uint64_t T_stride = d_stride;
-  if (it[0].g) {
-    for (int i = 0; i < n_items; ++i)
-      if ((rc = launch_automorph_ntt(c, s, it[i].d, T + i * per, 1, nq, 0, it[i].g))) return rc;
-    Tsrc = T;
-    T_stride = per;
-  }
-  // 2. iNTT to coefficient form (no 1/N)
-  NttJobs jobs;
-  for (int i = 0; i < nq; ++i) jobs.add(i, i, i);
-  if ((rc = ntt_run(c, s, Tsrc, C, T_stride, per, n_items, jobs, true, false))) return rc;
-  // 3. ModUp
-  ModUpArgs mu;
-  memset(&mu, 0, sizeof(mu));
-  mu.x = C;
-  mu.out = E;
-  mu.x_bstride = per;
-  mu.out_bstride = per;
-  mu.tables = c->d_modup;
-  mu.prime = c->d_prime;
-  mu.n = N;
-  mu.level = level;
-  mu.next = next;
-  mu.L = (int)c->L;
-  for (int j = 0; j < beta; ++j) {
-    const ModUpEntry& en = c->modup[level][j];
-    mu.lo[j] = en.lo;
-    mu.hi[j] = en.hi;
-    mu.offset[j] = en.offset;
-  }
-  if ((rc = launch_modup(c, s, mu, beta, n_items))) return rc;
-  // 4. NTT of the converted limbs
-  jobs.n = 0;
-  for (int j = 0; j < beta; ++j)
-    for (int t = 0; t < next; ++t) {
-      if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
-      jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
-    }
-  if ((rc = ntt_run(c, s, E, E, per, per, n_items, jobs, false, false))) return rc;
-  // 5. inner product
-  IPArgs ip;
-  memset(&ip, 0, sizeof(ip));
-  ip.d = Tsrc;
-  ip.ext = E;
-  ip.acc = A;
-  ip.d_bstride = T_stride;
-  ip.ext_bstride = per;
-  ip.acc_bstride = per;
-  for (int i = 0; i < n_items; ++i) ip.evk[i] = it[i].evk;
-  ip.prime = c->d_prime;
-  ip.n = N;
-  ip.level = level;
-  ip.next = next;
-  ip.beta = beta;
-  ip.alpha = (int)c->alpha;
-  ip.L = (int)c->L;
-  ip.K = (int)c->K;
-  if ((rc = launch_inner_product(c, s, ip, n_items))) return rc;
-  // 6. iNTT of the special limbs (no 1/N)
-  jobs.n = 0;
-  for (int comp = 0; comp < 2; ++comp)
-    for (int k = 0; k < (int)c->K; ++k) jobs.add(comp * next + nq + k, comp * next + nq + k, (int)c->L + k);
-  if ((rc = ntt_run(c, s, A, A, per, per, n_items, jobs, true, false))) return rc;
-  // 7. ModDown conversion
-  ModDownArgs md;
-  memset(&md, 0, sizeof(md));
-  md.acc = A;
-  md.w = W;
-  md.acc_bstride = per;
-  md.w_bstride = per;
-  md.phinv = c->d_moddown + c->md.phinv;
-  md.conv = c->d_moddown + c->md.conv;
-  md.prime = c->d_prime;
-  md.n = N;
-  md.level = level;
-  md.next = next;
-  md.L = (int)c->L;
-  md.K = (int)c->K;
-  if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
-  // 8. NTT of the converted limbs
-  jobs.n = 0;
-  for (int comp = 0; comp < 2; ++comp)
-    for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
-  if ((rc = ntt_run(c, s, W, W, per, per, n_items, jobs, false, false))) return rc;
-  // 9. combine
-  CombineArgs cb;
-  memset(&cb, 0, sizeof(cb));
-  cb.acc = A;
-  cb.w = W;
-  cb.acc_bstride = per;
-  cb.w_bstride = per;
-  cb.add[0] = it[0].add[0];
-  cb.add[1] = it[0].add[1];
-  cb.add_bstride = add_stride;
-  for (int i = 0; i < n_items; ++i) cb.add_g[i] = it[i].add_g;
-  cb.accum = it[0].accum;
-  cb.accum_bstride = accum_stride;
-  cb.out = it[0].out;
-  cb.out_bstride = out_stride;
-  cb.out_comp_limbs = out_comp_limbs;
-  cb.pinv = c->d_moddown + c->md.pinv;
-  cb.prime = c->d_prime;
-  cb.n = N;
-  cb.level = level;
-  cb.next = next;
-  cb.log_n = (int)c->log_n;
-  return launch_combine(c, s, cb, n_items);
 }
 
 uint32_t inv_mod_2n(uint32_t g, uint32_t two_n) {
