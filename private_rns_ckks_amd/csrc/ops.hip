@@ -1,6 +1,6 @@
 // Host orchestration of the hot path and the C ABI compute entry points.
 // The key-switch pipeline itself is in keyswitch.hip.  Batch items are
-// processed in chunks (CKKS_CHUNK, default 4, at most 8) so that one launch
+// processed in chunks (CKKS_CHUNK, default 8, at most 8) so that one launch
 // covers several ciphertexts: enough workgroups to fill 256 CUs while the
 // chunk's intermediates stay within the 256 MiB last-level cache.
 #include <string.h>
@@ -17,7 +17,7 @@ namespace {
 int g_chunk_default() {
   static int v = [] {
     const char* e = getenv("CKKS_CHUNK");
-    int x = e ? atoi(e) : 4;
+    int x = e ? atoi(e) : 8;
     return std::max(1, std::min(x, kMaxChunk));
   }();
   return v;
