@@ -35,9 +35,10 @@
  *              has no slot convention: a left rotation by k slots in the
  *              usual encoding is g = 5^k mod 2N.
  *   Memory     d_* arguments are device pointers (HIP), owned by the caller,
- *              not retained after the call's stream work completes.  Host
- *              arrays (galois element lists, key pointer lists) are read
- *              before the call returns.
+ *              not retained after the call's stream work completes, each
+ *              16-byte aligned (CKKS_EINVAL otherwise; hipMalloc gives 256).
+ *              Host arrays (galois element lists, key pointer lists) are
+ *              read before the call returns.
  *   Streams    every compute call enqueues on `stream` and returns; outputs
  *              are valid after the stream is synchronised.  A context is not
  *              thread-safe: use one context per host thread / stream.
@@ -62,7 +63,7 @@ typedef struct ihipStream_t* ckks_stream_t; /* a hipStream_t; NULL = the null st
 
 enum {
   CKKS_OK = 0,
-  CKKS_EINVAL = -1,    /* null pointer, bad count, even or out-of-range Galois element */
+  CKKS_EINVAL = -1,    /* null or misaligned pointer, bad count, even or out-of-range Galois element */
   CKKS_ERANGE = -2,    /* level out of range, rescale at level 0, limb range outside the basis */
   CKKS_ENOMEM = -3,    /* device or host allocation failed */
   CKKS_EHIP = -4,      /* HIP launch or API failure */

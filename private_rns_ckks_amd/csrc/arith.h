@@ -99,6 +99,16 @@ __device__ __forceinline__ uint64_t reduce128(U128 x, uint64_t q, uint64_t r64, 
   return reduce_2q(s, q);
 }
 
+// Montgomery product a*b*2^-64 mod m in [0, 2m) for a, b < m < 2^62, m odd,
+// mp = -m^-1 mod 2^64.  P + u*m with u = lo(P)*mp is divisible by 2^64 and
+// its low words cancel, so the carry out of the low half is (lo(P) != 0).
+__device__ __forceinline__ uint64_t mont_mul_lazy(uint64_t a, uint64_t b, uint64_t m, uint64_t mp) {
+  const uint64_t lo = a * b;
+  const uint64_t hi = mulhi64(a, b);
+  const uint64_t u = lo * mp;
+  return hi + mulhi64(u, m) + (lo != 0 ? 1 : 0);
+}
+
 // ---------------------------------------------------------------------------
 // Exact dot products of residues below 2^60 without carry chains.
 // Each operand is split into 30-bit halves (v = vh*2^30 + vl); a product then

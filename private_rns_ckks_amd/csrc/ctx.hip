@@ -118,6 +118,9 @@ static int build_tables(Ctx* c) {
     k.r64p = shoup(k.r64, m);
     k.ninv = invmod(N % m, m);
     k.ninvp = shoup(k.ninv, m);
+    uint64_t inv = m;  // Newton iteration: inverse of odd m modulo 2^64
+    for (int it = 0; it < 6; ++it) inv *= 2 - m * inv;
+    k.mprime = 0 - inv;
   }
   int rc = upload((void**)&c->d_prime, pc.data(), pc.size() * sizeof(PrimeConst));
   if (rc) return rc;

@@ -19,7 +19,8 @@ struct PrimeConst {
   uint64_t r64p;   // Shoup quotient of r64
   uint64_t ninv;   // N^-1 mod q
   uint64_t ninvp;  // Shoup quotient of ninv
-  uint64_t pad0, pad1;
+  uint64_t mprime; // -q^-1 mod 2^64 (Montgomery reduction)
+  uint64_t pad;
 };
 
 // Basis-conversion constants for ModUp of digit j at level l (device copy at

@@ -109,26 +109,34 @@ __global__ __launch_bounds__(256) void inner_product_kernel(IPArgs a) {
   const PrimeConst pc = a.prime[keyl];
   const uint64_t* evk = a.evk[item];
   const uint64_t LKN = (uint64_t)(a.L + a.K) * a.n;
-  Acc3 ab = {0, 0, 0}, aa = {0, 0, 0};
   uint64_t rb = 0, ra = 0;
-  for (int j = 0; j < a.beta; ++j) {
-    const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
-    const uint64_t d = in_digit ? a.d[item * a.d_bstride + (uint64_t)t * a.n + c]
-                                : a.ext[item * a.ext_bstride + ((uint64_t)j * a.next + t) * a.n + c];
-    const uint64_t kb = evk[(2 * j) * LKN + (uint64_t)keyl * a.n + c];
-    const uint64_t ka = evk[(2 * j + 1) * LKN + (uint64_t)keyl * a.n + c];
-    const uint32_t dl = lo30(d), dh = hi30(d);
-    acc3_mac(ab, dl, dh, lo30(kb), hi30(kb));
-    acc3_mac(aa, dl, dh, lo30(ka), hi30(ka));
-    if ((j & 7) == 7) {  // fold every 8 digits
-      rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      ab = {0, 0, 0};
-      aa = {0, 0, 0};
+  // digits in groups of 8 (the split accumulator's capacity); within a group
+  // every load is issued before the first multiply
+  for (int j0 = 0; j0 < a.beta; j0 += 8) {
+    uint64_t d[8], kb[8], ka[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj;
+      if (j < a.beta) {
+        const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
+        d[jj] = in_digit ? a.d[item * a.d_bstride + (uint64_t)t * a.n + c]
+                         : a.ext[item * a.ext_bstride + ((uint64_t)j * a.next + t) * a.n + c];
+        kb[jj] = evk[(2 * j) * LKN + (uint64_t)keyl * a.n + c];
+        ka[jj] = evk[(2 * j + 1) * LKN + (uint64_t)keyl * a.n + c];
+      }
     }
+    Acc3 ab = {0, 0, 0}, aa = {0, 0, 0};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < a.beta) {
+        const uint32_t dl = lo30(d[jj]), dh = hi30(d[jj]);
+        acc3_mac(ab, dl, dh, lo30(kb[jj]), hi30(kb[jj]));
+        acc3_mac(aa, dl, dh, lo30(ka[jj]), hi30(ka[jj]));
+      }
+    }
+    rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+    ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
   }
-  rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-  ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
   uint64_t* out = a.acc + item * a.acc_bstride + (uint64_t)t * a.n + c;
   out[0] = rb;
   out[(uint64_t)a.next * a.n] = ra;

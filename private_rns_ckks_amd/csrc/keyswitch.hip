@@ -8,8 +8,9 @@
 //   B  inverse column pass; its final multiply uses [qhat_i^-1 N^-1]_{q_i},
 //      so it produces the ModUp inputs y_i directly
 //   C  ModUp conversion sum_i y_i [qhat_i]_{m_t} mod m_t to every target limb
-//      t of every digit, then both forward NTT passes of those limbs
-//   E  inner product with the key digits (digit limbs read the NTT-form input)
+//      t of every digit, then the forward column pass of those limbs
+//   D  forward row pass of the converted limbs fused with the inner product
+//      against the key digits (digit limbs read the NTT-form input)
 //   F  inverse NTT of the special limbs of both accumulators, final multiply
 //      by [phat_k^-1 N^-1]_{p_k}: the ModDown inputs y_k
 //   H  ModDown conversion sum_k y_k [1/p_k]_{q_i} - #{k: y_k > (p_k-1)/2}
@@ -56,11 +57,12 @@ struct GatherArgs {
   int log_n;
 };
 
-template <int RA, int RB>
+template <int RA, int RB, int LOGN>
 __global__ __launch_bounds__(kThreads) void intt_row_gather_kernel(GatherArgs a) {
   constexpr int ROWS = 1 << (RA + RB);
   __shared__ uint64_t lds[lds_words<false, RB, ROWS>()];
-  const int limb = blockIdx.y, item = blockIdx.z;
+  const GridPos gp = row_grid_pos();
+  const int limb = gp.job, item = gp.item;
   const uint64_t off = (uint64_t)limb << a.log_n;
   GatherIO io;
   io.src = a.src + item * a.src_bstride + off;
@@ -70,8 +72,189 @@ __global__ __launch_bounds__(kThreads) void intt_row_gather_kernel(GatherArgs a)
   io.log_n = a.log_n;
   const PrimeConst& pc = a.prime[limb];
   Finish fin{0, 0, 0, pc.inv1};
-  run_pass<RA, RB, true, false>(io, lds, blockIdx.x, a.log_n, (uint32_t)logb_col(a.log_n),
-                                a.tw + ((uint64_t)limb << (a.log_n + 1)), pc.q, fin);
+  run_pass<RA, RB, true, false, LOGN>(io, lds, gp.tile, a.log_n, a.tw + ((uint64_t)limb << (a.log_n + 1)), pc.q,
+                                      fin);
+}
+
+// ---------------------------------------------------------------------------
+// D+E: forward row pass of the converted limbs fused with the inner product.
+// A workgroup owns target limb t on one row-pass tile and loops over the
+// digits: the digit's NTT (or, for t inside the digit, the NTT-form input)
+// ends in LDS, and every thread multiply-accumulates its words against the
+// key digit in a coalesced order (keys are read exactly once).  Products are
+// Montgomery products (a*b*2^-64, lazy in [0, 2m)), so one 64-bit register
+// per word and component carries the sum; the 2^-64 factor is removed at the
+// end by a Shoup multiplication with 2^64 mod m.
+struct RowIPArgs {
+  const uint64_t* E;  // item b: E + b*E_bstride, [beta][next][N] column-pass output
+  const uint64_t* T;  // item b: T + b*T_bstride, [nq][N] NTT-form input
+  uint64_t* acc;      // item b: acc + b*acc_bstride, [2][next][N]
+  uint64_t E_bstride, T_bstride, acc_bstride;
+  const uint64_t* evk[kMaxChunk];
+  const uint64_t* tw;  // forward twiddles
+  const PrimeConst* prime;
+  int log_n, level, next, beta, alpha, L, K;
+};
+
+// The row pass's LOGB stages run as register rounds of at most 3 stages, the
+// last of exactly 3, so every thread of the 2^(LOGB+1)-thread workgroup holds
+// 8 words in every round and ends with 8 consecutive words of one column:
+// the layout the multiply phase reads the key digits in.
+template <int LOGB>
+struct IPRounds {
+  static constexpr int R3 = 3;
+  static constexpr int R2 = LOGB >= 6 ? 3 : LOGB - 3;
+  static constexpr int R1 = LOGB - R2 - R3;  // 0 when two rounds suffice
+  static constexpr int THREADS = 2 << LOGB;
+};
+
+// LDS position of row-pass tile element (row, col): column-major, with row
+// bits 0-4 XOR-ed by (row bits 5-7) and (row bits 6-7) << 3.  For the rounds
+// of 2, 3, 3 stages at row bits 6, 3, 0 every 64-bit access of a wave then
+// shares its bank pair with at most one other lane.
+template <int LOGB>
+__device__ __forceinline__ int ip_lds(int row, int col) {
+  return col * (1 << LOGB) + (row ^ (((row >> 6) & 3) << 3) ^ ((row >> 5) & 7));
+}
+
+// One register round of R forward stages on row bits [POS, POS+R): item k of
+// the thread (k < 8 >> R) is tid + k * THREADS; its words are rows
+// base + (i << POS) of column col, read from global memory (src) or LDS and
+// left in LDS or in x[].
+template <int R, int POS, int LOGB, bool LAZY, bool FROM_GLOBAL, bool TO_LDS>
+__device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, uint32_t tile,
+                                         uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
+  constexpr int T = IPRounds<LOGB>::THREADS;
+  constexpr int NI = 8 >> R;
+  uint64_t y[NI][1 << R];
+  int col[NI], base[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    item_coords<false, R, LOGB>(threadIdx.x + k * T, POS, col[k], base[k]);
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) {
+      const int row = base[k] + (i << POS);
+      y[k][i] = FROM_GLOBAL ? src[tile_index<false>(tile, row, col[k], LOGB, log_n)] : lds[ip_lds<LOGB>(row, col[k])];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    round_regs<R, false, LAZY, false>(y[k], base[k], POS, col[k], LOGB, tile, s0, log_n, tw, q);
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) {
+      if (TO_LDS) lds[ip_lds<LOGB>(base[k] + (i << POS), col[k])] = y[k][i];
+      else x[(k << R) + i] = y[k][i];
+    }
+  }
+}
+
+template <int LOGB, int LOGN, bool LAZY>
+__device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, const PrimeConst& pc, int keyl,
+                                            const GridPos& gp) {
+  typedef IPRounds<LOGB> G;
+  const int log_n = LOGN ? LOGN : a.log_n;
+  const uint32_t s0 = (uint32_t)logb_col(log_n);
+  const int t = gp.job, item = gp.item;
+  const uint32_t tile = gp.tile;
+  const uint64_t q = pc.q, mp = pc.mprime;
+  const uint64_t* tw = a.tw + ((uint64_t)keyl << (log_n + 1));
+  const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
+  // this thread's 8 output words: rows base..base+7 of column col
+  int col, base;
+  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  const uint32_t w0 = tile_index<false>(tile, base, col, LOGB, log_n);
+  const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
+  // Montgomery products are below 2m, so four of them sum below 8m < 2^63
+  uint64_t accb[8], acca[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) accb[i] = acca[i] = 0;
+  for (int j = 0; j < a.beta; ++j) {
+    const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
+    uint64_t x[8];
+    if (in_digit) {  // NTT-form input limb, in [0, q)
+      const ulonglong2* src =
+          reinterpret_cast<const ulonglong2*>(a.T + item * a.T_bstride + ((uint64_t)t << log_n) + w0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const ulonglong2 v = src[i];
+        x[2 * i] = v.x;
+        x[2 * i + 1] = v.y;
+      }
+    } else {  // forward row pass of the converted limb; outputs stay lazy (< 65q, or < 8q)
+      const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
+      __syncthreads();  // the previous digit's last round has read the tile
+      if constexpr (G::R1 > 0) {
+        ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, tile, s0, log_n, tw, q);
+        __syncthreads();
+        ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, tile, s0, log_n, tw, q);
+      } else {
+        ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, tile, s0, log_n, tw, q);
+      }
+      __syncthreads();
+      ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, tile, s0, log_n, tw, q);
+    }
+    const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
+    const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
+    ulonglong2 vb[4], va[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vb[i] = kb[i];
+      va[i] = ka[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      accb[2 * i] += mont_mul_lazy(x[2 * i], vb[i].x, q, mp);
+      accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], vb[i].y, q, mp);
+      acca[2 * i] += mont_mul_lazy(x[2 * i], va[i].x, q, mp);
+      acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], va[i].y, q, mp);
+    }
+    if ((j & 3) == 3) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        accb[i] = reduce64(accb[i], q, pc.inv1);
+        acca[i] = reduce64(acca[i], q, pc.inv1);
+      }
+    }
+  }
+  // remove the 2^-64 of the Montgomery products: times 2^64 mod m
+  ulonglong2* ob = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)t << log_n) + w0);
+  ulonglong2* oa = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)(a.next + t) << log_n) + w0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ulonglong2 vb, va;
+    vb.x = reduce_4q(mul_shoup_lazy(accb[2 * i], pc.r64, pc.r64p, q), q);
+    vb.y = reduce_4q(mul_shoup_lazy(accb[2 * i + 1], pc.r64, pc.r64p, q), q);
+    va.x = reduce_4q(mul_shoup_lazy(acca[2 * i], pc.r64, pc.r64p, q), q);
+    va.y = reduce_4q(mul_shoup_lazy(acca[2 * i + 1], pc.r64, pc.r64p, q), q);
+    ob[i] = vb;
+    oa[i] = va;
+  }
+}
+
+template <int LOGB, int LOGN>
+__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_ip_kernel(RowIPArgs a) {
+  __shared__ uint64_t lds[(1 << LOGB) * kCols];
+  const GridPos gp = row_grid_pos();
+  const int t = gp.job;
+  const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
+  const PrimeConst& pc = a.prime[keyl];
+  if (pc.q < (1ull << 57))
+    row_ip_body<LOGB, LOGN, true>(a, lds, pc, keyl, gp);
+  else
+    row_ip_body<LOGB, LOGN, false>(a, lds, pc, keyl, gp);
+}
+
+typedef void (*RowIPFn)(RowIPArgs);
+
+RowIPFn pick_row_ip(int log_n, int logb) {
+  if (log_n == 16 && logb == 8) return ntt_row_ip_kernel<8, 16>;
+  switch (logb) {
+    case 5: return ntt_row_ip_kernel<5, 0>;
+    case 6: return ntt_row_ip_kernel<6, 0>;
+    case 7: return ntt_row_ip_kernel<7, 0>;
+    case 8: return ntt_row_ip_kernel<8, 0>;
+  }
+  return nullptr;
 }
 
 // ---------------------------------------------------------------------------
@@ -121,11 +304,12 @@ struct CombinePassArgs {
   int log_n, nq, next, out_comp_limbs;
 };
 
-template <int RA, int RB>
+template <int RA, int RB, int LOGN>
 __global__ __launch_bounds__(kThreads) void ntt_row_combine_kernel(CombinePassArgs a) {
   constexpr int ROWS = 1 << (RA + RB);
   __shared__ uint64_t lds[lds_words<false, RB, ROWS>()];
-  const int job = blockIdx.y, item = blockIdx.z;  // job = comp * nq + i
+  const GridPos gp = row_grid_pos();
+  const int job = gp.job, item = gp.item;  // job = comp * nq + i
   const int comp = job / a.nq, i = job % a.nq;
   const PrimeConst& pc = a.prime[i];
   CombineIO io;
@@ -140,19 +324,11 @@ __global__ __launch_bounds__(kThreads) void ntt_row_combine_kernel(CombinePassAr
   io.g = a.g[item];
   io.log_n = a.log_n;
   Finish fin{1, 0, 0, pc.inv1};
-  run_pass<RA, RB, false, false>(io, lds, blockIdx.x, a.log_n, (uint32_t)logb_col(a.log_n),
-                                 a.tw + ((uint64_t)i << (a.log_n + 1)), pc.q, fin);
+  run_pass<RA, RB, false, false, LOGN>(io, lds, gp.tile, a.log_n, a.tw + ((uint64_t)i << (a.log_n + 1)), pc.q,
+                                       fin);
 }
 
 // ---------------------------------------------------------------------------
-// launch helpers: kernel instance by pass size
-#define PICK(kern, logb)                       \
-  ((logb) == 5   ? kern<3, 2>                  \
-   : (logb) == 6 ? kern<3, 3>                  \
-   : (logb) == 7 ? kern<4, 3>                  \
-   : (logb) == 8 ? kern<4, 4>                  \
-                 : nullptr)
-
 size_t ws_words(const Ctx* c, int level) {
   const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
   return n * (nq /*T*/ + nq /*Y*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
@@ -190,7 +366,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ga.prime = c->d_prime;
     for (int i = 0; i < n_items; ++i) ga.g[i] = it[i].g;
     ga.log_n = log_n;
-    auto fn = PICK(intt_row_gather_kernel, lr);
+    auto fn = CKKS_PICK_PASS(intt_row_gather_kernel, log_n, lr);
     if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
     TraceScope ts(c, s, "ntt_pass", (double)n_items * nq * (N / 2) * lr);
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_items), dim3(kThreads), 0, s, ga);
@@ -239,28 +415,39 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
         if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
         jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
       }
-    if ((rc = ntt_run(c, s, E, E, per, per, n_items, jobs, false, false))) return rc;
+    if ((rc = ntt_pass_only(c, s, E, E, per, per, n_items, jobs, false, true, 0, nullptr, nullptr))) return rc;
   }
-  // E: inner product
+  // D+E: forward row pass fused with the inner product
   {
-    IPArgs ip;
+    RowIPArgs ip;
     memset(&ip, 0, sizeof(ip));
-    ip.d = Tsrc;
-    ip.ext = E;
+    ip.E = E;
+    ip.E_bstride = per;
+    ip.T = Tsrc;
+    ip.T_bstride = T_stride;
     ip.acc = A;
-    ip.d_bstride = T_stride;
-    ip.ext_bstride = per;
     ip.acc_bstride = per;
     for (int i = 0; i < n_items; ++i) ip.evk[i] = it[i].evk;
+    ip.tw = c->d_tw_fwd;
     ip.prime = c->d_prime;
-    ip.n = N;
+    ip.log_n = log_n;
     ip.level = level;
     ip.next = next;
     ip.beta = beta;
     ip.alpha = (int)c->alpha;
     ip.L = (int)c->L;
     ip.K = (int)c->K;
-    if ((rc = launch_inner_product(c, s, ip, n_items))) return rc;
+    RowIPFn fn = pick_row_ip(log_n, lr);
+    if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
+    double units = 0;
+    for (int j = 0; j < beta; ++j) {
+      const int na = c->modup[level][j].hi - c->modup[level][j].lo;
+      units += (double)(next - na) * (N / 2) * lr;  // butterflies
+    }
+    units += (double)next * N * (2.0 * beta + 2);  // products and final reductions
+    TraceScope ts(c, s, "ntt_pass", units * n_items);
+    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), next, n_items), dim3(2u << lr), 0, s, ip);
+    CKKS_HIP_CHECK(hipGetLastError());
   }
   // F, G: inverse NTT of the special limbs, times [phat_k^-1 N^-1]: y_k
   {
@@ -317,7 +504,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ca.nq = nq;
     ca.next = next;
     ca.out_comp_limbs = out_comp_limbs;
-    auto fn = PICK(ntt_row_combine_kernel, lr);
+    auto fn = CKKS_PICK_PASS(ntt_row_combine_kernel, log_n, lr);
     TraceScope ts(c, s, "ntt_pass", (double)n_items * 2 * nq * ((double)(N / 2) * lr + N));
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), 2 * nq, n_items), dim3(kThreads), 0, s, ca);
     CKKS_HIP_CHECK(hipGetLastError());

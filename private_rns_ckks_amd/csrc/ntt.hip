@@ -16,7 +16,6 @@ struct PassArgs {
   const PrimeConst* prime;   // [L+K]
   const uint64_t* scale_tab; // scale_mode 2: {w, w'} at word offset scale_off[job]
   uint32_t log_n;
-  uint32_t s0;               // first global stage handled by this pass
   uint32_t final_pass;       // reduce to [0,q) at the end
   uint32_t scale_mode;       // inverse final pass: 0 none, 1 times 1/N, 2 times the table entry
   uint16_t src_limb[kMaxJobs];
@@ -25,15 +24,23 @@ struct PassArgs {
   uint8_t prime_idx[kMaxJobs];
 };
 
-template <int RA, int RB, bool INV, bool COLFAST>
+template <int RA, int RB, int LOGN, bool INV, bool COLFAST>
 __global__ __launch_bounds__(kThreads) void ntt_pass_kernel(PassArgs a) {
   constexpr int ROWS = 1 << (RA + RB);
   __shared__ uint64_t lds[lds_words<COLFAST, RB, ROWS>()];
-  const int job = blockIdx.y;
+  GridPos gp;
+  if (COLFAST) {  // column-pass twiddles are few and shared by every tile
+    gp.tile = blockIdx.x;
+    gp.job = blockIdx.y;
+    gp.item = blockIdx.z;
+  } else {
+    gp = row_grid_pos();
+  }
+  const int job = gp.job;
   const int log_n = a.log_n;
   PlainIO io;
-  io.src = a.src + blockIdx.z * a.src_bstride + (uint64_t)a.src_limb[job] * (1u << log_n);
-  io.dst = a.dst + blockIdx.z * a.dst_bstride + (uint64_t)a.dst_limb[job] * (1u << log_n);
+  io.src = a.src + gp.item * a.src_bstride + (uint64_t)a.src_limb[job] * (1u << log_n);
+  io.dst = a.dst + gp.item * a.dst_bstride + (uint64_t)a.dst_limb[job] * (1u << log_n);
   const int p = a.prime_idx[job];
   const PrimeConst& pc = a.prime[p];
   const uint64_t* tw = a.tw + ((uint64_t)p << (log_n + 1));
@@ -51,25 +58,17 @@ __global__ __launch_bounds__(kThreads) void ntt_pass_kernel(PassArgs a) {
       fin.wp = a.scale_tab[a.scale_off[job] + 1];
     }
   }
-  run_pass<RA, RB, INV, COLFAST>(io, lds, blockIdx.x, log_n, a.s0, tw, pc.q, fin);
+  run_pass<RA, RB, INV, COLFAST, LOGN>(io, lds, gp.tile, log_n, tw, pc.q, fin);
 }
 
 typedef void (*PassFn)(PassArgs);
 
-template <bool INV, bool COLFAST>
-PassFn pick(int logb) {
-  switch (logb) {
-    case 5: return ntt_pass_kernel<3, 2, INV, COLFAST>;
-    case 6: return ntt_pass_kernel<3, 3, INV, COLFAST>;
-    case 7: return ntt_pass_kernel<4, 3, INV, COLFAST>;
-    case 8: return ntt_pass_kernel<4, 4, INV, COLFAST>;
-  }
-  return nullptr;
-}
-
 int launch_pass(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs, int logb, bool inv, bool colfast) {
-  PassFn fn = inv ? (colfast ? pick<true, true>(logb) : pick<true, false>(logb))
-                  : (colfast ? pick<false, true>(logb) : pick<false, false>(logb));
+  const int log_n = (int)c->log_n;
+  PassFn fn = inv ? (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, true)
+                             : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, false))
+                  : (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, true)
+                             : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, false));
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
   const double limbs = (double)njobs * batch;
   TraceScope ts(c, s, "ntt_pass", limbs * (c->N / 2) * logb + ((inv && a.final_pass && a.scale_mode) ? limbs * c->N : 0));
@@ -106,10 +105,8 @@ int ntt_run_scaled(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, si
   a.final_pass = 0;
   int rc;
   if (!inverse) {
-    a.s0 = 0;
     rc = launch_pass(c, s, a, batch, jobs.n, logb_col(log_n), false, true);
   } else {
-    a.s0 = (uint32_t)logb_col(log_n);
     rc = launch_pass(c, s, a, batch, jobs.n, logb_row(log_n), true, false);
   }
   if (rc) return rc;
@@ -118,10 +115,8 @@ int ntt_run_scaled(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, si
   for (int i = 0; i < jobs.n; ++i) a.src_limb[i] = jobs.dst_limb[i];
   a.final_pass = 1;
   if (!inverse) {
-    a.s0 = (uint32_t)logb_col(log_n);
     return launch_pass(c, s, a, batch, jobs.n, logb_row(log_n), false, false);
   }
-  a.s0 = 0;
   return launch_pass(c, s, a, batch, jobs.n, logb_col(log_n), true, true);
 }
 
@@ -149,7 +144,6 @@ int ntt_pass_only(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, siz
   a.dst_bstride = dst_bstride;
   a.final_pass = first ? 0 : 1;
   const bool colpass = (inverse != first);  // forward first / inverse second
-  a.s0 = colpass ? 0u : (uint32_t)logb_col(log_n);
   return launch_pass(c, s, a, batch, jobs.n, colpass ? logb_col(log_n) : logb_row(log_n), inverse, colpass);
 }
 

@@ -49,18 +49,21 @@ __device__ __forceinline__ uint32_t tile_index(uint32_t tile, uint32_t row, uint
   return ((tile * kCols + col) << logb) + row;
 }
 
-// LDS position of tile element (row, col).  Column pass: row-major with 16
-// padding words after every 2^RB rows; row pass: column-major with the low 4
-// row bits XOR-ed with the next 4 and 16 padding words per column.  Both make
-// the register rounds' 64-bit LDS accesses hit distinct bank pairs.
+// LDS position of tile element (row, col), unpadded (a 2^16 tile takes
+// exactly 32 KiB, so five workgroups fit a CU's 160 KiB).  Column pass:
+// row-major with row bit 0 flipped by row bit RB; row pass: column-major with
+// the low 4 row bits XOR-ed with the next 4 and row bit 4 flipped by column
+// bit 0.  In both register rounds and in the staging loops every 64-bit
+// access of a wave then shares its bank pair with at most one other lane
+// (the minimum for 64 lanes x 8 bytes on 64 four-byte banks).
 template <bool COLFAST, int RB, int ROWS>
 __device__ __forceinline__ int lds_index(int row, int col) {
-  if (COLFAST) return row * kCols + col + (row >> RB) * 16;
-  return col * (ROWS + 16) + (row ^ ((row >> 4) & 15));
+  if (COLFAST) return (row ^ ((row >> RB) & 1)) * kCols + col;
+  return col * ROWS + (row ^ ((row >> 4) & 15) ^ ((col & 1) << 4));
 }
 template <bool COLFAST, int RB, int ROWS>
 constexpr int lds_words() {
-  return COLFAST ? ROWS * kCols + (ROWS >> RB) * 16 : kCols * (ROWS + 16);
+  return ROWS * kCols;
 }
 
 __device__ __forceinline__ void load_tw(const uint64_t* tw, uint32_t ti, uint64_t& w, uint64_t& wp) {
@@ -138,9 +141,18 @@ struct Finish {
   uint64_t inv1;   // floor(2^64/q), forward reduction
 };
 
-template <int RA, int RB, bool INV, bool COLFAST, bool LAZY, class IO>
-__device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t tile, int log_n, uint32_t s0,
+// Pass geometry for N = 2^log_n: the column pass covers the first logb_col
+// stages of the forward transform.
+__host__ __device__ constexpr int logb_col(int log_n) { return (log_n + 1) / 2; }
+__host__ __device__ constexpr int logb_row(int log_n) { return log_n - logb_col(log_n); }
+
+// LOGN > 0 fixes log N at compile time (index arithmetic folds to constants);
+// LOGN = 0 takes it from log_n_rt.
+template <int RA, int RB, bool INV, bool COLFAST, bool LAZY, int LOGN, class IO>
+__device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t tile, int log_n_rt,
                                           const uint64_t* tw, uint64_t q, const Finish& fin) {
+  const int log_n = LOGN ? LOGN : log_n_rt;
+  const uint32_t s0 = COLFAST ? 0u : (uint32_t)logb_col(log_n);  // row pass follows the column pass
   constexpr int LOGB = RA + RB;
   constexpr int ROWS = 1 << LOGB;
   constexpr int TILE = ROWS * kCols;
@@ -234,20 +246,67 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
 }
 
 // Dispatch on the butterfly form (lazy forward for small primes).
-template <int RA, int RB, bool INV, bool COLFAST, class IO>
-__device__ __forceinline__ void run_pass(const IO& io, uint64_t* lds, uint32_t tile, int log_n, uint32_t s0,
+template <int RA, int RB, bool INV, bool COLFAST, int LOGN, class IO>
+__device__ __forceinline__ void run_pass(const IO& io, uint64_t* lds, uint32_t tile, int log_n,
                                          const uint64_t* tw, uint64_t q, const Finish& fin) {
   if (!INV && q < (1ull << 57))
-    pass_body<RA, RB, INV, COLFAST, true>(io, lds, tile, log_n, s0, tw, q, fin);
+    pass_body<RA, RB, INV, COLFAST, true, LOGN>(io, lds, tile, log_n, tw, q, fin);
   else
-    pass_body<RA, RB, INV, COLFAST, false>(io, lds, tile, log_n, s0, tw, q, fin);
+    pass_body<RA, RB, INV, COLFAST, false, LOGN>(io, lds, tile, log_n, tw, q, fin);
 }
 
-// Pass geometry for N = 2^log_n: the column pass covers the first logb_col
-// stages of the forward transform.
-__host__ __device__ inline int logb_col(int log_n) { return (log_n + 1) / 2; }
-__host__ __device__ inline int logb_row(int log_n) { return log_n - logb_col(log_n); }
 inline uint32_t pass_tiles(uint32_t n, int logb) { return n / ((1u << logb) * kCols); }
+
+// Position of a row-pass workgroup in a (tiles, jobs, items) grid.  The chip
+// hands workgroups to its 8 XCDs round-robin by linear id and each XCD has its
+// own L2.  A row pass reads about twice its tile's data in twiddles, shared by
+// every limb on the same prime, so the linear id is remapped to give each XCD
+// a contiguous stretch of the order (tile fastest, then item, then job): the
+// items that share a prime's twiddle table then run back to back on one L2,
+// while the workgroups in flight still cover contiguous addresses.
+constexpr uint32_t kXcds = 8;
+struct GridPos {
+  uint32_t tile;
+  int job, item;
+};
+// Start of part c when n things are split into kXcds near-equal contiguous
+// parts (the first n % kXcds parts one longer).
+__device__ __forceinline__ uint32_t xcd_part_start(uint32_t c, uint32_t n) {
+  const uint32_t m = n / kXcds, r = n % kXcds;
+  return c < r ? c * (m + 1) : r * (m + 1) + (c - r) * m;
+}
+__device__ __forceinline__ GridPos row_grid_pos() {
+  const uint32_t gx = gridDim.x, gy = gridDim.y, gz = gridDim.z;
+  const uint32_t b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const uint32_t logical = xcd_part_start(b % kXcds, gx * gy * gz) + b / kXcds;
+  GridPos p;
+  p.tile = logical % gx;
+  const uint32_t rest = logical / gx;
+  p.item = (int)(rest % gz);
+  // jobs in the order 0, 8, 16, ..., 1, 9, 17, ...: every XCD gets jobs from
+  // across the range (the special primes, at the end, cost more per limb)
+  const uint32_t jl = rest / gz, m = gy / kXcds, r = gy % kXcds;
+  uint32_t cls, idx;
+  if (jl < r * (m + 1)) {
+    cls = jl / (m + 1);
+    idx = jl % (m + 1);
+  } else {
+    cls = r + (jl - r * (m + 1)) / m;
+    idx = (jl - r * (m + 1)) % m;
+  }
+  p.job = (int)(cls + kXcds * idx);
+  return p;
+}
+
+// Kernel instance for a pass of 2^logb rows at N = 2^log_n: N = 2^16 gets a
+// compile-time specialisation, other sizes the generic one.
+#define CKKS_PICK_PASS(kern, log_n, logb, ...)                   \
+  ((log_n) == 16 && (logb) == 8 ? kern<4, 4, 16, ##__VA_ARGS__>  \
+   : (logb) == 5              ? kern<3, 2, 0, ##__VA_ARGS__>   \
+   : (logb) == 6              ? kern<3, 3, 0, ##__VA_ARGS__>   \
+   : (logb) == 7              ? kern<4, 3, 0, ##__VA_ARGS__>   \
+   : (logb) == 8              ? kern<4, 4, 0, ##__VA_ARGS__>   \
+                              : nullptr)
 
 // Element I/O policy.  load(j) supplies input word j; after_load(j, v) runs
 // once per word after all loads of a staging loop (side outputs); fetch(j)

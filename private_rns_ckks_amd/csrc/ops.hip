@@ -128,6 +128,9 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
 
 using namespace ckks;
 
+// device buffers are read and written with 16-byte vector accesses
+static bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
 #define CTX_OR_FAIL(ctx)                                             \
   if (!(ctx)) return set_error(CKKS_EINVAL, "ctx is NULL");         \
   if (hipSetDevice((ctx)->device) != hipSuccess) return set_error(CKKS_EHIP, "hipSetDevice failed")
@@ -138,6 +141,7 @@ int ckks_ntt(ckks_ctx* ctx, uint64_t* d_data, int npoly, int limb_begin, int n_l
              ckks_stream_t stream) {
   CTX_OR_FAIL(ctx);
   if (!d_data || npoly < 0 || n_limb < 0) return set_error(CKKS_EINVAL, "bad data pointer or count");
+  if (misaligned(d_data)) return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   if (limb_begin < 0 || limb_begin + n_limb > (int)(ctx->L + ctx->K)) return set_error(CKKS_ERANGE, "limb range outside the basis");
   if (npoly == 0 || n_limb == 0) return CKKS_OK;
   if (npoly > 65535) return set_error(CKKS_EINVAL, "npoly too large");
@@ -157,6 +161,7 @@ int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npo
                    int domain, ckks_stream_t stream) {
   CTX_OR_FAIL(ctx);
   if (!d_in || !d_out || npoly < 0) return set_error(CKKS_EINVAL, "bad pointer or count");
+  if (misaligned(d_in) || misaligned(d_out)) return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   int rc = check_level(ctx, level);
   if (rc || (rc = check_galois(ctx, galois_elt))) return rc;
   if (domain != 0 && domain != 1) return set_error(CKKS_EINVAL, "domain must be 0 (NTT) or 1 (coefficient)");
@@ -171,6 +176,8 @@ int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk,
                    ckks_stream_t stream) {
   CTX_OR_FAIL(ctx);
   if (!d_poly || !d_evk || !d_out) return set_error(CKKS_EINVAL, "NULL pointer");
+  if (misaligned(d_poly) || misaligned(d_evk) || misaligned(d_out))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (ctx->K == 0) return set_error(CKKS_EPARAM, "key switching needs special primes");
@@ -194,7 +201,10 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
   for (int b = 0; b < batch; ++b) {
     if ((rc = check_galois(ctx, galois_elts[b]))) return rc;
     if (galois_elts[b] != 1 && !d_evks[b]) return set_error(CKKS_EINVAL, "NULL key pointer");
+    if (galois_elts[b] != 1 && misaligned(d_evks[b])) return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   }
+  if (misaligned(d_ct_in) || misaligned(d_ct_out))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   if (batch > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
   return rotate_batch(ctx, stream, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
                       flags);
@@ -203,6 +213,7 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
 int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch, int level, ckks_stream_t stream) {
   CTX_OR_FAIL(ctx);
   if (!d_in || !d_out || batch < 0) return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  if (misaligned(d_in) || misaligned(d_out)) return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
@@ -216,6 +227,8 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
                            uint64_t* d_out, int batch, int level, unsigned flags, ckks_stream_t stream) {
   CTX_OR_FAIL(ctx);
   if (!d_a || !d_b || !d_rlk || !d_out || batch < 0) return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  if (misaligned(d_a) || misaligned(d_b) || misaligned(d_rlk) || misaligned(d_out))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (flags & ~CKKS_NO_RESCALE) return set_error(CKKS_EINVAL, "unknown flag");
@@ -279,6 +292,12 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
     return set_error(CKKS_EINVAL, "NULL pointer or bad size");
   if ((n1 > 1 && (!baby_galois || !d_evk_baby)) || (n2 > 1 && (!giant_galois || !d_evk_giant)))
     return set_error(CKKS_EINVAL, "missing rotation keys");
+  if (misaligned(d_x) || misaligned(d_diags) || misaligned(d_y))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
+  for (int b = 1; b < n1; ++b)
+    if (!d_evk_baby[b - 1] || misaligned(d_evk_baby[b - 1])) return set_error(CKKS_EINVAL, "NULL or misaligned key pointer");
+  for (int g = 1; g < n2; ++g)
+    if (!d_evk_giant[g - 1] || misaligned(d_evk_giant[g - 1])) return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (flags & ~CKKS_NO_RESCALE) return set_error(CKKS_EINVAL, "unknown flag");
