@@ -40,6 +40,52 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+# Sources the dominant kernel is compiled from: HBM traffic taken with
+# rocprofv3 counters is reported only while these are unchanged.
+KERNEL_SOURCES = ["keyswitch.hip", "ntt_core.h", "arith.h", "internal.h", "kernels.h", "automorph.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ntt_row_ip_c3_traffic.txt")
+
+
+def kernel_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "private_rns_ckks_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
+    reading for a copy of known size), or None when the kernel's sources have
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch):
+    """A plain device copy of 1 GiB, three times: the reference reading for
+    the FETCH_SIZE / WRITE_SIZE counters (each copy reads and writes 2^30 B)."""
+    a = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
     """The CPU oracle on a bounded sample of the batch (same words)."""
     import oracle
@@ -71,6 +117,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-ntt", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first copy 1 GiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -88,6 +136,8 @@ def main():
     N, L, K, dnum = 1 << cfg["log_n"], cfg["L"], cfg["K"], cfg["dnum"]
     level, B = L - 1, cfg["batch"]
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
     q = lib.ckks_find_primes(cfg["log_n"], cfg["q_bits"], L)
     p = lib.ckks_find_primes(cfg["log_n"], cfg["p_bits"], K)
     ctx = lib.Context(cfg["log_n"], q, p, dnum, device=0)
@@ -137,7 +187,7 @@ def main():
             "peak": round(VALU_PEAK_TOPS, 2),
             "unit": "Tops/s",
             "frac": round(achieved / VALU_PEAK_TOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(avg_s * 1e6, 2),
             "launches": kstat["launches"],
             "work_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"], kstat["ops_per_unit"]),

@@ -126,8 +126,12 @@ typedef struct {
 
 /* Start tracing the kernel family `kernel`: every later launch of it on any
  * stream is bracketed by a HIP event pair on that stream.  Families:
- * "ntt_pass", "automorph", "modup", "inner_product", "moddown_conv",
- * "combine", "rescale", "tensor", "ptmac", "add".  NULL or "" stops tracing.
+ * "ntt_pass" (plain NTT / inverse NTT passes), the key switch's fused
+ * passes "intt_row_gather" (automorphism gather + inverse row pass),
+ * "ntt_row_ip" (forward row pass + key inner product) and "ntt_row_combine"
+ * (forward row pass + final combination), "automorph", "modup",
+ * "moddown_conv", "rescale", "tensor", "ptmac", "add".  NULL or "" stops
+ * tracing.
  * Tracing adds two event records per traced launch and nothing else. */
 int ckks_trace_begin(ckks_ctx* ctx, const char* kernel);
 /* Waits for the recorded events, returns the totals and stops tracing. */

@@ -34,8 +34,9 @@ EXPORTED = [
     "ckks_mul_relin_rescale", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
 ]
 
-# Kernel family whose launches dominate a rotation batch (by rocprofv3 time).
-DOMINANT_KERNEL = "ntt_pass"
+# Kernel whose launches take the largest share of a rotation batch (by
+# rocprofv3 time): the forward row pass fused with the key inner product.
+DOMINANT_KERNEL = "ntt_row_ip"
 # int32 VALU operations per 64-bit modmul-class operation: the 10 32x32-bit
 # partial products of a 64-bit Shoup (or Barrett) multiplication plus 6 int32
 # adds/subtracts to combine them and apply the quotient.

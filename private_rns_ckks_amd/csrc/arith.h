@@ -142,12 +142,17 @@ __device__ __forceinline__ U128 acc3_value(const Acc3& A) {
   return r;
 }
 
-// x mod q for x.hi < 2^64, using the approximate Shoup product for the high
-// word: hi*2^64 = hi*r64 (mod q).
-__device__ __forceinline__ uint64_t reduce128_lazy(U128 x, uint64_t q, uint64_t r64, uint64_t r64p, uint64_t inv1) {
+// A value congruent to x mod q in [0, 6q), for x.hi < 2^64, using the
+// approximate Shoup product for the high word: hi*2^64 = hi*r64 (mod q).
+__device__ __forceinline__ uint64_t reduce128_6q(U128 x, uint64_t q, uint64_t r64, uint64_t r64p, uint64_t inv1) {
   const uint64_t a = mul_shoup_lazy(x.hi, r64, r64p, q);  // [0, 4q)
   const uint64_t b = x.lo - mulhi64(x.lo, inv1) * q;      // [0, 2q)
-  uint64_t s = a + b;                                      // [0, 6q) < 2^63
+  return a + b;                                            // [0, 6q) < 2^63
+}
+
+// x mod q for x.hi < 2^64.
+__device__ __forceinline__ uint64_t reduce128_lazy(U128 x, uint64_t q, uint64_t r64, uint64_t r64p, uint64_t inv1) {
+  uint64_t s = reduce128_6q(x, q, r64, r64p, inv1);
   s = s >= 4 * q ? s - 4 * q : s;
   s = s >= 2 * q ? s - 2 * q : s;
   return s >= q ? s - q : s;
@@ -164,6 +169,11 @@ struct DotMod {
 __device__ __forceinline__ uint64_t acc3_reduce(const Acc3& A, const uint64_t q, uint64_t r64, uint64_t r64p,
                                                 uint64_t inv1) {
   return reduce128_lazy(acc3_value(A), q, r64, r64p, inv1);
+}
+// The same sum, congruent mod q, in [0, 6q).
+__device__ __forceinline__ uint64_t acc3_reduce_6q(const Acc3& A, const uint64_t q, uint64_t r64, uint64_t r64p,
+                                                   uint64_t inv1) {
+  return reduce128_6q(acc3_value(A), q, r64, r64p, inv1);
 }
 
 __device__ __forceinline__ uint64_t add_mod(uint64_t a, uint64_t b, uint64_t q) {

@@ -146,6 +146,9 @@ static int build_tables(Ctx* c) {
   if ((rc = upload((void**)&c->d_tw_inv, iv.data(), iv.size() * 8))) return rc;
   if (c->K == 0) return CKKS_OK;
 
+  // Basis-conversion constants (below 2^60) are stored split in 30-bit halves,
+  // lo | hi << 32, the operand form of the split multiply-accumulate.
+  auto split30 = [](uint64_t v) { return (v & 0x3fffffffull) | ((v >> 30) << 32); };
   // ModUp constants per (level, digit)
   std::vector<uint64_t> mu;
   c->modup.assign(c->L, {});
@@ -165,16 +168,17 @@ static int build_tables(Ctx* c) {
         mu.push_back(v);
         mu.push_back(shoup(v, qi));
       }
-      for (int x = 0; x < a; ++x) {
+      // rows for x >= a are zero: the kernel always runs conv_rows(alpha) sources
+      for (int x = 0; x < conv_rows(c->alpha); ++x) {
         for (int t = 0; t < next; ++t) {
-          if (t >= en.lo && t < en.hi) {
+          if (x >= a || (t >= en.lo && t < en.hi)) {
             mu.push_back(0);
             continue;
           }
           uint64_t mt = c->mod[c->ext_prime((int)level, t)], prod = 1;
           for (int y = 0; y < a; ++y)
             if (y != x) prod = mulmod(prod, c->mod[en.lo + y] % mt, mt);
-          mu.push_back(prod);
+          mu.push_back(split30(prod));
         }
       }
       c->modup[level].push_back(en);
@@ -195,8 +199,9 @@ static int build_tables(Ctx* c) {
     md.push_back(shoup(v, pk));
   }
   c->md.conv = md.size();
-  for (uint32_t k = 0; k < K; ++k)
-    for (uint32_t i = 0; i < L; ++i) md.push_back(invmod(c->mod[L + k] % c->mod[i], c->mod[i]));  // phat_k / P = 1/p_k
+  for (uint32_t k = 0; k < (uint32_t)conv_rows(K); ++k)  // rows k >= K are zero
+    for (uint32_t i = 0; i < L; ++i)
+      md.push_back(k < K ? split30(invmod(c->mod[L + k] % c->mod[i], c->mod[i])) : 0);  // phat_k / P = 1/p_k
   c->md.pinv = md.size();
   for (uint32_t i = 0; i < L; ++i) {
     uint64_t qi = c->mod[i], prod = 1;

@@ -28,6 +28,9 @@ struct PrimeConst {
 //   [0, 2a)                : {[qhat_i^-1 * N^-1]_{q_i}, Shoup} for the a digit limbs
 //   [2a, 2a + a*next)      : [qhat_i]_{m_t}, row i, column t over the extended
 //                            basis at level l (next = l+1+K); unused in-digit columns are 0
+// Basis-conversion source count rounded up to the kernels' unrolled count.
+inline int conv_rows(uint32_t sources) { return sources <= 8 ? 8 : 16; }
+
 struct ModUpEntry {
   int lo, hi;       // digit limbs [lo, hi)
   size_t offset;    // word offset into d_modup

@@ -20,17 +20,6 @@ struct ModUpArgs {
   uint64_t offset[64];
 };
 
-struct IPArgs {
-  const uint64_t* d;    // NTT-form input, [level+1][N] per item
-  const uint64_t* ext;  // NTT-form ModUp output, [beta][next][N] per item
-  uint64_t* acc;        // [2][next][N] per item
-  uint64_t d_bstride, ext_bstride, acc_bstride;
-  const uint64_t* evk[kMaxChunk];  // [dnum][2][L+K][N]
-  const PrimeConst* prime;
-  uint32_t n;
-  int level, next, beta, alpha, L, K;
-};
-
 struct ModDownArgs {
   const uint64_t* acc;  // [2][next][N] per item; special limbs hold y_k (coefficient form)
   uint64_t* w;          // [2][level+1][N] per item (coefficient form)
@@ -39,20 +28,6 @@ struct ModDownArgs {
   const PrimeConst* prime;
   uint32_t n;
   int level, next, L, K;
-};
-
-struct CombineArgs {
-  const uint64_t* acc;  // [2][next][N] per item (NTT form)
-  const uint64_t* w;    // [2][level+1][N] per item (NTT form)
-  const uint64_t* add[2];    // optional [level+1][N] per item per component
-  const uint64_t* accum;     // optional [2][level+1][N] per item
-  uint64_t* out;             // [2][out_comp_limbs][N] per item
-  uint64_t acc_bstride, w_bstride, add_bstride, accum_bstride, out_bstride;
-  uint32_t add_g[kMaxChunk];  // gather `add` through X -> X^g (0 = none)
-  const uint64_t* pinv;       // [L][2]
-  const PrimeConst* prime;
-  uint32_t n;
-  int level, next, out_comp_limbs, log_n;
 };
 
 struct RescaleArgs {
@@ -108,9 +83,7 @@ int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* ou
 int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl,
                            uint64_t pstride, uint32_t ginv);
 int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch);
-int launch_inner_product(Ctx* c, hipStream_t s, IPArgs& a, int batch);
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch);
-int launch_combine(Ctx* c, hipStream_t s, CombineArgs& a, int batch);
 int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
 int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);

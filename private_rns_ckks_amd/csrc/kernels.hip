@@ -37,189 +37,112 @@ __global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64
   }
 }
 
+// Read-only tables read with wave-uniform indices: through the constant
+// address space the compiler fetches them with scalar loads, and the
+// multiply-accumulates take them straight from SGPRs.
+typedef const __attribute__((address_space(4))) uint64_t* ConstU64;
+typedef const __attribute__((address_space(4))) PrimeConst* ConstPrime;
+
+// The constants a reduction mod prime i needs.
+struct RedConst {
+  uint64_t q, r64, r64p, inv1;
+};
+__device__ __forceinline__ RedConst red_const(ConstPrime p, int i) {
+  RedConst r;
+  r.q = p[i].q;
+  r.r64 = p[i].r64;
+  r.r64p = p[i].r64p;
+  r.inv1 = p[i].inv1;
+  return r;
+}
+
+// Split multiply-accumulate of NS sources against one target's constants
+// (rows of a zero-padded table, stride `stride`), reduced mod the target q:
+// in [0, 6q) for NS = 8, in [0, q) for NS = 16.  Both ranges are valid inputs
+// of the forward NTT that follows (lazy butterflies start from words below
+// 6q and stay below 70q < 2^64 for q < 2^57; the others accept words below
+// 8q).  NS is 8 or 16; sources past the real count have zero constants and
+// words.
+template <int NS>
+__device__ __forceinline__ uint64_t conv_dot(const uint32_t (&yl)[NS], const uint32_t (&yh)[NS], ConstU64 conv,
+                                             int stride, const RedConst& pc) {
+  uint64_t cw[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) cw[i] = conv[i * stride];
+  uint64_t r = 0;
+#pragma unroll
+  for (int g = 0; g < NS; g += 8) {
+    Acc3 A = {0, 0, 0};
+#pragma unroll
+    for (int i = g; i < g + 8; ++i) acc3_mac(A, yl[i], yh[i], (uint32_t)cw[i], (uint32_t)(cw[i] >> 32));
+    if (NS == 8) return acc3_reduce_6q(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    const uint64_t v = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    r = g ? add_mod(r, v, pc.q) : v;
+  }
+  return r;
+}
+
 // ModUp for digit blockIdx.y of batch item blockIdx.z.
 // x: the digit limbs already multiplied by [qhat_i^-1]_{q_i} (canonical y_i),
 // [level+1][N] per item.  out: [beta][next][N] per item; for every target limb
-// t outside the digit, out_t = sum_i y_i [qhat_i]_{m_t} mod m_t (exact).
-// The conversion constants and target moduli are staged in LDS once per
-// workgroup so the target loop reads them with broadcast LDS loads.
+// t outside the digit, out_t = sum_i y_i [qhat_i]_{m_t} mod m_t (exact,
+// left in the range conv_dot gives).
+// Constants [qhat_i]_{m_t}: [NS][next], split into 30-bit halves, zero rows
+// past the digit's size.
+template <int NS>
 __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
-  __shared__ uint64_t s_conv[16 * kMaxExt];
-  __shared__ uint64_t s_pc[4 * kMaxExt];
   const int j = blockIdx.y;
   const int lo = a.lo[j], hi = a.hi[j], na = hi - lo;
-  const uint64_t* conv = a.tables + a.offset[j] + 2 * na;
-  for (int k = threadIdx.x; k < na * a.next; k += blockDim.x) s_conv[k] = conv[k];
-  for (int t = threadIdx.x; t < a.next; t += blockDim.x) {
-    const PrimeConst& pc = a.prime[t <= a.level ? t : a.L + (t - a.level - 1)];
-    s_pc[4 * t] = pc.q;
-    s_pc[4 * t + 1] = pc.r64;
-    s_pc[4 * t + 2] = pc.r64p;
-    s_pc[4 * t + 3] = pc.inv1;
-  }
-  __syncthreads();
+  const ConstU64 conv = (ConstU64)(a.tables + a.offset[j] + 2 * na);
+  const ConstPrime prime = (ConstPrime)a.prime;
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t* x = a.x + blockIdx.z * a.x_bstride + (uint64_t)lo * a.n + c;
   uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
-  uint32_t yl[16], yh[16];
+  uint32_t yl[NS], yh[NS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < na) {
-      const uint64_t y = x[(uint64_t)i * a.n];
-      yl[i] = lo30(y);
-      yh[i] = hi30(y);
-    }
+  for (int i = 0; i < NS; ++i) {
+    const uint64_t y = i < na ? x[(uint64_t)i * a.n] : 0;
+    yl[i] = lo30(y);
+    yh[i] = hi30(y);
   }
   for (int t = 0; t < a.next; ++t) {
     if (t >= lo && t < hi) continue;
-    const uint64_t q = s_pc[4 * t], r64 = s_pc[4 * t + 1], r64p = s_pc[4 * t + 2], inv1 = s_pc[4 * t + 3];
-    Acc3 A = {0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < na) {
-        const uint64_t cv = s_conv[i * a.next + t];
-        acc3_mac(A, yl[i], yh[i], lo30(cv), hi30(cv));
-      }
-    }
-    uint64_t r = acc3_reduce(A, q, r64, r64p, inv1);
-    if (na > 8) {
-      Acc3 B = {0, 0, 0};
-#pragma unroll
-      for (int i = 8; i < 16; ++i) {
-        if (i < na) {
-          const uint64_t cv = s_conv[i * a.next + t];
-          acc3_mac(B, yl[i], yh[i], lo30(cv), hi30(cv));
-        }
-      }
-      r = add_mod(r, acc3_reduce(B, q, r64, r64p, inv1), q);
-    }
-    out[(uint64_t)t * a.n] = r;
+    const RedConst pc = red_const(prime, t <= a.level ? t : a.L + (t - a.level - 1));
+    out[(uint64_t)t * a.n] = conv_dot<NS>(yl, yh, conv + t, a.next, pc);
   }
-}
-
-// Inner product with the key digits for extended limb t = blockIdx.y:
-// acc_b[t] = sum_j d_j[t] * evk_j.b[t], acc_a[t] likewise, where d_j[t] is the
-// NTT-form input itself for limbs inside digit j and the NTT-form ModUp output
-// otherwise.
-__global__ __launch_bounds__(256) void inner_product_kernel(IPArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int t = blockIdx.y;
-  const int item = blockIdx.z;
-  const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
-  const PrimeConst pc = a.prime[keyl];
-  const uint64_t* evk = a.evk[item];
-  const uint64_t LKN = (uint64_t)(a.L + a.K) * a.n;
-  uint64_t rb = 0, ra = 0;
-  // digits in groups of 8 (the split accumulator's capacity); within a group
-  // every load is issued before the first multiply
-  for (int j0 = 0; j0 < a.beta; j0 += 8) {
-    uint64_t d[8], kb[8], ka[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = j0 + jj;
-      if (j < a.beta) {
-        const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
-        d[jj] = in_digit ? a.d[item * a.d_bstride + (uint64_t)t * a.n + c]
-                         : a.ext[item * a.ext_bstride + ((uint64_t)j * a.next + t) * a.n + c];
-        kb[jj] = evk[(2 * j) * LKN + (uint64_t)keyl * a.n + c];
-        ka[jj] = evk[(2 * j + 1) * LKN + (uint64_t)keyl * a.n + c];
-      }
-    }
-    Acc3 ab = {0, 0, 0}, aa = {0, 0, 0};
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (j0 + jj < a.beta) {
-        const uint32_t dl = lo30(d[jj]), dh = hi30(d[jj]);
-        acc3_mac(ab, dl, dh, lo30(kb[jj]), hi30(kb[jj]));
-        acc3_mac(aa, dl, dh, lo30(ka[jj]), hi30(ka[jj]));
-      }
-    }
-    rb = add_mod(rb, acc3_reduce(ab, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-    ra = add_mod(ra, acc3_reduce(aa, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-  }
-  uint64_t* out = a.acc + item * a.acc_bstride + (uint64_t)t * a.n + c;
-  out[0] = rb;
-  out[(uint64_t)a.next * a.n] = ra;
 }
 
 // ModDown conversion for component blockIdx.y of item blockIdx.z.
 // The special limbs of acc hold y_k = z_k [phat_k^-1]_{p_k} (canonical,
 // coefficient form).  Centred lift: y_k counts as negative when
 // y_k > (p_k-1)/2, and then sum_k ybar_k [phat_k P^-1]_{q_i} =
-// sum_k y_k [1/p_k]_{q_i} - #negative  (mod q_i).  w: [2][level+1][N] per item.
+// sum_k y_k [1/p_k]_{q_i} - #negative  (mod q_i).  w: [2][level+1][N] per item,
+// in the range conv_dot gives.
+// Constants [1/p_k]_{q_i}: [NS][L], split into 30-bit halves, zero rows past K.
+template <int NS>
 __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
-  __shared__ uint64_t s_conv[16 * 64];
-  __shared__ uint64_t s_pc[4 * 64];
   const int nq = a.level + 1;
-  for (int k = threadIdx.x; k < a.K * nq; k += blockDim.x) s_conv[k] = a.conv[(k / nq) * a.L + (k % nq)];
-  for (int i = threadIdx.x; i < nq; i += blockDim.x) {
-    const PrimeConst& pc = a.prime[i];
-    s_pc[4 * i] = pc.q;
-    s_pc[4 * i + 1] = pc.r64;
-    s_pc[4 * i + 2] = pc.r64p;
-    s_pc[4 * i + 3] = pc.inv1;
-  }
-  __syncthreads();
+  const ConstU64 conv = (ConstU64)a.conv;
+  const ConstPrime prime = (ConstPrime)a.prime;
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int comp = blockIdx.y;
   const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.next + nq) * a.n + c;
-  uint32_t yl[16], yh[16];
+  uint32_t yl[NS], yh[NS];
   uint32_t neg = 0;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < NS; ++k) {
+    uint64_t v = 0;
     if (k < a.K) {
-      const uint64_t v = acc[(uint64_t)k * a.n];
-      neg += v > (a.prime[a.L + k].q >> 1) ? 1u : 0u;
-      yl[k] = lo30(v);
-      yh[k] = hi30(v);
+      v = acc[(uint64_t)k * a.n];
+      neg += v > (prime[a.L + k].q >> 1) ? 1u : 0u;
     }
+    yl[k] = lo30(v);
+    yh[k] = hi30(v);
   }
   uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * nq * a.n + c;
   for (int i = 0; i < nq; ++i) {
-    const uint64_t q = s_pc[4 * i], r64 = s_pc[4 * i + 1], r64p = s_pc[4 * i + 2], inv1 = s_pc[4 * i + 3];
-    Acc3 A = {0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < a.K) {
-        const uint64_t cv = s_conv[k * nq + i];
-        acc3_mac(A, yl[k], yh[k], lo30(cv), hi30(cv));
-      }
-    }
-    uint64_t r = acc3_reduce(A, q, r64, r64p, inv1);
-    if (a.K > 8) {
-      Acc3 B = {0, 0, 0};
-#pragma unroll
-      for (int k = 8; k < 16; ++k) {
-        if (k < a.K) {
-          const uint64_t cv = s_conv[k * nq + i];
-          acc3_mac(B, yl[k], yh[k], lo30(cv), hi30(cv));
-        }
-      }
-      r = add_mod(r, acc3_reduce(B, q, r64, r64p, inv1), q);
-    }
-    w[(uint64_t)i * a.n] = sub_mod(r, neg, q);
-  }
-}
-
-// out[comp][i] = acc[comp][i] * P^-1 - w[comp][i]  (+ add[comp][i] gathered
-// through X -> X^g when add_g != 0)  (+ accum[comp][i]).
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int i = blockIdx.y;
-  const int item = blockIdx.z;
-  const PrimeConst pc = a.prime[i];
-  const uint64_t q = pc.q;
-  for (int comp = 0; comp < 2; ++comp) {
-    const uint64_t av = a.acc[item * a.acc_bstride + ((uint64_t)comp * a.next + i) * a.n + c];
-    const uint64_t wv = a.w[item * a.w_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c];
-    uint64_t r = sub_mod(reduce_2q(mul_shoup(av, a.pinv[2 * i], a.pinv[2 * i + 1], q), q), wv, q);
-    if (a.add[comp]) {
-      const uint32_t g = a.add_g[item];
-      const uint32_t src = g ? automorph_src(c, g, a.log_n) : c;
-      r = add_mod(r, a.add[comp][item * a.add_bstride + (uint64_t)i * a.n + src], q);
-    }
-    if (a.accum) r = add_mod(r, a.accum[item * a.accum_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c], q);
-    a.out[item * a.out_bstride + ((uint64_t)comp * a.out_comp_limbs + i) * a.n + c] = r;
+    const RedConst pc = red_const(prime, i);
+    w[(uint64_t)i * a.n] = sub_mod(conv_dot<NS>(yl, yh, conv + i, a.L, pc), neg, pc.q);
   }
 }
 
@@ -352,28 +275,20 @@ int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch) {
     units += na + (double)(a.next - na) * (na + 1);
   }
   TraceScope ts(c, s, "modup", units * batch * c->N);
-  hipLaunchKernelGGL(modup_kernel, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
-  LAUNCH_CHECK();
-  return CKKS_OK;
-}
-
-int launch_inner_product(Ctx* c, hipStream_t s, IPArgs& a, int batch) {
-  TraceScope ts(c, s, "inner_product", (double)batch * a.next * 2 * (a.beta + 1) * c->N);
-  hipLaunchKernelGGL(inner_product_kernel, dim3(c->N / 256, a.next, batch), dim3(256), 0, s, a);
+  if (conv_rows(c->alpha) == 8)
+    hipLaunchKernelGGL(modup_kernel<8>, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(modup_kernel<16>, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
   TraceScope ts(c, s, "moddown_conv", (double)batch * 2 * (a.K + (double)(a.level + 1) * (a.K + 1)) * c->N);
-  hipLaunchKernelGGL(moddown_conv_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
-  LAUNCH_CHECK();
-  return CKKS_OK;
-}
-
-int launch_combine(Ctx* c, hipStream_t s, CombineArgs& a, int batch) {
-  TraceScope ts(c, s, "combine", (double)batch * 2 * (a.level + 1) * c->N);
-  hipLaunchKernelGGL(combine_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
+  if (conv_rows(c->K) == 8)
+    hipLaunchKernelGGL(moddown_conv_kernel<8>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(moddown_conv_kernel<16>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -117,13 +117,49 @@ __device__ __forceinline__ int ip_lds(int row, int col) {
   return col * (1 << LOGB) + (row ^ (((row >> 6) & 3) << 3) ^ ((row >> 5) & 7));
 }
 
+// The row pass's twiddles for one tile, staged in LDS once per workgroup and
+// used by every digit: relative stage d (global stage s0 + d) of column col
+// needs entries col * 2^d .. col * 2^d + 2^d - 1 of a run of 16 * 2^d
+// consecutive table entries, stored from LDS entry 16 * (2^d - 1) on.
+template <int LOGB>
+__device__ __forceinline__ void ip_stage_twiddles(ulonglong2* twl, const uint64_t* tw, uint32_t tile, uint32_t s0) {
+  constexpr int T = 2 << LOGB;
+  constexpr int ENTRIES = kCols * ((1 << LOGB) - 1);
+  for (int e = threadIdx.x; e < ENTRIES; e += T) {
+    const int d = 31 - __clz((e >> 4) + 1);
+    const uint32_t g = (1u << (s0 + d)) + (tile << (4 + d)) + (uint32_t)(e - kCols * ((1 << d) - 1));
+    twl[e] = *reinterpret_cast<const ulonglong2*>(tw + 2 * (uint64_t)g);
+  }
+}
+
+// R forward stages on the 2^R words of one item (rows base + (i << pos) of
+// column col), twiddles from the LDS copy.
+template <int R, int LOGB, bool LAZY>
+__device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, int pos, int col, const ulonglong2* twl,
+                                               uint64_t q) {
+  constexpr int E = 1 << R;
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int half = E >> (s + 1);
+    const int d = LOGB - pos - R + s;
+#pragma unroll
+    for (int g = 0; g < (1 << s); ++g) {
+      const int i0 = g * 2 * half;
+      const int row = base + (i0 << pos);
+      const ulonglong2 w = twl[kCols * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
+#pragma unroll
+      for (int m = 0; m < half; ++m) ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w.x, w.y, q);
+    }
+  }
+}
+
 // One register round of R forward stages on row bits [POS, POS+R): item k of
 // the thread (k < 8 >> R) is tid + k * THREADS; its words are rows
 // base + (i << POS) of column col, read from global memory (src) or LDS and
 // left in LDS or in x[].
 template <int R, int POS, int LOGB, bool LAZY, bool FROM_GLOBAL, bool TO_LDS>
-__device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, uint32_t tile,
-                                         uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
+__device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
+                                         uint32_t tile, int log_n, uint64_t q) {
   constexpr int T = IPRounds<LOGB>::THREADS;
   constexpr int NI = 8 >> R;
   uint64_t y[NI][1 << R];
@@ -139,7 +175,7 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
   }
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    round_regs<R, false, LAZY, false>(y[k], base[k], POS, col[k], LOGB, tile, s0, log_n, tw, q);
+    ip_butterflies<R, LOGB, LAZY>(y[k], base[k], POS, col[k], twl, q);
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       if (TO_LDS) lds[ip_lds<LOGB>(base[k] + (i << POS), col[k])] = y[k][i];
@@ -149,8 +185,8 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
 }
 
 template <int LOGB, int LOGN, bool LAZY>
-__device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, const PrimeConst& pc, int keyl,
-                                            const GridPos& gp) {
+__device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, ulonglong2* twl, const PrimeConst& pc,
+                                            int keyl, const GridPos& gp) {
   typedef IPRounds<LOGB> G;
   const int log_n = LOGN ? LOGN : a.log_n;
   const uint32_t s0 = (uint32_t)logb_col(log_n);
@@ -164,6 +200,7 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, c
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   const uint32_t w0 = tile_index<false>(tile, base, col, LOGB, log_n);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
+  ip_stage_twiddles<LOGB>(twl, tw, tile, s0);  // read after the barrier that opens each digit's transform
   // Montgomery products are below 2m, so four of them sum below 8m < 2^63
   uint64_t accb[8], acca[8];
 #pragma unroll
@@ -184,14 +221,14 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, c
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
       __syncthreads();  // the previous digit's last round has read the tile
       if constexpr (G::R1 > 0) {
-        ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, tile, s0, log_n, tw, q);
+        ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
         __syncthreads();
-        ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, tile, s0, log_n, tw, q);
+        ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, twl, tile, log_n, q);
       } else {
-        ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, tile, s0, log_n, tw, q);
+        ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
       }
       __syncthreads();
-      ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, tile, s0, log_n, tw, q);
+      ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, twl, tile, log_n, q);
     }
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
@@ -234,14 +271,15 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, c
 template <int LOGB, int LOGN>
 __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_ip_kernel(RowIPArgs a) {
   __shared__ uint64_t lds[(1 << LOGB) * kCols];
+  __shared__ ulonglong2 twl[kCols * ((1 << LOGB) - 1)];
   const GridPos gp = row_grid_pos();
   const int t = gp.job;
   const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
   const PrimeConst& pc = a.prime[keyl];
   if (pc.q < (1ull << 57))
-    row_ip_body<LOGB, LOGN, true>(a, lds, pc, keyl, gp);
+    row_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp);
   else
-    row_ip_body<LOGB, LOGN, false>(a, lds, pc, keyl, gp);
+    row_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp);
 }
 
 typedef void (*RowIPFn)(RowIPArgs);
@@ -368,7 +406,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ga.log_n = log_n;
     auto fn = CKKS_PICK_PASS(intt_row_gather_kernel, log_n, lr);
     if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
-    TraceScope ts(c, s, "ntt_pass", (double)n_items * nq * (N / 2) * lr);
+    TraceScope ts(c, s, "intt_row_gather", (double)n_items * nq * (N / 2) * lr);
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_items), dim3(kThreads), 0, s, ga);
     CKKS_HIP_CHECK(hipGetLastError());
   }
@@ -445,7 +483,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
       units += (double)(next - na) * (N / 2) * lr;  // butterflies
     }
     units += (double)next * N * (2.0 * beta + 2);  // products and final reductions
-    TraceScope ts(c, s, "ntt_pass", units * n_items);
+    TraceScope ts(c, s, "ntt_row_ip", units * n_items);
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), next, n_items), dim3(2u << lr), 0, s, ip);
     CKKS_HIP_CHECK(hipGetLastError());
   }
@@ -505,7 +543,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ca.next = next;
     ca.out_comp_limbs = out_comp_limbs;
     auto fn = CKKS_PICK_PASS(ntt_row_combine_kernel, log_n, lr);
-    TraceScope ts(c, s, "ntt_pass", (double)n_items * 2 * nq * ((double)(N / 2) * lr + N));
+    TraceScope ts(c, s, "ntt_row_combine", (double)n_items * 2 * nq * ((double)(N / 2) * lr + N));
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), 2 * nq, n_items), dim3(kThreads), 0, s, ca);
     CKKS_HIP_CHECK(hipGetLastError());
   }
