@@ -132,6 +132,35 @@ def test_keyswitch_parity_c1(lib, orc, c1):
         assert np.array_equal(to_host(out), orc.keyswitch(P, level, d, evk))
 
 
+# Parameter shapes beyond the workload recipes: every NTT pass geometry
+# (log N 10..15), digits of one limb and of more than 8 limbs, more than 8
+# special primes (the 16-source conversion path), a single digit, and
+# ciphertext primes above 2^57 (no lazy butterflies on any limb).
+KS_SHAPES = [
+    # log_n, L, q_bits, K, p_bits, dnum, levels
+    (10, 3, 40, 1, 50, 3, (2, 0)),
+    (11, 10, 54, 10, 60, 1, (9, 4)),
+    (12, 24, 54, 12, 60, 2, (23, 12, 11)),
+    (13, 5, 54, 5, 60, 1, (4, 2)),
+    (14, 8, 30, 4, 36, 2, (7, 3)),
+    (15, 6, 59, 3, 60, 2, (5, 3, 0)),
+]
+
+
+@pytest.mark.parametrize("shape", KS_SHAPES, ids=lambda s: "logn%d_L%d_K%d_dnum%d" % (s[0], s[1], s[3], s[5]))
+def test_keyswitch_shapes(lib, orc, shape):
+    log_n, L, q_bits, K, p_bits, dnum, levels = shape
+    ctx, P = make_pair(lib, orc, log_n, L, q_bits, K, p_bits, dnum)
+    for level in levels:
+        announce("keyswitch shape %s level=%d" % (shape[:6], level))
+        d = S.uniform_limbs(S.stream(level, "gpu/kss/d"), P.q[: level + 1], P.N)
+        evk = S.uniform_limbs(S.stream(level, "gpu/kss/k"), P.mods, P.N, lead=(P.dnum, 2))
+        out = empty_dev((2, level + 1, P.N))
+        lib.ckks_keyswitch(ctx, to_dev(d), to_dev(evk), out, level)
+        assert np.array_equal(to_host(out), orc.keyswitch(P, level, d, evk)), level
+    ctx.close()
+
+
 # ---------------------------------------------------------------- rotation
 
 def test_rotate_c1_encrypted(lib, orc, c1):
@@ -182,6 +211,12 @@ def test_rotate_errors(lib, orc, c3small):
         with pytest.raises(lib.CKKSError) as e:
             lib.ckks_rotate(ctx, x, x, *args)
         assert e.value.code == code
+    # buffers must be 16-byte aligned; rejected on the host before any launch
+    out = empty_dev((1, 2, 24, P.N))
+    for a_in, keys in [(x, [k.view(-1)[1:]]), (x.view(-1)[1:], [k])]:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_rotate(ctx, a_in, out, 1, 23, [5], keys)
+        assert e.value.code == lib.CKKS_EINVAL
 
 
 # ---------------------------------------------------------------- rescale, multiply
