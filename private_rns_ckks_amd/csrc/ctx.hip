@@ -93,10 +93,25 @@ static int upload(void** dst, const void* src, size_t bytes) {
   return CKKS_OK;
 }
 
+int ensure_lanes(Ctx* c) {
+  if (c->lane[0]) return CKKS_OK;
+  for (int i = 0; i < Ctx::kMaxLanes; ++i) {
+    CKKS_HIP_CHECK(hipStreamCreateWithFlags(&c->lane[i], hipStreamNonBlocking));
+    CKKS_HIP_CHECK(hipEventCreateWithFlags(&c->join_ev[i], hipEventDisableTiming));
+  }
+  CKKS_HIP_CHECK(hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming));
+  return CKKS_OK;
+}
+
 static void destroy(Ctx* c) {
   if (!c) return;
   (void)hipSetDevice(c->device);
   for (hipEvent_t e : c->trace.pool) (void)hipEventDestroy(e);
+  for (int i = 0; i < Ctx::kMaxLanes; ++i) {
+    if (c->lane[i]) (void)hipStreamDestroy(c->lane[i]);
+    if (c->join_ev[i]) (void)hipEventDestroy(c->join_ev[i]);
+  }
+  if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
   void* bufs[] = {c->d_prime, c->d_tw_fwd, c->d_tw_inv, c->d_modup, c->d_moddown, c->d_rescale, c->ws};
   for (void* b : bufs)
     if (b) (void)hipFree(b);

@@ -68,6 +68,12 @@ struct Ctx {
   uint64_t* ws = nullptr;         // workspace
   size_t ws_words = 0;
   TraceState trace;
+  // Internal streams (default priority) on which consecutive chunks of a
+  // batch run concurrently, forked from and joined back to the caller's
+  // stream with events; created on first use.
+  static constexpr int kMaxLanes = 3;
+  hipStream_t lane[kMaxLanes] = {};
+  hipEvent_t fork_ev = nullptr, join_ev[kMaxLanes] = {};
 
   int beta(int level) const { return (level + 1 + (int)alpha - 1) / (int)alpha; }
   // basis index of extended limb t at level l (q_0..q_l, then p_0..p_{K-1})
@@ -83,6 +89,7 @@ int set_error(int code, const std::string& msg);
   } while (0)
 
 int ensure_workspace(Ctx* c, size_t words);
+int ensure_lanes(Ctx* c);
 
 // Records the start event (if `family` is being traced) on construction and
 // the stop event on destruction; wrap exactly one kernel launch.

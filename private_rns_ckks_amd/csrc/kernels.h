@@ -5,7 +5,7 @@
 
 namespace ckks {
 
-constexpr int kMaxChunk = 8;  // batch items per launch of the key-switch pipeline
+constexpr int kMaxChunk = 32;  // batch items per launch of the key-switch pipeline
 constexpr int kMaxExt = 80;   // limbs of the extended basis: L (<= 64) + K (<= 16)
 
 struct ModUpArgs {

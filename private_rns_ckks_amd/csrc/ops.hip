@@ -14,10 +14,21 @@ namespace ckks {
 
 namespace {
 
+// Tuning knobs, read once: CKKS_LANES (concurrent chunks of a batch, 1 to
+// Ctx::kMaxLanes) and CKKS_CHUNK (items per chunk).
+int g_lanes_default() {
+  static int v = [] {
+    const char* e = getenv("CKKS_LANES");
+    int x = e ? atoi(e) : 2;
+    return std::max(1, std::min(x, Ctx::kMaxLanes));
+  }();
+  return v;
+}
+
 int g_chunk_default() {
   static int v = [] {
     const char* e = getenv("CKKS_CHUNK");
-    int x = e ? atoi(e) : 8;
+    int x = e ? atoi(e) : 4;
     return std::max(1, std::min(x, kMaxChunk));
   }();
   return v;
@@ -78,15 +89,41 @@ int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride,
   return CKKS_OK;
 }
 
+// Chunks of a batch on `lanes` internal streams: fork_lanes makes them wait
+// for the work already on s; join_lanes makes s wait for them (also after a
+// failure, so no lane work escapes the caller's stream order).
+int fork_lanes(Ctx* c, hipStream_t s, int lanes) {
+  if (lanes < 2) return CKKS_OK;
+  int rc = ensure_lanes(c);
+  if (rc) return rc;
+  CKKS_HIP_CHECK(hipEventRecord(c->fork_ev, s));
+  for (int l = 0; l < lanes; ++l) CKKS_HIP_CHECK(hipStreamWaitEvent(c->lane[l], c->fork_ev, 0));
+  return CKKS_OK;
+}
+
+int join_lanes(Ctx* c, hipStream_t s, int lanes, int rc) {
+  if (lanes < 2) return rc;
+  for (int l = 0; l < lanes; ++l) {
+    CKKS_HIP_CHECK(hipEventRecord(c->join_ev[l], c->lane[l]));
+    CKKS_HIP_CHECK(hipStreamWaitEvent(s, c->join_ev[l], 0));
+  }
+  return rc;
+}
+
+hipStream_t lane_stream(Ctx* c, hipStream_t s, int lanes, int k) { return lanes > 1 ? c->lane[k % lanes] : s; }
+
 // Batched rotation with contiguous input/output (item b at base + b*stride).
+// Items with g != 1 are key-switched in chunks (runs of consecutive items of
+// at most g_chunk_default()); with several lanes, chunk k runs on internal
+// stream k % lanes with its own workspace, so one chunk's memory-bound kernels
+// overlap another's arithmetic-bound ones.
 int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint64_t stride, int batch, int level,
                  const uint32_t* g, const uint64_t* const* evk, unsigned flags) {
   const int nq = level + 1;
   const uint64_t ct_words = 2ull * nq * c->N;
   const uint64_t per = ks_ws_words(c, level);
   const int chunk = g_chunk_default();
-  int rc = ensure_workspace(c, per * chunk);
-  if (rc) return rc;
+  int rc;
   std::vector<int> idx;
   for (int b = 0; b < batch; ++b) {
     if (g[b] == 1) {
@@ -100,14 +137,21 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
     }
   }
   // consecutive runs of non-identity items share a stride
-  size_t p = 0;
-  while (p < idx.size()) {
+  std::vector<std::pair<size_t, size_t>> pieces;
+  for (size_t p = 0; p < idx.size();) {
     size_t q = p + 1;
     while (q < idx.size() && q - p < (size_t)chunk && idx[q] == idx[q - 1] + 1) ++q;
+    pieces.emplace_back(p, q);
+    p = q;
+  }
+  const int lanes = (int)std::min<size_t>(pieces.size(), g_lanes_default());
+  if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
+  for (size_t k = 0; k < pieces.size() && rc == CKKS_OK; ++k) {
+    const size_t p = pieces[k].first, q = pieces[k].second;
     KSItem items[kMaxChunk];
-    for (size_t k = p; k < q; ++k) {
-      const int b = idx[k];
-      KSItem& it = items[k - p];
+    for (size_t m = p; m < q; ++m) {
+      const int b = idx[m];
+      KSItem& it = items[m - p];
       it.d = in + b * stride + (uint64_t)nq * c->N;  // c1
       it.g = g[b];
       it.evk = evk[b];
@@ -117,10 +161,10 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
       it.accum = (flags & CKKS_ROT_ACCUMULATE) ? in + b * stride : nullptr;
       it.out = out + b * stride;
     }
-    if ((rc = ks_chunk(c, s, level, (int)(q - p), items, stride, stride, stride, stride, nq, c->ws))) return rc;
-    p = q;
+    rc = ks_chunk(c, lane_stream(c, s, lanes, (int)k), level, (int)(q - p), items, stride, stride, stride, stride,
+                  nq, c->ws + per * chunk * (k % lanes));
   }
-  return CKKS_OK;
+  return join_lanes(c, s, lanes, rc);
 }
 
 }  // namespace
@@ -240,17 +284,20 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
   const int nq = level + 1;
   const uint64_t ct = 2ull * nq * N;
   const int chunk = g_chunk_default();
+  const int n_chunks = (batch + chunk - 1) / chunk;
+  const int lanes = std::min(n_chunks, g_lanes_default());
   const uint64_t ks = ks_ws_words(ctx, level);
   // per chunk: tensor output [3][nq][N] per item, relinearised [2][nq][N] per item, then key-switch scratch
   const uint64_t tens = 3ull * nq * N, rel = ct;
   const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
-  const uint64_t need = chunk * (tens + rel + std::max(ks, rs_per));
-  if ((rc = ensure_workspace(ctx, need))) return rc;
-  uint64_t* D = ctx->ws;
-  uint64_t* R = D + chunk * tens;
-  uint64_t* S = R + chunk * rel;
-  for (int b0 = 0; b0 < batch; b0 += chunk) {
-    const int n = std::min(chunk, batch - b0);
+  const uint64_t region = chunk * (tens + rel + std::max(ks, rs_per));  // one lane's workspace
+  if ((rc = ensure_workspace(ctx, region * lanes)) || (rc = fork_lanes(ctx, stream, lanes))) return rc;
+  for (int k = 0; k < n_chunks && rc == CKKS_OK; ++k) {
+    const int b0 = k * chunk, n = std::min(chunk, batch - b0);
+    const hipStream_t ls = lane_stream(ctx, stream, lanes, k);
+    uint64_t* D = ctx->ws + region * (k % lanes);
+    uint64_t* R = D + chunk * tens;
+    uint64_t* S = R + chunk * rel;
     TensorArgs ta;
     ta.a = d_a + b0 * ct;
     ta.b = d_b + b0 * ct;
@@ -260,7 +307,7 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
     ta.prime = ctx->d_prime;
     ta.n = N;
     ta.level = level;
-    if ((rc = launch_tensor(ctx, stream, ta, n))) return rc;
+    if ((rc = launch_tensor(ctx, ls, ta, n))) break;
     KSItem items[kMaxChunk];
     for (int i = 0; i < n; ++i) {
       KSItem& it = items[i];
@@ -273,14 +320,12 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
       it.accum = nullptr;
       it.out = rescale ? R + i * rel : d_out + (b0 + i) * ct;
     }
-    if ((rc = ks_chunk(ctx, stream, level, n, items, tens, tens, 0, rel, nq, S))) return rc;
-    if (rescale) {
-      if ((rc = rescale_batch(ctx, stream, R, rel, d_out + (b0)*2ull * level * N, 2ull * level * N, n, level, S,
-                              chunk * std::max(ks, rs_per))))
-        return rc;
-    }
+    if ((rc = ks_chunk(ctx, ls, level, n, items, tens, tens, 0, rel, nq, S))) break;
+    if (rescale)
+      rc = rescale_batch(ctx, ls, R, rel, d_out + b0 * 2ull * level * N, 2ull * level * N, n, level, S,
+                         chunk * std::max(ks, rs_per));
   }
-  return CKKS_OK;
+  return join_lanes(ctx, stream, lanes, rc);
 }
 
 int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
