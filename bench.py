@@ -34,6 +34,12 @@ HBM_PEAK_GBPS = 8000.0
 # int32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 BYTES_PER_HROT = 150_994_944  # ciphertext in (24 MiB) + key (96 MiB) + ciphertext out (24 MiB)
+# modmul-class operations per HRot at level 23: 83.9M butterflies (160 limb
+# transforms), 44.0M ModUp, 16.8M inner product, 32.5M ModDown
+OPS_PER_HROT = 177_200_000
+# limbs the dominant kernel reads or writes per ciphertext at level 23: 192 key
+# limbs (3 digits x 2 x 32), 72 converted limbs, 24 input limbs, 64 accumulator limbs
+IP_LIMBS_PER_ITEM = 192 + 72 + 24 + 64
 
 
 def log(msg):
@@ -95,17 +101,24 @@ def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
     t0 = time.perf_counter()
     oracle.rotate_batch(P, level, cts[:1], gs[:1], keys[:1])
     t1 = time.perf_counter() - t0
-    k = max(1, min(len(gs) - 1, int(round(target_s / max(t1, 1e-3)))))
-    t0 = time.perf_counter()
-    oracle.rotate_batch(P, level, cts[1:1 + k], gs[1:1 + k], keys[1:1 + k])
-    dt = time.perf_counter() - t0
+    # items 1..B-1 of the batch, cycled until about target_s of work
+    k = max(1, int(round(target_s / max(t1, 1e-3))))
+    B = len(gs)
+    done, dt = 0, 0.0
+    while done < k:
+        lo = 1 + done % (B - 1)
+        hi = min(B, lo + (k - done))
+        t0 = time.perf_counter()
+        oracle.rotate_batch(P, level, cts[lo:hi], gs[lo:hi], keys[lo:hi])
+        dt += time.perf_counter() - t0
+        done += hi - lo
     return {
         "value": k / dt,
         "unit": "HRot/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%d of the 32 rotations of the batch (items 1..%d), same words as the GPU run, "
-                  "plain __int128 %% oracle with OpenMP over limbs/coefficients; %.1f s" % (k, k, dt),
+        "sample": "%d rotations of the C3 batch (items 1..%d cycled), same words as the GPU run, "
+                  "plain __int128 %% oracle with OpenMP over limbs/coefficients; %.1f s" % (k, B - 1, dt),
     }
 
 
@@ -188,10 +201,13 @@ def main():
             "unit": "Tops/s",
             "frac": round(achieved / VALU_PEAK_TOPS, 4),
             "traffic": measured_traffic(),
+            "alg_bytes_per_launch": int(B * args.steps / kstat["launches"] * IP_LIMBS_PER_ITEM * N * 8),
             "avg_launch_us": round(avg_s * 1e6, 2),
             "launches": kstat["launches"],
             "work_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"], kstat["ops_per_unit"]),
             "hbm_frac_step": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "chunks of the batch run on two streams at once, so a launch's duration includes "
+                    "co-running kernels of the other stream; alu_roofline_frac covers the whole step",
         }
 
     ntt = None
@@ -223,6 +239,7 @@ def main():
         },
         "roofline": roof,
         "hbm_roofline_frac": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
+        "alu_roofline_frac": round(value * OPS_PER_HROT * lib.OPS_PER_MODMUL / 1e12 / VALU_PEAK_TOPS, 4),
         "ntt": ntt,
         "cpu_baseline": cpu,
     }
