@@ -96,17 +96,28 @@ struct RowIPArgs {
   int log_n, level, next, beta, alpha, L, K;
 };
 
-// The row pass's LOGB stages run as register rounds of at most 3 stages, the
-// last of exactly 3, so every thread of the 2^(LOGB+1)-thread workgroup holds
-// 8 words in every round and ends with 8 consecutive words of one column:
-// the layout the multiply phase reads the key digits in.
+// A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
+// on, so several workgroups share a CU).  The row pass's LOGB stages run as
+// register rounds of at most 3 stages, the last of exactly 3, so every thread
+// holds 8 words in every round and ends with 8 consecutive words of one
+// column: the layout the multiply phase reads the key digits in.
+__host__ __device__ constexpr int ip_logkc(int logb) { return logb >= 7 ? 3 : 4; }
+
 template <int LOGB>
 struct IPRounds {
   static constexpr int R3 = 3;
   static constexpr int R2 = LOGB >= 6 ? 3 : LOGB - 3;
   static constexpr int R1 = LOGB - R2 - R3;  // 0 when two rounds suffice
-  static constexpr int THREADS = 2 << LOGB;
+  static constexpr int LOGKC = ip_logkc(LOGB);
+  static constexpr int KC = 1 << LOGKC;
+  static constexpr int THREADS = KC << (LOGB - 3);
 };
+
+// global word index (within the limb) of tile element (row, col)
+template <int LOGB>
+__device__ __forceinline__ uint32_t ip_word(uint32_t tile, int row, int col) {
+  return ((tile * IPRounds<LOGB>::KC + col) << LOGB) + row;
+}
 
 // LDS position of row-pass tile element (row, col): column-major, with row
 // bits 0-4 XOR-ed by (row bits 5-7) and (row bits 6-7) << 3.  For the rounds
@@ -119,15 +130,15 @@ __device__ __forceinline__ int ip_lds(int row, int col) {
 
 // The row pass's twiddles for one tile, staged in LDS once per workgroup and
 // used by every digit: relative stage d (global stage s0 + d) of column col
-// needs entries col * 2^d .. col * 2^d + 2^d - 1 of a run of 16 * 2^d
-// consecutive table entries, stored from LDS entry 16 * (2^d - 1) on.
+// needs entries col * 2^d .. col * 2^d + 2^d - 1 of a run of KC * 2^d
+// consecutive table entries, stored from LDS entry KC * (2^d - 1) on.
 template <int LOGB>
 __device__ __forceinline__ void ip_stage_twiddles(ulonglong2* twl, const uint64_t* tw, uint32_t tile, uint32_t s0) {
-  constexpr int T = 2 << LOGB;
-  constexpr int ENTRIES = kCols * ((1 << LOGB) - 1);
-  for (int e = threadIdx.x; e < ENTRIES; e += T) {
-    const int d = 31 - __clz((e >> 4) + 1);
-    const uint32_t g = (1u << (s0 + d)) + (tile << (4 + d)) + (uint32_t)(e - kCols * ((1 << d) - 1));
+  typedef IPRounds<LOGB> G;
+  constexpr int ENTRIES = G::KC * ((1 << LOGB) - 1);
+  for (int e = threadIdx.x; e < ENTRIES; e += G::THREADS) {
+    const int d = 31 - __clz((e >> G::LOGKC) + 1);
+    const uint32_t g = (1u << (s0 + d)) + (tile << (G::LOGKC + d)) + (uint32_t)(e - G::KC * ((1 << d) - 1));
     twl[e] = *reinterpret_cast<const ulonglong2*>(tw + 2 * (uint64_t)g);
   }
 }
@@ -146,7 +157,7 @@ __device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, 
     for (int g = 0; g < (1 << s); ++g) {
       const int i0 = g * 2 * half;
       const int row = base + (i0 << pos);
-      const ulonglong2 w = twl[kCols * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
+      const ulonglong2 w = twl[IPRounds<LOGB>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
 #pragma unroll
       for (int m = 0; m < half; ++m) ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w.x, w.y, q);
     }
@@ -170,7 +181,7 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       const int row = base[k] + (i << POS);
-      y[k][i] = FROM_GLOBAL ? src[tile_index<false>(tile, row, col[k], LOGB, log_n)] : lds[ip_lds<LOGB>(row, col[k])];
+      y[k][i] = FROM_GLOBAL ? src[ip_word<LOGB>(tile, row, col[k])] : lds[ip_lds<LOGB>(row, col[k])];
     }
   }
 #pragma unroll
@@ -198,7 +209,7 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
   // this thread's 8 output words: rows base..base+7 of column col
   int col, base;
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
-  const uint32_t w0 = tile_index<false>(tile, base, col, LOGB, log_n);
+  const uint32_t w0 = ip_word<LOGB>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
   ip_stage_twiddles<LOGB>(twl, tw, tile, s0);  // read after the barrier that opens each digit's transform
   // Montgomery products are below 2m, so four of them sum below 8m < 2^63
@@ -268,10 +279,12 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
   }
 }
 
+// at most 168 VGPRs: three waves per SIMD (three workgroups per CU at 2^8 rows)
 template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_ip_kernel(RowIPArgs a) {
-  __shared__ uint64_t lds[(1 << LOGB) * kCols];
-  __shared__ ulonglong2 twl[kCols * ((1 << LOGB) - 1)];
+__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void ntt_row_ip_kernel(
+    RowIPArgs a) {
+  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
+  __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
   const GridPos gp = row_grid_pos();
   const int t = gp.job;
   const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
@@ -484,7 +497,8 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     }
     units += (double)next * N * (2.0 * beta + 2);  // products and final reductions
     TraceScope ts(c, s, "ntt_row_ip", units * n_items);
-    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), next, n_items), dim3(2u << lr), 0, s, ip);
+    const int logkc = ip_logkc(lr);
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), next, n_items), dim3(1u << (lr - 3 + logkc)), 0, s, ip);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   // F, G: inverse NTT of the special limbs, times [phat_k^-1 N^-1]: y_k

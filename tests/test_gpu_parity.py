@@ -201,6 +201,24 @@ def test_rotate_batch_mixed(lib, orc, c3small, flags):
     assert np.array_equal(got, ref)
 
 
+def test_rotate_batch_chunks(lib, orc, c3small):
+    """Runs of 5, 1 and 6 key-switched items between identity items: chunks of
+    4, 1, 1, 4 and 2 items spread over the internal streams."""
+    ctx, P = c3small
+    level = 20
+    ks = [1, 2, 3, 4, 5, 0, 6, 0, 7, 8, 9, 10, 11, 12]
+    B = len(ks)
+    announce("rotate batch of %d in chunks" % B)
+    cts = S.uniform_limbs(S.stream(5, "gpu/rotc/ct"), P.q[: level + 1], P.N, lead=(B, 2))
+    gs = [P.galois(k) for k in ks]
+    keys_h = [S.uniform_limbs(S.stream(b, "gpu/rotc/k"), P.mods, P.N, lead=(P.dnum, 2)) for b in range(B)]
+    out = empty_dev(cts.shape)
+    lib.ckks_rotate(ctx, to_dev(cts), out, B, level, gs, [to_dev(k) for k in keys_h], lib.CKKS_ROT_ACCUMULATE)
+    got = to_host(out)
+    ref = orc.rotate_batch(P, level, cts, gs, keys_h, orc.ROT_ACCUMULATE)
+    assert np.array_equal(got, ref)
+
+
 def test_rotate_errors(lib, orc, c3small):
     ctx, P = c3small
     x = empty_dev((1, 2, 24, P.N))
