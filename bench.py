@@ -130,6 +130,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-ntt", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the C4 / C5 timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 1 GiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -214,6 +215,10 @@ def main():
     if not args.no_ntt:
         ntt = ntt_bench(lib, S, torch, np, args)
 
+    workloads = None
+    if not args.no_workloads:
+        workloads = workload_bench(lib, S, torch, ctx, q, p, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -241,11 +246,79 @@ def main():
         "hbm_roofline_frac": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
         "alu_roofline_frac": round(value * OPS_PER_HROT * lib.OPS_PER_MODMUL / 1e12 / VALU_PEAK_TOPS, 4),
         "ntt": ntt,
+        "workloads": workloads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     ctx.close()
     return 0
+
+
+def uniform_dev(torch, moduli, N, lead):
+    """Uniform residues generated on the device: [*lead][len(moduli)][N] int64 words, limb i below moduli[i]."""
+    out = torch.empty(tuple(lead) + (len(moduli), N), dtype=torch.int64, device="cuda")
+    for i, m in enumerate(moduli):
+        out[..., i, :].random_(0, int(m))
+    return out
+
+
+def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
+    """Wall time of the other two workload recipes on the same parameters:
+    C4, the BSGS matrix-vector product (3 inputs at level 12, 12 outputs, 8 x 8
+    steps, 15.7 GB of diagonals), and C5, 48 ciphertext products with
+    relinearisation and rescale followed by 15 rotate-and-sum steps."""
+    N = 1 << S.CONFIGS["C4"]["log_n"]
+    dnum = S.CONFIGS["C4"]["dnum"]
+    res = {}
+    c4 = S.CONFIGS["C4"]
+    level, n_in, n_out, n1, n2 = c4["level"], c4["n_in"], c4["n_out"], c4["n1"], c4["n2"]
+    nq = level + 1
+    x = uniform_dev(torch, q[:nq], N, (n_in, 2))
+    diags = uniform_dev(torch, q[:nq], N, (n_out, n_in, n2, n1))
+    kb = [uniform_dev(torch, q + p, N, (dnum, 2)) for _ in range(n1 - 1)]
+    kg = [uniform_dev(torch, q + p, N, (dnum, 2)) for _ in range(n2 - 1)]
+    gb = [pow(5, b, 2 * N) for b in range(1, n1)]
+    gg = [pow(5, n1 * g, 2 * N) for g in range(1, n2)]
+    y = torch.empty((n_out, 2, level, N), dtype=torch.int64, device="cuda")
+
+    def run_c4():
+        lib.ckks_ptmatvec(ctx, x, n_in, diags, n_out, n1, n2, gb, kb, gg, kg, y, level, 0, stream)
+
+    res["c4_ptmatvec_ms"] = round(timed(torch, stream, run_c4, reps), 3)
+    del x, diags, kb, kg, y
+    torch.cuda.empty_cache()
+    c5 = S.CONFIGS["C5"]
+    B, level, steps = c5["batch"], S.CONFIGS["C5"]["L"] - 1, c5["rotsum_steps"]
+    a = uniform_dev(torch, q, N, (B, 2))
+    b = uniform_dev(torch, q, N, (B, 2))
+    rlk = uniform_dev(torch, q + p, N, (dnum, 2))
+    keys = [uniform_dev(torch, q + p, N, (dnum, 2)) for _ in range(steps)]
+    gs = [pow(5, 1 << k, 2 * N) for k in range(steps)]
+    bufs = [torch.empty((B, 2, level, N), dtype=torch.int64, device="cuda") for _ in range(2)]
+
+    def run_c5():
+        lib.ckks_mul_relin_rescale(ctx, a, b, rlk, bufs[0], B, level, 0, stream)
+        for k in range(steps):
+            lib.ckks_rotate(ctx, bufs[k % 2], bufs[(k + 1) % 2], B, level - 1, [gs[k]] * B, [keys[k]] * B,
+                            lib.CKKS_ROT_ACCUMULATE, stream)
+
+    res["c5_mul_rotsum_ms"] = round(timed(torch, stream, run_c5, reps), 3)
+    res["note"] = "C4: one ckks_ptmatvec call; C5: ckks_mul_relin_rescale on 48 pairs + 15 accumulate rotations " \
+                  "of the 48 products (768 key switches); device-generated uniform words, %d timed reps" % reps
+    log("C4 ptmatvec %.2f ms, C5 %.2f ms" % (res["c4_ptmatvec_ms"], res["c5_mul_rotsum_ms"]))
+    return res
+
+
+def timed(torch, stream, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def ntt_bench(lib, S, torch, np, args):
