@@ -87,6 +87,7 @@ def lib():
             "orc_keyswitch": (None, [pp, c_int, u64p, u64p, u64p]),
             "orc_rotate": (None, [pp, c_int, u64p, c_u32, u64p, u64p, ctypes.c_uint]),
             "orc_rotate_batch": (None, [pp, c_int, u64p, c_int, u32p, ctypes.POINTER(u64p), u64p, ctypes.c_uint]),
+            "orc_rotate_hoisted": (None, [pp, c_int, u64p, c_int, u32p, ctypes.POINTER(u64p), u64p]),
             "orc_rescale": (c_int, [pp, c_int, u64p, u64p]),
             "orc_tensor": (None, [pp, c_int, u64p, u64p, u64p]),
             "orc_mul_relin_rescale": (c_int, [pp, c_int, u64p, u64p, u64p, u64p, c_int, ctypes.c_uint]),
@@ -290,6 +291,19 @@ def rotate_batch(P: Params, level: int, cts, gs, evks, flags: int = 0):
     g = np.ascontiguousarray(np.asarray(gs, dtype=np.uint32))
     lib().orc_rotate_batch(P.ref(), level, _u64(cts), B, g.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
                            _ptr_array(evks), _u64(out), flags)
+    return out
+
+
+def rotate_hoisted(P: Params, level: int, ct, gs, evks):
+    """Rotations of one ciphertext by every element of gs sharing one basis
+    extension; returns [len(gs)][2][l+1][N]."""
+    ct = _arr(ct)
+    R = len(gs)
+    out = np.empty((R,) + ct.shape, dtype=np.uint64)
+    evks = [_arr(e) for e in evks]
+    g = np.ascontiguousarray(np.asarray(gs, dtype=np.uint32))
+    lib().orc_rotate_hoisted(P.ref(), level, _u64(ct), R, g.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                             _ptr_array(evks), _u64(out))
     return out
 
 

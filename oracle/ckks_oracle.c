@@ -525,6 +525,72 @@ void orc_rotate(const orc_params *P, int level, const uint64_t *ct, uint32_t g, 
     free(r);
 }
 
+/* Rotations of one ciphertext by n_rot Galois elements that share one basis
+ * extension ("hoisting"; the AEGIS page, "Methodology", item 4, schedules
+ * several rotations of the same ciphertext).  The digits of c1 are raised to
+ * the extended basis and transformed once:
+ *   dt_j = NTT(ModUp_j(iNTT(c1)))                       (extended basis)
+ * and for every element g (out_r, [2][l+1][N]):
+ *   acc_b = sum_j tau_g(dt_j) * evk_r,j.b,  acc_a = sum_j tau_g(dt_j) * evk_r,j.a
+ *   out_r = (tau_g(c0) + ModDown(acc_b), ModDown(acc_a)).
+ * tau_g acts on each extended limb by the NTT-form permutation.  tau_g(dt_j)
+ * lifts tau_g of digit j exactly, so this is a key switch of tau_g(c1); its
+ * words differ from orc_rotate's, where tau_g comes before the extension (the
+ * sign changes of tau_g meet a different multiple of the digit modulus).
+ * g = 1 gives a copy.  out: [n_rot][2][l+1][N]. */
+void orc_rotate_hoisted(const orc_params *P, int level, const uint64_t *ct, int n_rot, const uint32_t *g,
+                        const uint64_t *const *evks, uint64_t *out)
+{
+    uint64_t n = (uint64_t)1 << P->log_n;
+    int nq = level + 1, next = nq + P->K, LK = P->L + P->K;
+    int beta = digits_at(P, level);
+    uint64_t csz = (uint64_t)2 * nq * n;
+    uint64_t *ext_mods = malloc(sizeof(uint64_t) * next), *ext_psis = malloc(sizeof(uint64_t) * next);
+    for (int t = 0; t < next; t++) { ext_mods[t] = ext_mod(P, level, t); ext_psis[t] = ext_psi(P, level, t); }
+    uint64_t *dc = malloc(sizeof(uint64_t) * n * nq);
+    memcpy(dc, ct + (uint64_t)nq * n, sizeof(uint64_t) * n * nq);
+    orc_ntt_limbs(dc, nq, P->log_n, P->mod, P->psi, 1);
+    uint64_t *dt = malloc(sizeof(uint64_t) * n * next * beta);
+    for (int j = 0; j < beta; j++) {
+        orc_modup(P, level, j, dc, dt + (uint64_t)j * next * n);
+        orc_ntt_limbs(dt + (uint64_t)j * next * n, next, P->log_n, ext_mods, ext_psis, 0);
+    }
+    uint64_t *acc = malloc(sizeof(uint64_t) * 2 * next * n);
+    uint64_t *tj = malloc(sizeof(uint64_t) * next * n);
+    uint64_t *t0 = malloc(sizeof(uint64_t) * nq * n);
+    for (int r = 0; r < n_rot; r++) {
+        uint64_t *o = out + (uint64_t)r * csz;
+        if (g[r] == 1) {
+            memcpy(o, ct, sizeof(uint64_t) * csz);
+            continue;
+        }
+        memset(acc, 0, sizeof(uint64_t) * 2 * next * n);
+        for (int j = 0; j < beta; j++) {
+            orc_automorph_ntt(dt + (uint64_t)j * next * n, tj, next, P->log_n, g[r]);
+            for (int comp = 0; comp < 2; comp++) {
+#pragma omp parallel for
+                for (int t = 0; t < next; t++) {
+                    const uint64_t *key = evks[r] + (((uint64_t)j * 2 + comp) * LK + key_limb(P, level, t)) * n;
+                    uint64_t *ac = acc + ((uint64_t)comp * next + t) * n;
+                    uint64_t mt = ext_mods[t];
+                    for (uint64_t c = 0; c < n; c++) ac[c] = addmod(ac[c], mulmod(tj[(uint64_t)t * n + c], key[c], mt), mt);
+                }
+            }
+        }
+        orc_moddown(P, level, acc, o);
+        orc_moddown(P, level, acc + (uint64_t)next * n, o + (uint64_t)nq * n);
+        orc_automorph_ntt(ct, t0, nq, P->log_n, g[r]);
+        orc_poly_add(o, t0, o, nq, P->log_n, P->mod);
+    }
+    free(t0);
+    free(tj);
+    free(acc);
+    free(dt);
+    free(dc);
+    free(ext_mods);
+    free(ext_psis);
+}
+
 /* Batch of independent rotations: ct/out are [B][2][l+1][N]. */
 void orc_rotate_batch(const orc_params *P, int level, const uint64_t *ct, int batch, const uint32_t *g,
                       const uint64_t *const *evks, uint64_t *out, unsigned flags)
@@ -626,7 +692,9 @@ int orc_mul_relin_rescale(const orc_params *P, int level, const uint64_t *a, con
  * giant-step rotation.  Baby step b (1..n1-1) rotates by Galois element
  * g_baby[b-1] with key evk_baby[b-1]; giant step g (1..n2-1) by
  * g_giant[g-1] with evk_giant[g-1].
- *   baby_{c,b} = Rot_b(x_c)                  (b = 0: x_c itself)
+ *   baby_{c,b} = Rot_b(x_c)                  (b = 0: x_c itself; the n1-1
+ *                                             baby steps of x_c are hoisted
+ *                                             rotations sharing one extension)
  *   inner_{o,g} = sum_c sum_b diag_{o,c,g,b} (*) baby_{c,b}
  *   y_o = sum_g Rot_g(inner_{o,g})           (g = 0: no rotation)
  * then y_o is rescaled unless ORC_NO_RESCALE.  y: [n_out][2][l or l+1][N].
@@ -642,8 +710,9 @@ int orc_ptmatvec(const orc_params *P, int level, const uint64_t *x, int n_in, co
     uint64_t *baby = malloc(sizeof(uint64_t) * csz * n_in * n1);
     for (int c = 0; c < n_in; c++) {
         memcpy(baby + (uint64_t)(c * n1) * csz, x + (uint64_t)c * csz, sizeof(uint64_t) * csz);
-        for (int b = 1; b < n1; b++)
-            orc_rotate(P, level, x + (uint64_t)c * csz, g_baby[b - 1], evk_baby[b - 1], baby + (uint64_t)(c * n1 + b) * csz, 0);
+        if (n1 > 1)
+            orc_rotate_hoisted(P, level, x + (uint64_t)c * csz, n1 - 1, g_baby, evk_baby,
+                               baby + (uint64_t)(c * n1 + 1) * csz);
     }
     uint64_t *inner = malloc(sizeof(uint64_t) * csz), *acc = malloc(sizeof(uint64_t) * csz);
     uint64_t *tmp = malloc(sizeof(uint64_t) * csz), *rot = malloc(sizeof(uint64_t) * csz);

@@ -2,9 +2,11 @@
 
 Checks against what the mathematics fixes, never against the oracle itself:
   * with error-free keys, KS(d) decrypts to d*s' up to the ModDown rounding
-    only: |k0 + k1*s - d*s'| <= (K/2)*(1 + h) per coefficient;
+    only: |k0 + k1*s - d*s'| <= (K/2)*(1 + h) per coefficient (also for
+    hoisted rotations, where d = tau_g(c1) and s' = tau_g(s));
   * decrypt(rotate_k(ct)) = slots shifted left by k (C1 tolerance 2^-12,
-    C3 parameters 2^-20), Rot_a(Rot_b) = Rot_(a+b), accumulate = ct + Rot;
+    C3 parameters 2^-20), also for hoisted rotations, Rot_a(Rot_b) = Rot_(a+b),
+    accumulate = ct + Rot;
   * mul/relinearise/rescale decrypts to the slot-wise product;
   * the BSGS matvec equals the float64 map y_o[s] = sum_c sum_t
     D_{o,c,t}[s] * x_c[(s+t) mod n];
@@ -41,6 +43,38 @@ def test_keyswitch_noise_free_bound(orc, level):
     e = np.array([[(int(a) + int(b) - int(c)) % m for a, b, c in zip(k[0, i], t1[i], t2[i])]
                   for i, m in enumerate(mods)], dtype=np.uint64)
     assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h)
+
+
+def test_hoisted_rotation_noise_free_bound(orc):
+    """Hoisted rotations are key switches of tau_g(c1): with error-free keys
+    k0 + k1*s = tau_g(c0) + tau_g(c1)*tau_g(s) up to the ModDown rounding."""
+    P = config_params(orc, "C3", log_n=9)
+    level, h = 17, 64
+    s, s_ntt = secret(orc, P, 7, h)
+    gs = [P.galois(k) for k in (1, 5, 100)]
+    evks = [galois_key(orc, P, s_ntt, g, 7, "hk%d" % g, zero_error=True) for g in gs]
+    ct = S.uniform_limbs(S.stream(7, "h/ct"), P.q[: level + 1], P.N, lead=(2,))
+    out = orc.rotate_hoisted(P, level, ct, gs, evks)
+    nq = level + 1
+    mods = P.q[:nq]
+    for r, g in enumerate(gs):
+        c0g = orc.automorph_ntt(ct[0], P.log_n, g)
+        c1g = orc.automorph_ntt(ct[1], P.log_n, g)
+        sg = orc.automorph_ntt(s_ntt, P.log_n, g)[:nq]
+        e = np.array([[(int(k0) + int(k1) * int(sv) - int(a0) - int(a1) * int(sgv)) % m
+                       for k0, k1, sv, a0, a1, sgv in zip(out[r, 0, i], out[r, 1, i], s_ntt[i], c0g[i], c1g[i], sg[i])]
+                      for i, m in enumerate(mods)], dtype=np.uint64)
+        assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h), g
+
+
+def test_hoisted_rotations_decrypt_to_shifts(orc):
+    P, s_ntt, z, ct, level, scale = c1_setup(orc, seed=3)
+    ks = [1, 3, 7, P.N // 2 - 1]
+    gs = [P.galois(k) for k in ks]
+    evks = [galois_key(orc, P, s_ntt, g, 3, "hg%d" % g) for g in gs]
+    out = orc.rotate_hoisted(P, level, ct, gs, evks)
+    for r, k in enumerate(ks):
+        assert rel_err(orc.decrypt(P, level, out[r], s_ntt, scale), np.roll(z, -k)) < 2 ** -12, k
 
 
 def test_relin_key_noise_free_bound(orc):
