@@ -172,6 +172,22 @@ int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk,
 int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
                 const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream);
 
+/* Hoisted rotations (AEGIS page, "Methodology", item 4: several rotations of
+ * one ciphertext): each of the n_in ciphertexts of d_ct_in
+ * ([n_in][2][level+1][N]) is rotated by every galois_elts[r] (host array,
+ * r < n_rot) with the switch key d_evks[r] (host array of device pointers)
+ * into d_ct_out ([n_in][n_rot][2][level+1][N]).  The digits of c1 are raised
+ * to the extended basis and transformed once per ciphertext; each rotation
+ * then applies tau_g to those extended limbs (an NTT-form permutation) before
+ * the inner product, so out = (tau_g(c0) + k0, k1) with (k0, k1) the key
+ * switch of tau_g(c1) whose decomposition is tau_g of c1's.  The result
+ * decrypts like ckks_rotate's but its words differ: the automorphism's sign
+ * changes meet the raised digit rather than the digit.  Galois element 1 is
+ * a copy (its key pointer may be NULL).  Requires K > 0. */
+int ckks_rotate_hoisted(ckks_ctx* ctx, const uint64_t* d_ct_in, int n_in, int level, int n_rot,
+                        const uint32_t* galois_elts, const uint64_t* const* d_evks, uint64_t* d_ct_out,
+                        ckks_stream_t stream);
+
 /* Rescale (divide by q_level, rounding to nearest) of d_in
  * ([batch][2][level+1][N]) into d_out ([batch][2][level][N]).
  * CKKS_ERANGE at level 0. */
@@ -194,7 +210,8 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
  *   giant    n2-1 Galois elements / switch keys for the giant steps 1..n2-1
  *   d_y      [n_out][2][level][N] (level+1 with CKKS_NO_RESCALE)
  * y_o = sum_g Rot_g( sum_c sum_b diag(o,c,g,b) * Rot_b(x_c) ), then rescale.
- * The baby-step rotations are computed once and shared by all outputs. */
+ * The baby-step rotations are computed once and shared by all outputs, as
+ * hoisted rotations of each input (ckks_rotate_hoisted). */
 int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
                   const uint32_t* baby_galois, const uint64_t* const* d_evk_baby, const uint32_t* giant_galois,
                   const uint64_t* const* d_evk_giant, uint64_t* d_y, int level, unsigned flags,

@@ -30,7 +30,7 @@ CKKS_NO_RESCALE = 2
 EXPORTED = [
     "ckks_find_primes", "ckks_params_validate", "ckks_strerror", "ckks_last_error",
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
-    "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rescale",
+    "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_hoisted", "ckks_rescale",
     "ckks_mul_relin_rescale", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
 ]
 
@@ -86,6 +86,7 @@ def _load():
         "ckks_automorph": (i, [vp, vp, vp, i, i, u32, i, vp]),
         "ckks_keyswitch": (i, [vp, vp, vp, vp, i, vp]),
         "ckks_rotate": (i, [vp, vp, vp, i, i, u32p, pp, ctypes.c_uint, vp]),
+        "ckks_rotate_hoisted": (i, [vp, vp, i, i, i, u32p, pp, vp, vp]),
         "ckks_rescale": (i, [vp, vp, vp, i, i, vp]),
         "ckks_mul_relin_rescale": (i, [vp, vp, vp, vp, vp, i, i, ctypes.c_uint, vp]),
         "ckks_ptmatvec": (i, [vp, vp, i, vp, i, i, i, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
@@ -214,6 +215,13 @@ def ckks_rotate(ctx, d_ct_in, d_ct_out, batch, level, galois_elts, d_evks, flags
     g = (ctypes.c_uint32 * max(1, batch))(*[int(v) for v in galois_elts])
     _check(_lib.ckks_rotate(ctx.handle, _ptr(d_ct_in), _ptr(d_ct_out), batch, level, g, _ptr_list(d_evks),
                             flags, _stream(stream)), "ckks_rotate")
+
+
+def ckks_rotate_hoisted(ctx, d_ct_in, n_in, level, galois_elts, d_evks, d_ct_out, stream=None):
+    n_rot = len(galois_elts)
+    g = (ctypes.c_uint32 * max(1, n_rot))(*[int(v) for v in galois_elts])
+    _check(_lib.ckks_rotate_hoisted(ctx.handle, _ptr(d_ct_in), n_in, level, n_rot, g, _ptr_list(d_evks),
+                                    _ptr(d_ct_out), _stream(stream)), "ckks_rotate_hoisted")
 
 
 def ckks_rescale(ctx, d_in, d_out, batch, level, stream=None):

@@ -78,6 +78,20 @@ size_t ks_ws_words(const Ctx* c, int level);
 int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
              uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws);
 
+// Hoisted rotations of several inputs that share one decomposition each:
+// ks_decompose raises the digits of c1 (input i at c1 + i*c1_stride, NTT form)
+// to the extended basis and transforms them, into dec (input i at
+// dec + i*dec_stride, ks_dec_words per input); ks_hoisted_chunk key-switches
+// up to kMaxChunk rotations of ONE decomposed input (it[i].g and it[i].evk;
+// the output adds it[0].add[0] gathered through it[i].add_g), using
+// ks_back_words of `ws` per item.
+size_t ks_dec_words(const Ctx* c, int level);
+size_t ks_back_words(const Ctx* c, int level);
+int ks_decompose(Ctx* c, hipStream_t s, int level, int n_in, const uint64_t* c1, uint64_t c1_stride, uint64_t* dec,
+                 uint64_t dec_stride);
+int ks_hoisted_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, const uint64_t* dec,
+                     const uint64_t* c1, uint64_t out_stride, uint64_t* ws);
+
 int launch_automorph_ntt(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl, uint64_t pstride,
                          uint32_t g);
 int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, int npoly, int nl,

@@ -380,14 +380,287 @@ __global__ __launch_bounds__(kThreads) void ntt_row_combine_kernel(CombinePassAr
 }
 
 // ---------------------------------------------------------------------------
+// Hoisted rotations.  The digits of c1 are raised to the extended basis and
+// transformed once per input (ks_decompose: [beta][next][N], NTT form,
+// canonical); every rotation then gathers tau_g of those limbs straight into
+// the inner product, with no transform of its own.
+struct IPGatherArgs {
+  const uint64_t* E;  // the chunk's input: [beta][next][N] raised digits
+  const uint64_t* T;  // the chunk's input: c1, [nq][N] (limbs inside their own digit)
+  uint64_t* acc;      // item b: acc + b*acc_bstride, [2][next][N]
+  uint64_t acc_bstride;
+  const uint64_t* evk[kMaxChunk];
+  uint32_t g[kMaxChunk];
+  const PrimeConst* prime;
+  int log_n, level, next, beta, alpha, L, K;
+};
+
+constexpr int kGatherWords = 4;  // consecutive output words per thread
+
+// acc_b[t][w] = sum_j D_j[t][pi_g(w)] * evk_j.b[t][w] (and acc_a), D_j the
+// raised digit j (c1 itself for limbs inside digit j), pi_g the NTT-form
+// automorphism.  Lazy Montgomery products as in ntt_row_ip_kernel.
+__global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
+  const int t = blockIdx.y, item = blockIdx.z;
+  const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
+  const PrimeConst& pc = a.prime[keyl];
+  const uint64_t q = pc.q, mp = pc.mprime;
+  const int log_n = a.log_n;
+  const uint32_t w0 = (blockIdx.x * blockDim.x + threadIdx.x) * kGatherWords;
+  const uint32_t g = __builtin_amdgcn_readfirstlane(a.g[item]);
+  const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
+  const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
+  uint32_t src[kGatherWords];
+#pragma unroll
+  for (int i = 0; i < kGatherWords; ++i) src[i] = automorph_src(w0 + i, g, log_n);
+  uint64_t accb[kGatherWords], acca[kGatherWords];
+#pragma unroll
+  for (int i = 0; i < kGatherWords; ++i) accb[i] = acca[i] = 0;
+  for (int j = 0; j < a.beta; ++j) {
+    const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
+    const uint64_t* d = in_digit ? a.T + ((uint64_t)t << log_n) : a.E + ((uint64_t)(j * a.next + t) << log_n);
+    const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
+    const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
+    uint64_t x[kGatherWords];
+    ulonglong2 vb[kGatherWords / 2], va[kGatherWords / 2];
+#pragma unroll
+    for (int i = 0; i < kGatherWords; ++i) x[i] = d[src[i]];
+#pragma unroll
+    for (int i = 0; i < kGatherWords / 2; ++i) {
+      vb[i] = kb[i];
+      va[i] = ka[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kGatherWords / 2; ++i) {
+      accb[2 * i] += mont_mul_lazy(x[2 * i], vb[i].x, q, mp);
+      accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], vb[i].y, q, mp);
+      acca[2 * i] += mont_mul_lazy(x[2 * i], va[i].x, q, mp);
+      acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], va[i].y, q, mp);
+    }
+    if ((j & 3) == 3) {  // sums of up to 4 products below 2m stay below 8m < 2^63
+#pragma unroll
+      for (int i = 0; i < kGatherWords; ++i) {
+        accb[i] = reduce64(accb[i], q, pc.inv1);
+        acca[i] = reduce64(acca[i], q, pc.inv1);
+      }
+    }
+  }
+  ulonglong2* ob = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)t << log_n) + w0);
+  ulonglong2* oa = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)(a.next + t) << log_n) + w0);
+#pragma unroll
+  for (int i = 0; i < kGatherWords / 2; ++i) {
+    ulonglong2 vb, va;
+    vb.x = reduce_4q(mul_shoup_lazy(accb[2 * i], pc.r64, pc.r64p, q), q);
+    vb.y = reduce_4q(mul_shoup_lazy(accb[2 * i + 1], pc.r64, pc.r64p, q), q);
+    va.x = reduce_4q(mul_shoup_lazy(acca[2 * i], pc.r64, pc.r64p, q), q);
+    va.y = reduce_4q(mul_shoup_lazy(acca[2 * i + 1], pc.r64, pc.r64p, q), q);
+    ob[i] = vb;
+    oa[i] = va;
+  }
+}
+
+// ---------------------------------------------------------------------------
 size_t ws_words(const Ctx* c, int level) {
   const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
   return n * (nq /*T*/ + nq /*Y*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
 }
 
+// Steps F to I for n_items accumulators A (item i at A + i*per, [2][next][N]
+// NTT form) with W as the ModDown scratch: out = ModDown(acc) (+ add, gathered
+// through add_g) (+ accum).
+int ks_back(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t* A, uint64_t* W, uint64_t per,
+            uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs) {
+  const uint32_t N = c->N;
+  const int log_n = (int)c->log_n;
+  const int nq = level + 1, next = nq + (int)c->K;
+  const int lr = logb_row(log_n);
+  int rc;
+  // F, G: inverse NTT of the special limbs, times [phat_k^-1 N^-1]: y_k
+  {
+    NttJobs jobs;
+    uint32_t off[kMaxJobs];
+    for (int comp = 0; comp < 2; ++comp)
+      for (int k = 0; k < (int)c->K; ++k) {
+        off[jobs.n] = (uint32_t)(c->md.phinv + 2 * k);
+        jobs.add(comp * next + nq + k, comp * next + nq + k, (int)c->L + k);
+      }
+    if ((rc = ntt_run_scaled(c, s, A, A, per, per, n_items, jobs, true, 2, c->d_moddown, off))) return rc;
+  }
+  // H: ModDown conversion, then the forward column pass
+  {
+    ModDownArgs md;
+    memset(&md, 0, sizeof(md));
+    md.acc = A;
+    md.w = W;
+    md.acc_bstride = per;
+    md.w_bstride = per;
+    md.conv = c->d_moddown + c->md.conv;
+    md.prime = c->d_prime;
+    md.n = N;
+    md.level = level;
+    md.next = next;
+    md.L = (int)c->L;
+    md.K = (int)c->K;
+    if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
+    NttJobs jobs;
+    for (int comp = 0; comp < 2; ++comp)
+      for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
+    if ((rc = ntt_pass_only(c, s, W, W, per, per, n_items, jobs, false, true, 0, nullptr, nullptr))) return rc;
+  }
+  // I: forward row pass with the final combination
+  {
+    CombinePassArgs ca;
+    memset(&ca, 0, sizeof(ca));
+    ca.w = W;
+    ca.w_bstride = per;
+    ca.acc = A;
+    ca.acc_bstride = per;
+    ca.add[0] = it[0].add[0];
+    ca.add[1] = it[0].add[1];
+    ca.add_bstride = add_stride;
+    ca.accum = it[0].accum;
+    ca.accum_bstride = accum_stride;
+    ca.out = it[0].out;
+    ca.out_bstride = out_stride;
+    ca.pinv = c->d_moddown + c->md.pinv;
+    ca.tw = c->d_tw_fwd;
+    ca.prime = c->d_prime;
+    for (int i = 0; i < n_items; ++i) ca.g[i] = it[i].add_g;
+    ca.log_n = log_n;
+    ca.nq = nq;
+    ca.next = next;
+    ca.out_comp_limbs = out_comp_limbs;
+    auto fn = CKKS_PICK_PASS(ntt_row_combine_kernel, log_n, lr);
+    TraceScope ts(c, s, "ntt_row_combine", (double)n_items * 2 * nq * ((double)(N / 2) * lr + N));
+    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), 2 * nq, n_items), dim3(kThreads), 0, s, ca);
+    CKKS_HIP_CHECK(hipGetLastError());
+  }
+  return CKKS_OK;
+}
+
 }  // namespace
 
 size_t ks_ws_words(const Ctx* c, int level) { return ws_words(c, level); }
+
+size_t ks_dec_words(const Ctx* c, int level) {
+  const size_t nq = level + 1, next = nq + c->K;
+  return (size_t)c->N * (nq /*Y*/ + c->beta(level) * next /*E*/);
+}
+
+size_t ks_back_words(const Ctx* c, int level) {
+  const size_t nq = level + 1, next = nq + c->K;
+  return (size_t)c->N * (2 * next /*A*/ + 2 * nq /*W*/);
+}
+
+int ks_decompose(Ctx* c, hipStream_t s, int level, int n_in, const uint64_t* c1, uint64_t c1_stride, uint64_t* dec,
+                 uint64_t dec_stride) {
+  const uint32_t N = c->N;
+  const int log_n = (int)c->log_n;
+  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
+  uint64_t* Y = dec;
+  uint64_t* E = dec + (uint64_t)nq * N;
+  const int lr = logb_row(log_n);
+  int rc;
+  if (n_in > kMaxChunk) return set_error(CKKS_EINTERNAL, "too many inputs to decompose at once");
+  // inverse row pass of c1
+  {
+    GatherArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    ga.src = c1;
+    ga.src_bstride = c1_stride;
+    ga.side = nullptr;
+    ga.dst = Y;
+    ga.dst_bstride = dec_stride;
+    ga.tw = c->d_tw_inv;
+    ga.prime = c->d_prime;
+    ga.log_n = log_n;
+    auto fn = CKKS_PICK_PASS(intt_row_gather_kernel, log_n, lr);
+    if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
+    TraceScope ts(c, s, "intt_row_gather", (double)n_in * nq * (N / 2) * lr);
+    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_in), dim3(kThreads), 0, s, ga);
+    CKKS_HIP_CHECK(hipGetLastError());
+  }
+  // inverse column pass, times [qhat_i^-1 N^-1]: the ModUp inputs y_i
+  {
+    NttJobs jobs;
+    uint32_t off[kMaxJobs];
+    for (int j = 0; j < beta; ++j) {
+      const ModUpEntry& en = c->modup[level][j];
+      for (int i = en.lo; i < en.hi; ++i) {
+        off[jobs.n] = (uint32_t)(en.offset + 2 * (i - en.lo));
+        jobs.add(i, i, i);
+      }
+    }
+    if ((rc = ntt_pass_only(c, s, Y, Y, dec_stride, dec_stride, n_in, jobs, true, false, 2, c->d_modup, off)))
+      return rc;
+  }
+  // ModUp, then the whole forward transform of the converted limbs (canonical)
+  {
+    ModUpArgs mu;
+    memset(&mu, 0, sizeof(mu));
+    mu.x = Y;
+    mu.out = E;
+    mu.x_bstride = dec_stride;
+    mu.out_bstride = dec_stride;
+    mu.tables = c->d_modup;
+    mu.prime = c->d_prime;
+    mu.n = N;
+    mu.level = level;
+    mu.next = next;
+    mu.L = (int)c->L;
+    for (int j = 0; j < beta; ++j) {
+      const ModUpEntry& en = c->modup[level][j];
+      mu.lo[j] = en.lo;
+      mu.hi[j] = en.hi;
+      mu.offset[j] = en.offset;
+    }
+    if ((rc = launch_modup(c, s, mu, beta, n_in))) return rc;
+    NttJobs jobs;
+    for (int j = 0; j < beta; ++j)
+      for (int t = 0; t < next; ++t) {
+        if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
+        jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
+      }
+    if ((rc = ntt_pass_only(c, s, E, E, dec_stride, dec_stride, n_in, jobs, false, true, 0, nullptr, nullptr)))
+      return rc;
+    if ((rc = ntt_pass_only(c, s, E, E, dec_stride, dec_stride, n_in, jobs, false, false, 0, nullptr, nullptr)))
+      return rc;
+  }
+  return CKKS_OK;
+}
+
+int ks_hoisted_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, const uint64_t* dec,
+                     const uint64_t* c1, uint64_t out_stride, uint64_t* ws) {
+  const uint32_t N = c->N;
+  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
+  const uint64_t per = ks_back_words(c, level);
+  uint64_t* A = ws;
+  uint64_t* W = ws + (uint64_t)2 * next * N;
+  {
+    IPGatherArgs ip;
+    memset(&ip, 0, sizeof(ip));
+    ip.E = dec + (uint64_t)nq * N;
+    ip.T = c1;
+    ip.acc = A;
+    ip.acc_bstride = per;
+    for (int i = 0; i < n_items; ++i) {
+      ip.evk[i] = it[i].evk;
+      ip.g[i] = it[i].g;
+    }
+    ip.prime = c->d_prime;
+    ip.log_n = (int)c->log_n;
+    ip.level = level;
+    ip.next = next;
+    ip.beta = beta;
+    ip.alpha = (int)c->alpha;
+    ip.L = (int)c->L;
+    ip.K = (int)c->K;
+    TraceScope ts(c, s, "ip_gather", (double)n_items * next * N * (2.0 * beta + 2));
+    hipLaunchKernelGGL(ip_gather_kernel, dim3(N / (256 * kGatherWords), next, n_items), dim3(256), 0, s, ip);
+    CKKS_HIP_CHECK(hipGetLastError());
+  }
+  return ks_back(c, s, level, n_items, it, A, W, per, 0, 0, out_stride, nq);
+}
 
 int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
              uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
@@ -501,67 +774,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), next, n_items), dim3(1u << (lr - 3 + logkc)), 0, s, ip);
     CKKS_HIP_CHECK(hipGetLastError());
   }
-  // F, G: inverse NTT of the special limbs, times [phat_k^-1 N^-1]: y_k
-  {
-    NttJobs jobs;
-    uint32_t off[kMaxJobs];
-    for (int comp = 0; comp < 2; ++comp)
-      for (int k = 0; k < (int)c->K; ++k) {
-        off[jobs.n] = (uint32_t)(c->md.phinv + 2 * k);
-        jobs.add(comp * next + nq + k, comp * next + nq + k, (int)c->L + k);
-      }
-    if ((rc = ntt_run_scaled(c, s, A, A, per, per, n_items, jobs, true, 2, c->d_moddown, off))) return rc;
-  }
-  // H: ModDown conversion, then the forward column pass
-  {
-    ModDownArgs md;
-    memset(&md, 0, sizeof(md));
-    md.acc = A;
-    md.w = W;
-    md.acc_bstride = per;
-    md.w_bstride = per;
-    md.conv = c->d_moddown + c->md.conv;
-    md.prime = c->d_prime;
-    md.n = N;
-    md.level = level;
-    md.next = next;
-    md.L = (int)c->L;
-    md.K = (int)c->K;
-    if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
-    NttJobs jobs;
-    for (int comp = 0; comp < 2; ++comp)
-      for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
-    if ((rc = ntt_pass_only(c, s, W, W, per, per, n_items, jobs, false, true, 0, nullptr, nullptr))) return rc;
-  }
-  // I: forward row pass with the final combination
-  {
-    CombinePassArgs ca;
-    memset(&ca, 0, sizeof(ca));
-    ca.w = W;
-    ca.w_bstride = per;
-    ca.acc = A;
-    ca.acc_bstride = per;
-    ca.add[0] = it[0].add[0];
-    ca.add[1] = it[0].add[1];
-    ca.add_bstride = add_stride;
-    ca.accum = it[0].accum;
-    ca.accum_bstride = accum_stride;
-    ca.out = it[0].out;
-    ca.out_bstride = out_stride;
-    ca.pinv = c->d_moddown + c->md.pinv;
-    ca.tw = c->d_tw_fwd;
-    ca.prime = c->d_prime;
-    for (int i = 0; i < n_items; ++i) ca.g[i] = it[i].add_g;
-    ca.log_n = log_n;
-    ca.nq = nq;
-    ca.next = next;
-    ca.out_comp_limbs = out_comp_limbs;
-    auto fn = CKKS_PICK_PASS(ntt_row_combine_kernel, log_n, lr);
-    TraceScope ts(c, s, "ntt_row_combine", (double)n_items * 2 * nq * ((double)(N / 2) * lr + N));
-    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), 2 * nq, n_items), dim3(kThreads), 0, s, ca);
-    CKKS_HIP_CHECK(hipGetLastError());
-  }
-  return CKKS_OK;
+  return ks_back(c, s, level, n_items, it, A, W, per, add_stride, accum_stride, out_stride, out_comp_limbs);
 }
 
 }  // namespace ckks

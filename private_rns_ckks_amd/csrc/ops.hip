@@ -167,6 +167,74 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
   return join_lanes(c, s, lanes, rc);
 }
 
+// Hoisted rotations: input c (at in + c*in_stride, [2][l+1][N]) rotated by
+// g[r] (key evk[r]) into out + c*out_in_stride + r*out_rot_stride.  Inputs are
+// decomposed in groups of up to kMaxChunk on s; the rotations of each input
+// then run in chunks alternating over the lanes.
+int rotate_hoisted(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride, int n_in, int level, int n_rot,
+                   const uint32_t* g, const uint64_t* const* evk, uint64_t* out, uint64_t out_in_stride,
+                   uint64_t out_rot_stride) {
+  const int nq = level + 1;
+  const uint64_t ct_words = 2ull * nq * c->N;
+  const uint64_t dec_per = ks_dec_words(c, level), back_per = ks_back_words(c, level);
+  const int chunk = g_chunk_default();
+  int rc;
+  std::vector<int> rots;  // rotations that need a key switch
+  for (int r = 0; r < n_rot; ++r) {
+    if (g[r] != 1) {
+      rots.push_back(r);
+      continue;
+    }
+    for (int ci = 0; ci < n_in; ++ci)
+      CKKS_HIP_CHECK(hipMemcpyAsync(out + ci * out_in_stride + r * out_rot_stride, in + ci * in_stride, ct_words * 8,
+                                    hipMemcpyDeviceToDevice, s));
+  }
+  if (rots.empty() || n_in == 0) return CKKS_OK;
+  const int group = std::min(n_in, kMaxChunk);
+  const int per_input = ((int)rots.size() + chunk - 1) / chunk;
+  const int lanes = std::min(per_input * n_in, g_lanes_default());
+  if ((rc = ensure_workspace(c, dec_per * group + back_per * chunk * lanes))) return rc;
+  uint64_t* dec = c->ws;
+  uint64_t* back = c->ws + dec_per * group;
+  int k = 0;  // chunk counter, for the lane choice
+  for (int c0 = 0; c0 < n_in; c0 += group) {
+    const int n = std::min(group, n_in - c0);
+    if ((rc = ks_decompose(c, s, level, n, in + c0 * in_stride + (uint64_t)nq * c->N, in_stride, dec, dec_per)))
+      return rc;
+    if ((rc = fork_lanes(c, s, lanes))) return rc;
+    for (int ci = c0; ci < c0 + n && rc == CKKS_OK; ++ci) {
+      for (size_t p = 0; p < rots.size() && rc == CKKS_OK; p += chunk, ++k) {
+        const int m = (int)std::min<size_t>(chunk, rots.size() - p);
+        KSItem items[kMaxChunk];
+        memset(items, 0, sizeof(items));
+        for (int i = 0; i < m; ++i) {
+          const int r = rots[p + i];
+          items[i].g = g[r];
+          items[i].evk = evk[r];
+          items[i].add[0] = in + ci * in_stride;  // c0, gathered through g
+          items[i].add_g = g[r];
+          items[i].out = out + ci * out_in_stride + r * out_rot_stride;
+        }
+        // consecutive entries of rots are not always consecutive rotations:
+        // output items must advance by one stride, so split at gaps
+        int i0 = 0;
+        while (i0 < m && rc == CKKS_OK) {
+          int i1 = i0 + 1;
+          while (i1 < m && rots[p + i1] == rots[p + i1 - 1] + 1) ++i1;
+          rc = ks_hoisted_chunk(c, lane_stream(c, s, lanes, k), level, i1 - i0, items + i0,
+                                dec + (uint64_t)(ci - c0) * dec_per, in + ci * in_stride + (uint64_t)nq * c->N,
+                                out_rot_stride, back + back_per * chunk * (k % lanes));
+          i0 = i1;
+        }
+      }
+    }
+    // the next group's decomposition overwrites dec: wait for this group's chunks
+    rc = join_lanes(c, s, lanes, rc);
+    if (rc) return rc;
+  }
+  return CKKS_OK;
+}
+
 }  // namespace
 }  // namespace ckks
 
@@ -252,6 +320,26 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
   if (batch > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
   return rotate_batch(ctx, stream, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
                       flags);
+}
+
+int ckks_rotate_hoisted(ckks_ctx* ctx, const uint64_t* d_ct_in, int n_in, int level, int n_rot,
+                        const uint32_t* galois_elts, const uint64_t* const* d_evks, uint64_t* d_ct_out,
+                        ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_ct_in || !d_ct_out || n_in < 0 || n_rot < 0 || (n_rot > 0 && (!galois_elts || !d_evks)))
+    return set_error(CKKS_EINVAL, "NULL pointer or bad count");
+  if (misaligned(d_ct_in) || misaligned(d_ct_out))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  for (int r = 0; r < n_rot; ++r) {
+    if ((rc = check_galois(ctx, galois_elts[r]))) return rc;
+    if (galois_elts[r] != 1 && (!d_evks[r] || misaligned(d_evks[r])))
+      return set_error(CKKS_EINVAL, "NULL or misaligned key pointer");
+  }
+  if (n_rot > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
+  const uint64_t ct = 2ull * (level + 1) * ctx->N;
+  return rotate_hoisted(ctx, stream, d_ct_in, ct, n_in, level, n_rot, galois_elts, d_evks, d_ct_out, n_rot * ct, ct);
 }
 
 int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch, int level, ckks_stream_t stream) {
@@ -376,16 +464,11 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
       rc = set_error(CKKS_EHIP, "copy");
       break;
     }
-    std::vector<uint32_t> gs(n_in);
-    std::vector<const uint64_t*> ks(n_in);
-    for (int b = 1; b < n1 && !rc; ++b) {
-      for (int c = 0; c < n_in; ++c) {
-        gs[c] = baby_galois[b - 1];
-        ks[c] = d_evk_baby[b - 1];
-      }
-      rc = rotate_batch(ctx, stream, d_x, baby + (uint64_t)b * n_in * ct, ct, n_in, level, gs.data(), ks.data(), 0);
-    }
-    if (rc) break;
+    // baby steps: the n1-1 rotations of each input share one decomposition;
+    // baby step b of input c lands at baby[b][c]
+    if (n1 > 1 && (rc = rotate_hoisted(ctx, stream, d_x, ct, n_in, level, n1 - 1, baby_galois, d_evk_baby,
+                                       baby + (uint64_t)n_in * ct, ct, (uint64_t)n_in * ct)))
+      break;
     PtMacArgs pm;
     pm.diags = d_diags;
     pm.baby = baby;

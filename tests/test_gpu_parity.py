@@ -219,6 +219,46 @@ def test_rotate_batch_chunks(lib, orc, c3small):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("level", [23, 12])
+def test_rotate_hoisted_parity(lib, orc, c3small, level):
+    """Hoisted rotations of 3 inputs by 6 elements (one the identity), in
+    chunks across the internal streams, against the oracle's hoisted rotation."""
+    ctx, P = c3small
+    ks = [1, 3, 0, 100, 2047, 5]
+    n_in, R = 3, len(ks)
+    announce("hoisted rotations level=%d" % level)
+    cts = S.uniform_limbs(S.stream(level, "gpu/hoist/ct"), P.q[: level + 1], P.N, lead=(n_in, 2))
+    gs = [P.galois(k) for k in ks]
+    keys_h = [S.uniform_limbs(S.stream(r, "gpu/hoist/k"), P.mods, P.N, lead=(P.dnum, 2)) for r in range(R)]
+    out = empty_dev((n_in, R) + cts.shape[1:])
+    lib.ckks_rotate_hoisted(ctx, to_dev(cts), n_in, level, gs, [to_dev(k) for k in keys_h], out)
+    got = to_host(out)
+    for c in range(n_in):
+        assert np.array_equal(got[c], orc.rotate_hoisted(P, level, cts[c], gs, keys_h)), c
+
+
+def test_rotate_hoisted_c1_encrypted(lib, orc, c1):
+    """C1: real encryption, four hoisted rotations; words equal the oracle's and decrypt to the shifts."""
+    from helpers import encrypt_slots, galois_key, rel_err, secret
+
+    ctx, P = c1
+    c = S.CONFIGS["C1"]
+    level = P.L - 1
+    s, s_ntt = secret(orc, P, 4, c["h"])
+    z = S.uniform_slots(S.stream(4, "gpu/hc1/msg"), P.N // 2, complex_values=True)
+    ct = encrypt_slots(orc, P, s_ntt, z, c["scale"], level, 4, "gpu/hc1/ct")
+    ks = [1, 2, 7, 100]
+    gs = [P.galois(k) for k in ks]
+    keys_h = [galois_key(orc, P, s_ntt, g, 4, "gpu/hc1/k%d" % g) for g in gs]
+    out = empty_dev((1, len(ks)) + ct.shape)
+    lib.ckks_rotate_hoisted(ctx, to_dev(ct[None]), 1, level, gs, [to_dev(k) for k in keys_h], out)
+    got = to_host(out)[0]
+    ref = orc.rotate_hoisted(P, level, ct, gs, keys_h)
+    assert np.array_equal(got, ref)
+    for r, k in enumerate(ks):
+        assert rel_err(orc.decrypt(P, level, got[r], s_ntt, c["scale"]), np.roll(z, -k)) < 2 ** -12, k
+
+
 def test_rotate_errors(lib, orc, c3small):
     ctx, P = c3small
     x = empty_dev((1, 2, 24, P.N))
