@@ -9,6 +9,7 @@
 #include "arith.h"
 #include "automorph.h"
 #include "kernels.h"
+#include "ntt_core.h"
 
 namespace ckks {
 
@@ -202,42 +203,54 @@ __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
 }
 
 // BSGS inner sums: inner[o][g][comp][i] = sum_c sum_b diag[o][c][g][b][i] * baby[b][c][comp][i].
-// blockIdx.y = limb i, blockIdx.z = o * n2 + g.
+// A workgroup owns 256 coefficients of limb i for output o and loops over the
+// giant steps g; the (c, b) terms go in groups of 8 (the split accumulator's
+// capacity) with every load of a group issued before its products.  The
+// diagonals stream from HBM once; the baby-step words a thread needs are the
+// same for every g and every o, and the workgroup order below keeps the
+// workgroups of one coefficient tile (all o) together on one XCD, so they are
+// served by that XCD's L2.
 __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int i = blockIdx.y;
-  const int o = blockIdx.z / a.n2, g = blockIdx.z % a.n2;
-  const PrimeConst pc = a.prime[i];
+  const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
+  const int o = (int)gp.tile, i = gp.job;
+  const uint32_t c = (uint32_t)gp.item * blockDim.x + threadIdx.x;
+  const RedConst pc = red_const((ConstPrime)a.prime, i);
   const uint64_t limbs = (uint64_t)(a.level + 1);
   const uint64_t off = (uint64_t)i * a.n + c;
-  Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
-  uint64_t r0 = 0, r1 = 0;
-  int terms = 0;
-  for (int ci = 0; ci < a.n_in; ++ci) {
-    for (int b = 0; b < a.n1; ++b) {
-      const uint64_t pt = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * limbs * a.n + off];
-      const uint64_t* ct = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * limbs * a.n;
-      const uint64_t c0 = ct[off], c1 = ct[limbs * a.n + off];
-      const uint32_t pl = lo30(pt), ph = hi30(pt);
-      acc3_mac(s0, pl, ph, lo30(c0), hi30(c0));
-      acc3_mac(s1, pl, ph, lo30(c1), hi30(c1));
-      if (++terms == 8) {  // fold every 8 terms
-        r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        s0 = {0, 0, 0};
-        s1 = {0, 0, 0};
-        terms = 0;
+  const uint64_t ln = limbs * a.n;
+  const int terms = a.n_in * a.n1;
+  for (int g = 0; g < a.n2; ++g) {
+    uint64_t r0 = 0, r1 = 0;
+    for (int t0 = 0; t0 < terms; t0 += 8) {
+      uint64_t pt[8], c0[8], c1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pt[k] = c0[k] = c1[k] = 0;
+        const int t = t0 + k;
+        if (t < terms) {
+          const int ci = t / a.n1, b = t % a.n1;
+          pt[k] = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * ln + off];
+          const uint64_t* ct = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * ln + off;
+          c0[k] = ct[0];
+          c1[k] = ct[ln];
+        }
       }
+      Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t pl = lo30(pt[k]), ph = hi30(pt[k]);
+        acc3_mac(s0, pl, ph, lo30(c0[k]), hi30(c0[k]));
+        acc3_mac(s1, pl, ph, lo30(c1[k]), hi30(c1[k]));
+      }
+      r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
     }
+    uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 2 * ln;
+    out[off] = r0;
+    out[ln + off] = r1;
   }
-  r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-  r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-  uint64_t* out = a.out + (uint64_t)blockIdx.z * 2 * limbs * a.n;
-  out[off] = r0;
-  out[limbs * a.n + off] = r1;
 }
 
-// out = x + y on [nl] limbs per item (limb i uses prime i).
 __global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, uint64_t bstride, int nl,
                            const PrimeConst* prime, int log_n) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -316,7 +329,7 @@ int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
 
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ptmac", (double)n_out * a.n2 * (a.level + 1) * 2 * (a.n_in * a.n1 + 1) * c->N);
-  hipLaunchKernelGGL(ptmac_kernel, dim3(c->N / 256, a.level + 1, n_out * a.n2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(ptmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
