@@ -211,7 +211,9 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
  *   d_y      [n_out][2][level][N] (level+1 with CKKS_NO_RESCALE)
  * y_o = sum_g Rot_g( sum_c sum_b diag(o,c,g,b) * Rot_b(x_c) ), then rescale.
  * The baby-step rotations are computed once and shared by all outputs, as
- * hoisted rotations of each input (ckks_rotate_hoisted). */
+ * hoisted rotations of each input (ckks_rotate_hoisted).  The intermediate
+ * ciphertexts live in a context-owned buffer grown on demand (growing it
+ * synchronises the device); otherwise the call only enqueues work. */
 int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
                   const uint32_t* baby_galois, const uint64_t* const* d_evk_baby, const uint32_t* giant_galois,
                   const uint64_t* const* d_evk_giant, uint64_t* d_y, int level, unsigned flags,

@@ -16,21 +16,26 @@ int set_error(int code, const std::string& msg) {
   return code;
 }
 
-int ensure_workspace(Ctx* c, size_t words) {
-  if (words <= c->ws_words) return CKKS_OK;
-  if (c->ws) {
+// Grows a context-owned device buffer; the device is synchronised before the
+// old buffer is freed, since queued work may still use it.
+static int grow(uint64_t*& buf, size_t& have, size_t words, const char* what) {
+  if (words <= have) return CKKS_OK;
+  if (buf) {
     CKKS_HIP_CHECK(hipDeviceSynchronize());
-    CKKS_HIP_CHECK(hipFree(c->ws));
-    c->ws = nullptr;
-    c->ws_words = 0;
+    CKKS_HIP_CHECK(hipFree(buf));
+    buf = nullptr;
+    have = 0;
   }
-  if (hipMalloc((void**)&c->ws, words * sizeof(uint64_t)) != hipSuccess) {
+  if (hipMalloc((void**)&buf, words * sizeof(uint64_t)) != hipSuccess) {
     (void)hipGetLastError();
-    return set_error(CKKS_ENOMEM, "workspace allocation of " + std::to_string(words * 8) + " bytes failed");
+    return set_error(CKKS_ENOMEM, std::string(what) + " allocation of " + std::to_string(words * 8) + " bytes failed");
   }
-  c->ws_words = words;
+  have = words;
   return CKKS_OK;
 }
+
+int ensure_workspace(Ctx* c, size_t words) { return grow(c->ws, c->ws_words, words, "workspace"); }
+int ensure_aux(Ctx* c, size_t words) { return grow(c->aux, c->aux_words, words, "operand buffer"); }
 
 TraceScope::TraceScope(Ctx* c, hipStream_t s, const char* family, double units)
     : c_(c), s_(s), on_(!c->trace.name.empty() && c->trace.name == family) {
@@ -112,7 +117,7 @@ static void destroy(Ctx* c) {
     if (c->join_ev[i]) (void)hipEventDestroy(c->join_ev[i]);
   }
   if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
-  void* bufs[] = {c->d_prime, c->d_tw_fwd, c->d_tw_inv, c->d_modup, c->d_moddown, c->d_rescale, c->ws};
+  void* bufs[] = {c->d_prime, c->d_tw_fwd, c->d_tw_inv, c->d_modup, c->d_moddown, c->d_rescale, c->ws, c->aux};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete c;

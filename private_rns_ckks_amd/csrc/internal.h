@@ -67,6 +67,8 @@ struct Ctx {
   uint64_t* d_rescale = nullptr;  // [L][L][4]: for level l, limb i < l: {ql^-1, Shoup, ql mod q_i, 0}
   uint64_t* ws = nullptr;         // workspace
   size_t ws_words = 0;
+  uint64_t* aux = nullptr;        // intermediate operands of composite calls (BSGS matvec)
+  size_t aux_words = 0;
   TraceState trace;
   // Internal streams (default priority) on which consecutive chunks of a
   // batch run concurrently, forked from and joined back to the caller's
@@ -89,6 +91,7 @@ int set_error(int code, const std::string& msg);
   } while (0)
 
 int ensure_workspace(Ctx* c, size_t words);
+int ensure_aux(Ctx* c, size_t words);
 int ensure_lanes(Ctx* c);
 
 // Records the start event (if `family` is being traced) on construction and

@@ -444,20 +444,13 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
   const uint32_t N = ctx->N;
   const int nq = level + 1;
   const uint64_t ct = 2ull * nq * N;
-  // baby [n1][n_in] ciphertexts, inner [n_out][n2], rotated [n_out][n2], sum [n_out]
-  uint64_t *baby = nullptr, *inner = nullptr, *rot = nullptr;
-  auto cleanup = [&]() {
-    if (baby) (void)hipFree(baby);
-    if (inner) (void)hipFree(inner);
-    if (rot) (void)hipFree(rot);
-  };
-  if (hipMalloc((void**)&baby, ct * n1 * n_in * 8) != hipSuccess ||
-      hipMalloc((void**)&inner, ct * n_out * n2 * 8) != hipSuccess ||
-      hipMalloc((void**)&rot, ct * n_out * n2 * 8) != hipSuccess) {
-    (void)hipGetLastError();
-    cleanup();
-    return set_error(CKKS_ENOMEM, "ptmatvec buffers");
-  }
+  // baby [n1][n_in] ciphertexts, inner [n_out][n2], rotated [n_out][n2]: in
+  // the context's operand buffer, kept between calls
+  const uint64_t n_baby = ct * n1 * n_in, n_inner = ct * n_out * n2;
+  if ((rc = ensure_aux(ctx, n_baby + 2 * n_inner))) return rc;
+  uint64_t* baby = ctx->aux;
+  uint64_t* inner = baby + n_baby;
+  uint64_t* rot = inner + n_inner;
   rc = CKKS_OK;
   do {
     if (hipMemcpyAsync(baby, d_x, ct * n_in * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess) {
@@ -502,8 +495,6 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
           rc = set_error(CKKS_EHIP, "copy");
     }
   } while (0);
-  if (hipStreamSynchronize(stream) != hipSuccess && !rc) rc = set_error(CKKS_EHIP, "stream sync");
-  cleanup();
   return rc;
 }
 
