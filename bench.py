@@ -188,27 +188,36 @@ def main():
     value = B * args.steps / (ms / 1e3)
     log("HRot/s %.1f  (%.3f ms per batch of %d)" % (value, ms_step, B))
 
-    # dominant kernel roofline, from the events recorded around each of its launches
+    # dominant kernel roofline, from the events recorded around each of its
+    # launches: the bound is whichever of its algorithmic ALU work (at the
+    # int32 VALU peak) and algorithmic bytes (at the HBM peak) takes longer
     roof = None
     if kstat["launches"]:
         avg_s = kstat["total_ms"] / kstat["launches"] / 1e3
         per_launch = kstat["alg_units"] / kstat["launches"]
-        achieved = per_launch * kstat["ops_per_unit"] / avg_s / 1e12
+        ops = per_launch * kstat["ops_per_unit"]
+        alg_bytes = B * args.steps / kstat["launches"] * IP_LIMBS_PER_ITEM * N * 8
+        alu_tops = ops / avg_s / 1e12
+        hbm_gbps = alg_bytes / avg_s / 1e9
+        hbm_bound = alg_bytes / (HBM_PEAK_GBPS * 1e9) > ops / (VALU_PEAK_TOPS * 1e12)
         roof = {
             "kernel": kstat["name"],
-            "bound": "alu",
-            "achieved": round(achieved, 3),
-            "peak": round(VALU_PEAK_TOPS, 2),
-            "unit": "Tops/s",
-            "frac": round(achieved / VALU_PEAK_TOPS, 4),
+            "bound": "hbm" if hbm_bound else "alu",
+            "achieved": round(hbm_gbps if hbm_bound else alu_tops, 3),
+            "peak": HBM_PEAK_GBPS if hbm_bound else round(VALU_PEAK_TOPS, 2),
+            "unit": "GB/s" if hbm_bound else "Tops/s",
+            "frac": round(hbm_gbps / HBM_PEAK_GBPS if hbm_bound else alu_tops / VALU_PEAK_TOPS, 4),
             "traffic": measured_traffic(),
-            "alg_bytes_per_launch": int(B * args.steps / kstat["launches"] * IP_LIMBS_PER_ITEM * N * 8),
+            "alg_bytes_per_launch": int(alg_bytes),
+            "alg_ops_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"],
+                                                               kstat["ops_per_unit"]),
+            "alu_frac": round(alu_tops / VALU_PEAK_TOPS, 4),
+            "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
             "avg_launch_us": round(avg_s * 1e6, 2),
             "launches": kstat["launches"],
-            "work_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"], kstat["ops_per_unit"]),
-            "hbm_frac_step": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
             "note": "chunks of the batch run on two streams at once, so a launch's duration includes "
-                    "co-running kernels of the other stream; alu_roofline_frac covers the whole step",
+                    "co-running kernels of the other stream; alu_roofline_frac and hbm_roofline_frac "
+                    "cover the whole step",
         }
 
     ntt = None

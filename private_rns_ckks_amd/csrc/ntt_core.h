@@ -93,7 +93,13 @@ __device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t 
 // R stages in registers on the 2^R words x[] of one thread; the words are
 // rows base + (i << pos) of column col.  Global stage of sub-stage s is
 // s0 + logb - pos - R + s.
-template <int R, bool INV, bool LAZY, bool COLFAST>
+// With UTW the round's twiddles are the same for every thread of the
+// workgroup (a column-pass round on row bits [pos, pos+R) whose base rows are
+// below 2^pos, so the twiddle index depends on the group only): they are read
+// with scalar loads into SGPRs.
+typedef const __attribute__((address_space(4))) uint64_t* ConstTw;
+
+template <int R, bool INV, bool LAZY, bool COLFAST, bool UTW = false>
 __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int pos, int col, int logb, uint32_t tile,
                                            uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
   constexpr int E = 1 << R;
@@ -105,9 +111,16 @@ __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int 
 #pragma unroll
     for (int g = 0; g < (1 << s); ++g) {
       const int i0 = g * 2 * half;
-      const uint32_t j = tile_index<COLFAST>(tile, base + (i0 << pos), col, logb, log_n);
       uint64_t w, wp;
-      load_tw(tw, (1u << S) + (j >> (log_n - S)), w, wp);
+      if (UTW) {
+        const uint32_t ti = (1u << S) + (((uint32_t)i0 << pos) >> (logb - S));
+        const ConstTw twc = (ConstTw)tw;
+        w = twc[2 * ti];
+        wp = twc[2 * ti + 1];
+      } else {
+        const uint32_t j = tile_index<COLFAST>(tile, base + (i0 << pos), col, logb, log_n);
+        load_tw(tw, (1u << S) + (j >> (log_n - S)), w, wp);
+      }
 #pragma unroll
       for (int m = 0; m < half; ++m) {
         if (INV) gs_butterfly(x[i0 + m], x[i0 + m + half], w, wp, q);
@@ -191,7 +204,7 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
       x[i] = stage_in ? lds[lds_index<COLFAST, RB, ROWS>(row, col)]
                       : io.load(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
     }
-    round_regs<R1, INV, LAZY, COLFAST>(x, base, pos1, col, LOGB, tile, s0, log_n, tw, q);
+    round_regs<R1, INV, LAZY, COLFAST, COLFAST && !INV>(x, base, pos1, col, LOGB, tile, s0, log_n, tw, q);
     // each thread writes back exactly the words it read: no hazard with other threads
 #pragma unroll
     for (int i = 0; i < (1 << R1); ++i) lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos1), col)] = x[i];
@@ -203,7 +216,7 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
     uint64_t x[1 << R2];
 #pragma unroll
     for (int i = 0; i < (1 << R2); ++i) x[i] = lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)];
-    round_regs<R2, INV, LAZY, COLFAST>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
+    round_regs<R2, INV, LAZY, COLFAST, COLFAST && INV>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
     if (fin.mode == 1) {
       if (INV) {
 #pragma unroll
