@@ -310,10 +310,14 @@ def test_mul_relin_rescale_parity(lib, orc, c3small, flags):
     assert np.array_equal(to_host(out), orc.mul_relin_rescale(P, level, a, b, rlk, flags))
 
 
-def test_ptmatvec_parity(lib, orc, c3small):
+@pytest.mark.parametrize("shape", [(12, 2, 3, 4, 3), (5, 1, 2, 3, 1), (20, 5, 2, 1, 4), (8, 3, 4, 5, 2)],
+                         ids=lambda s: "l%d_in%d_out%d_n1%d_n2%d" % s)
+def test_ptmatvec_parity(lib, orc, c3small, shape):
+    """BSGS shapes with partial 8-term groups, a single baby or giant step and
+    more than 8 (c, b) terms."""
     ctx, P = c3small
-    level, n_in, n_out, n1, n2 = 12, 2, 3, 4, 3
-    announce("ptmatvec small")
+    level, n_in, n_out, n1, n2 = shape
+    announce("ptmatvec %s" % (shape,))
     x = S.uniform_limbs(S.stream(4, "gpu/pmv/x"), P.q[: level + 1], P.N, lead=(n_in, 2))
     diags = S.uniform_limbs(S.stream(4, "gpu/pmv/d"), P.q[: level + 1], P.N, lead=(n_out, n_in, n2, n1))
     gb = [P.galois(b) for b in range(1, n1)]
