@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
     """Compile the C oracle with gcc into oracle/liboracle.so."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=gnu11", "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=gnu11", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -88,6 +88,8 @@ def lib():
             "orc_rotate": (None, [pp, c_int, u64p, c_u32, u64p, u64p, ctypes.c_uint]),
             "orc_rotate_batch": (None, [pp, c_int, u64p, c_int, u32p, ctypes.POINTER(u64p), u64p, ctypes.c_uint]),
             "orc_rotate_hoisted": (None, [pp, c_int, u64p, c_int, u32p, ctypes.POINTER(u64p), u64p]),
+            "orc_poly_eval": (c_int, [pp, c_int, u64p, c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double), c_int,
+                                      u64p, u64p, ctypes.POINTER(ctypes.c_double)]),
             "orc_rescale": (c_int, [pp, c_int, u64p, u64p]),
             "orc_tensor": (None, [pp, c_int, u64p, u64p, u64p]),
             "orc_mul_relin_rescale": (c_int, [pp, c_int, u64p, u64p, u64p, u64p, c_int, ctypes.c_uint]),
@@ -331,6 +333,24 @@ def mul_relin_rescale(P: Params, level: int, a, b, rlk, flags: int = 0):
     if rc != 0:
         raise ValueError("rescale at level 0")
     return out
+
+
+def poly_eval(P: Params, level: int, cts, scale: float, coeffs, rlk):
+    """p(x) = sum_k coeffs[k] x^k on [B][2][l+1][N] ciphertexts by Horner's
+    rule; returns ([B][2][l-d+1][N], output scale)."""
+    cts = _arr(cts)
+    B = cts.shape[0]
+    d = len(coeffs) - 1
+    out = np.empty((B, 2, level - d + 1, P.N), dtype=np.uint64)
+    c = (ctypes.c_double * len(coeffs))(*[float(v) for v in coeffs])
+    s = ctypes.c_double(0.0)
+    rc = lib().orc_poly_eval(P.ref(), level, _u64(cts), B, float(scale), c, d, _u64(_arr(rlk)), _u64(out),
+                             ctypes.byref(s))
+    if rc == -2:
+        raise ValueError("degree must be 1..level")
+    if rc == -3:
+        raise ValueError("a rounded constant reaches 2^62")
+    return out, s.value
 
 
 def ptmatvec(P: Params, level: int, x, diags, g_baby, evk_baby, g_giant, evk_giant, flags: int = 0,

@@ -41,6 +41,7 @@
  *   ciphertext: [2][l+1][N] in NTT form, component 0 = c0, 1 = c1;
  *   switch key: [dnum][2][L+K][N] in NTT form, component 0 = b, 1 = a.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -742,6 +743,95 @@ int orc_ptmatvec(const orc_params *P, int level, const uint64_t *x, int n_in, co
     free(acc);
     free(tmp);
     free(rot);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Polynomial evaluation                                                 */
+/* ------------------------------------------------------------------ */
+
+/* round(x) as a signed integer, or -1 in *bad when |x| >= 2^62. */
+static int64_t round_checked(double x, int *bad)
+{
+    if (!(fabs(x) < 4611686018427387904.0)) { *bad = 1; return 0; }
+    return llround(x);
+}
+
+/* Each limb times the integer v (signed), in place: [nlimb][N]. */
+static void poly_mul_int(uint64_t *a, int nlimb, int log_n, const uint64_t *mods, int64_t v)
+{
+    uint64_t n = (uint64_t)1 << log_n;
+    for (int i = 0; i < nlimb; i++) {
+        uint64_t k = smod((i128)v, mods[i]);
+        for (uint64_t c = 0; c < n; c++) a[(uint64_t)i * n + c] = mulmod(a[(uint64_t)i * n + c], k, mods[i]);
+    }
+}
+
+/* The constant polynomial v (signed) added in NTT form: the transform of a
+ * constant is that constant in every word. */
+static void poly_add_int(uint64_t *a, int nlimb, int log_n, const uint64_t *mods, int64_t v)
+{
+    uint64_t n = (uint64_t)1 << log_n;
+    for (int i = 0; i < nlimb; i++) {
+        uint64_t k = smod((i128)v, mods[i]);
+        for (uint64_t c = 0; c < n; c++) a[(uint64_t)i * n + c] = addmod(a[(uint64_t)i * n + c], k, mods[i]);
+    }
+}
+
+/* p(x) = sum_{k<=d} c[k] x^k on each of `batch` ciphertexts ct
+ * ([batch][2][l+1][N], NTT form, scale s_x), by Horner's rule: depth d.
+ *   acc = c[d] * x       every limb times K = round(c[d] * q_l), then rescale;
+ *                        the scale stays s_x (the factor q_l is divided out)
+ *   acc += c[d-1]        round(c[d-1] * s_acc) added to c0
+ *   for k = d-2 .. 0     x' = x on acc's limbs; with l' the level of acc:
+ *                        acc = rescale(relin(acc * x')), s_acc = s_acc * s_x / q_l';
+ *                        acc += round(c[k] * s_acc)
+ * out: [batch][2][l-d+1][N]; *out_scale the final scale.  Returns -2 when
+ * level < d or d < 1, -3 when a rounded constant reaches 2^62. */
+int orc_poly_eval(const orc_params *P, int level, const uint64_t *ct, int batch, double scale, const double *c,
+                  int degree, const uint64_t *rlk, uint64_t *out, double *out_scale)
+{
+    if (degree < 1 || level < degree) return -2;
+    uint64_t n = (uint64_t)1 << P->log_n;
+    int d = degree, bad = 0;
+    /* the constants first, so a range error leaves out untouched */
+    int64_t kmul = round_checked(c[d] * (double)P->mod[level], &bad);
+    int64_t kadd[64];
+    double s_acc = scale;
+    kadd[d - 1] = round_checked(c[d - 1] * s_acc, &bad);
+    for (int k = d - 2, l = level - 1; k >= 0; k--, l--) {
+        s_acc = s_acc * scale / (double)P->mod[l];
+        kadd[k] = round_checked(c[k] * s_acc, &bad);
+    }
+    if (bad) return -3;
+    uint64_t csz_in = (uint64_t)2 * (level + 1) * n;
+    uint64_t *acc = malloc(sizeof(uint64_t) * csz_in), *nxt = malloc(sizeof(uint64_t) * csz_in);
+    uint64_t *xd = malloc(sizeof(uint64_t) * csz_in);
+    for (int b = 0; b < batch; b++) {
+        const uint64_t *x = ct + b * csz_in;
+        int l = level;
+        memcpy(acc, x, sizeof(uint64_t) * csz_in);
+        poly_mul_int(acc, l + 1, P->log_n, P->mod, kmul);
+        poly_mul_int(acc + (uint64_t)(l + 1) * n, l + 1, P->log_n, P->mod, kmul);
+        orc_rescale(P, l, acc, nxt);
+        l--;
+        memcpy(acc, nxt, sizeof(uint64_t) * 2 * (l + 1) * n);
+        poly_add_int(acc, l + 1, P->log_n, P->mod, kadd[d - 1]);
+        for (int k = d - 2; k >= 0; k--) {
+            uint64_t lsz = (uint64_t)(l + 1) * n;
+            memcpy(xd, x, sizeof(uint64_t) * lsz);
+            memcpy(xd + lsz, x + (uint64_t)(level + 1) * n, sizeof(uint64_t) * lsz);
+            orc_mul_relin_rescale(P, l, acc, xd, rlk, nxt, 1, 0);
+            l--;
+            memcpy(acc, nxt, sizeof(uint64_t) * 2 * (l + 1) * n);
+            poly_add_int(acc, l + 1, P->log_n, P->mod, kadd[k]);
+        }
+        memcpy(out + (uint64_t)b * 2 * (l + 1) * n, acc, sizeof(uint64_t) * 2 * (l + 1) * n);
+    }
+    *out_scale = s_acc;
+    free(acc);
+    free(nxt);
+    free(xd);
     return 0;
 }
 

@@ -10,7 +10,9 @@ Checks against what the mathematics fixes, never against the oracle itself:
   * mul/relinearise/rescale decrypts to the slot-wise product;
   * the BSGS matvec equals the float64 map y_o[s] = sum_c sum_t
     D_{o,c,t}[s] * x_c[(s+t) mod n];
-  * rotate-and-sum over all power-of-two offsets gives the slot sum in every slot.
+  * rotate-and-sum over all power-of-two offsets gives the slot sum in every slot;
+  * Horner evaluation of p(x) = sum_k c_k x^k decrypts to p(z) slot-wise
+    (float64 reference) at a scale equal to the primes' size.
 """
 import numpy as np
 import pytest
@@ -209,3 +211,36 @@ def test_rotate_and_sum_gives_slot_sum(orc):
         ct = orc.rotate(P, level, ct, g, galois_key(orc, P, s_ntt, g, 8, "r%d" % k), flags=orc.ROT_ACCUMULATE)
     dec = orc.decrypt(P, level, ct, s_ntt, scale).real
     assert np.max(np.abs(dec - z.sum())) / np.sum(np.abs(z)) < 2 ** -20
+
+
+@pytest.mark.parametrize("coeffs", [
+    [1.0, 1.0, 0.5, 1 / 6, 1 / 24, 1 / 120, 1 / 720, 1 / 5040],   # exp, degree 7 Taylor
+    [0.25, -1.5],                                                  # affine
+    [0.0, 0.5, 0.0, -0.125, 0.0, 0.03],                            # odd, degree 5
+    [-1.75, 0.3, 1.9, -0.6],                                       # cubic, |c| up to 2
+], ids=["exp7", "affine", "odd5", "cubic"])
+def test_poly_eval_decrypts_to_polynomial(orc, coeffs):
+    P = config_params(orc, "C3", log_n=9)
+    level, h = 23, 64
+    s, s_ntt = secret(orc, P, 9, h)
+    rlk = relin_key(orc, P, s_ntt, 9)
+    z = S.uniform_slots(S.stream(9, "pe/z"), P.N // 2, complex_values=False)
+    scale = 2.0 ** 54
+    ct = encrypt_slots(orc, P, s_ntt, z, scale, level, 9, "pe/ct")
+    out, s_out = orc.poly_eval(P, level, ct[None], scale, coeffs, rlk)
+    d = len(coeffs) - 1
+    assert out.shape == (1, 2, level - d + 1, P.N)
+    dec = orc.decrypt(P, level - d, out[0], s_ntt, s_out)
+    ref = sum(c * z ** k for k, c in enumerate(coeffs))
+    assert np.max(np.abs(dec - ref)) < 2 ** -30
+
+
+def test_poly_eval_rejects_bad_input(orc):
+    P = config_params(orc, "C1")
+    s, s_ntt = secret(orc, P, 1, 64)
+    rlk = relin_key(orc, P, s_ntt, 1)
+    ct = S.uniform_limbs(S.stream(1, "pe/bad"), P.q, P.N, lead=(1, 2))
+    with pytest.raises(ValueError):
+        orc.poly_eval(P, 2, ct[:, :, :3], 2.0 ** 25, [1.0] * 5, rlk)  # degree 4 > level 2
+    with pytest.raises(ValueError):
+        orc.poly_eval(P, 3, ct, 2.0 ** 25, [0.0, 2.0 ** 40], rlk)     # c * q reaches 2^62
