@@ -201,6 +201,23 @@ int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch
 int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d_b, const uint64_t* d_rlk,
                            uint64_t* d_out, int batch, int level, unsigned flags, ckks_stream_t stream);
 
+/* Polynomial p(x) = sum_{k<=degree} coeffs[k] x^k (host doubles) on each of
+ * the batch ciphertexts d_ct_in ([batch][2][level+1][N], NTT form, scale
+ * `scale`), by Horner's rule (the polynomial approximations of the nonlinear
+ * layers, AEGIS page "Methodology" and the Nimbus post; no scheme is given):
+ *   acc = c_d * x         every limb times K = round(c_d * q_level), rescale
+ *                         (the scale stays `scale`)
+ *   acc += c_{d-1}        round(c_{d-1} * s_acc) added to c0 in NTT form
+ *   for k = d-2 .. 0      acc = rescale(relin(acc * x)) with x restricted to
+ *                         acc's limbs, s_acc = s_acc * scale / q_l (l the
+ *                         level of acc before the product); acc += c_k
+ * Rounding is llround; the constants must stay below 2^62 (CKKS_EINVAL).
+ * d_ct_out: [batch][2][level-degree+1][N]; *out_scale receives the output
+ * scale.  Needs 1 <= degree <= level and K > 0 (d_rlk: the s^2 -> s key).
+ * The scale should be close to the primes so the rescales keep it. */
+int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level, double scale, const double* coeffs,
+                   int degree, const uint64_t* d_rlk, uint64_t* d_ct_out, double* out_scale, ckks_stream_t stream);
+
 /* Baby-step / giant-step ciphertext x plaintext matrix-vector product.
  *   d_x      [n_in][2][level+1][N] input ciphertexts
  *   d_diags  [n_out][n_in][n2][n1][level+1][N] plaintexts (NTT form); entry

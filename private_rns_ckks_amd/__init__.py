@@ -31,7 +31,7 @@ EXPORTED = [
     "ckks_find_primes", "ckks_params_validate", "ckks_strerror", "ckks_last_error",
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
     "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_hoisted", "ckks_rescale",
-    "ckks_mul_relin_rescale", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
+    "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
 ]
 
 # Kernel whose launches take the largest share of a rotation batch (by
@@ -89,6 +89,8 @@ def _load():
         "ckks_rotate_hoisted": (i, [vp, vp, i, i, i, u32p, pp, vp, vp]),
         "ckks_rescale": (i, [vp, vp, vp, i, i, vp]),
         "ckks_mul_relin_rescale": (i, [vp, vp, vp, vp, vp, i, i, ctypes.c_uint, vp]),
+        "ckks_poly_eval": (i, [vp, vp, i, i, ctypes.c_double, ctypes.POINTER(ctypes.c_double), i, vp, vp,
+                               ctypes.POINTER(ctypes.c_double), vp]),
         "ckks_ptmatvec": (i, [vp, vp, i, vp, i, i, i, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
         "ckks_trace_begin": (i, [vp, ctypes.c_char_p]),
         "ckks_trace_end": (i, [vp, ctypes.POINTER(ckks_trace_stats)]),
@@ -231,6 +233,16 @@ def ckks_rescale(ctx, d_in, d_out, batch, level, stream=None):
 def ckks_mul_relin_rescale(ctx, d_a, d_b, d_rlk, d_out, batch, level, flags=0, stream=None):
     _check(_lib.ckks_mul_relin_rescale(ctx.handle, _ptr(d_a), _ptr(d_b), _ptr(d_rlk), _ptr(d_out), batch, level,
                                        flags, _stream(stream)), "ckks_mul_relin_rescale")
+
+
+def ckks_poly_eval(ctx, d_ct_in, batch, level, scale, coeffs, d_rlk, d_ct_out, stream=None):
+    """Horner evaluation of sum_k coeffs[k] x^k; returns the output scale."""
+    c = (ctypes.c_double * len(coeffs))(*[float(v) for v in coeffs])
+    out_scale = ctypes.c_double(0.0)
+    _check(_lib.ckks_poly_eval(ctx.handle, _ptr(d_ct_in), batch, level, float(scale), c, len(coeffs) - 1,
+                               _ptr(d_rlk), _ptr(d_ct_out), ctypes.byref(out_scale), _stream(stream)),
+           "ckks_poly_eval")
+    return out_scale.value
 
 
 def ckks_ptmatvec(ctx, d_x, n_in, d_diags, n_out, n1, n2, baby_galois, d_evk_baby, giant_galois, d_evk_giant, d_y,

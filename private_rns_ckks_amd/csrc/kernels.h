@@ -60,6 +60,21 @@ struct PtMacArgs {
   int level, n_in, n1, n2;
 };
 
+struct ConstMulArgs {
+  const uint64_t* in;  // [2][nl][N] per item
+  uint64_t* out;       // [2][nl][N] per item
+  uint64_t in_bstride, out_bstride;
+  const PrimeConst* prime;
+  uint64_t k[64][2];  // per limb: constant mod q_i and its Shoup quotient
+  int nl, log_n;
+};
+
+struct ConstAddArgs {
+  const PrimeConst* prime;
+  uint64_t v[64];  // per limb: constant mod q_i
+  int log_n;
+};
+
 struct KSItem {
   const uint64_t* d;       // NTT-form input polynomial [level+1][N]
   uint32_t g;              // automorphism applied to d before switching (0 = none)
@@ -102,6 +117,8 @@ int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
 int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
+int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
+int launch_add_const(Ctx* c, hipStream_t s, uint64_t* x, uint64_t bstride, int nl, ConstAddArgs& a, int batch);
 int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
                int ncomp, uint64_t bstride);
 

@@ -259,6 +259,26 @@ __global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, 
   out[off] = add_mod(x[off], y[off], prime[i].q);
 }
 
+// Every limb times a per-limb constant: out = in * k_i mod q_i (Shoup, with
+// the constant's quotient), both components; in and out [2][nl][N] per item.
+__global__ void const_mul_kernel(ConstMulArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y % a.nl;
+  const uint64_t q = a.prime[i].q;
+  const uint64_t off = ((uint64_t)blockIdx.y << a.log_n) + c;
+  const uint64_t v = a.in[blockIdx.z * a.in_bstride + off];
+  a.out[blockIdx.z * a.out_bstride + off] = reduce_4q(mul_shoup_lazy(v, a.k[i][0], a.k[i][1], q), q);
+}
+
+// The constant polynomial v_i (per limb) added to component 0 in place: in NTT
+// form a constant is that constant in every word.
+__global__ void add_const_kernel(uint64_t* x, uint64_t bstride, ConstAddArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y;
+  const uint64_t off = blockIdx.z * bstride + ((uint64_t)i << a.log_n) + c;
+  x[off] = add_mod(x[off], a.v[i], a.prime[i].q);
+}
+
 }  // namespace
 
 #define LAUNCH_CHECK() CKKS_HIP_CHECK(hipGetLastError())
@@ -339,6 +359,20 @@ int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint
   TraceScope ts(c, s, "add", 0);
   hipLaunchKernelGGL(add_kernel, dim3(c->N / 256, nl * ncomp, npoly), dim3(256), 0, s, x, y, out, bstride, nl,
                      c->d_prime, (int)c->log_n);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch) {
+  TraceScope ts(c, s, "const_mul", (double)batch * 2 * a.nl * c->N);
+  hipLaunchKernelGGL(const_mul_kernel, dim3(c->N / 256, 2 * a.nl, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_add_const(Ctx* c, hipStream_t s, uint64_t* x, uint64_t bstride, int nl, ConstAddArgs& a, int batch) {
+  TraceScope ts(c, s, "add", 0);
+  hipLaunchKernelGGL(add_const_kernel, dim3(c->N / 256, nl, batch), dim3(256), 0, s, x, bstride, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -1,13 +1,15 @@
 // Host orchestration of the hot path and the C ABI compute entry points.
 // The key-switch pipeline itself is in keyswitch.hip.  Batch items are
-// processed in chunks (CKKS_CHUNK, default 8, at most 8) so that one launch
-// covers several ciphertexts: enough workgroups to fill 256 CUs while the
-// chunk's intermediates stay within the 256 MiB last-level cache.
+// processed in chunks (CKKS_CHUNK, default 4) so that one launch covers
+// several ciphertexts, and consecutive chunks alternate between internal
+// streams (CKKS_LANES, default 2) so their kernels overlap.
+#include <math.h>
 #include <string.h>
 
 #include <algorithm>
 #include <vector>
 
+#include "host_math.h"
 #include "kernels.h"
 
 namespace ckks {
@@ -414,6 +416,95 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
                          chunk * std::max(ks, rs_per));
   }
   return join_lanes(ctx, stream, lanes, rc);
+}
+
+// round(x) for |x| < 2^62, the same rounding (llround) as the reference
+// evaluation; false when out of range.
+static bool round_checked(double x, int64_t* out) {
+  if (!(fabs(x) < 4611686018427387904.0)) return false;
+  *out = llround(x);
+  return true;
+}
+
+static uint64_t signed_mod(int64_t v, uint64_t m) {
+  if (v >= 0) return (uint64_t)v % m;
+  const uint64_t r = (uint64_t)(-(v + 1)) % m;  // -(v+1) >= 0 without overflow
+  return r == m - 1 ? 0 : m - 1 - r;
+}
+
+int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level, double scale, const double* coeffs,
+                   int degree, const uint64_t* d_rlk, uint64_t* d_ct_out, double* out_scale, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_ct_in || !d_ct_out || !d_rlk || !coeffs || !out_scale || batch < 0)
+    return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  if (misaligned(d_ct_in) || misaligned(d_ct_out) || misaligned(d_rlk))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (degree < 1 || degree > level) return set_error(CKKS_ERANGE, "degree must be 1..level");
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation needs special primes");
+  const int d = degree;
+  // constants and scales, in the order and arithmetic of the reference
+  int64_t kmul, kadd[64];
+  double s_acc = scale;
+  bool ok = round_checked(coeffs[d] * (double)ctx->mod[level], &kmul);
+  ok = ok && round_checked(coeffs[d - 1] * s_acc, &kadd[d - 1]);
+  for (int k = d - 2, l = level - 1; k >= 0; --k, --l) {
+    s_acc = s_acc * scale / (double)ctx->mod[l];
+    ok = ok && round_checked(coeffs[k] * s_acc, &kadd[k]);
+  }
+  if (!ok) return set_error(CKKS_EINVAL, "a rounded polynomial constant reaches 2^62");
+  *out_scale = s_acc;
+  if (batch == 0) return CKKS_OK;
+  const uint32_t N = ctx->N;
+  const uint64_t in_ct = 2ull * (level + 1) * N, ct_l = 2ull * level * N;
+  // operand buffers: the constant product at level `level`, two accumulators
+  // and the input restricted to the accumulator's limbs (level - 1 and below)
+  if ((rc = ensure_aux(ctx, batch * (in_ct + 3 * ct_l)))) return rc;
+  uint64_t* T = ctx->aux;
+  uint64_t* acc[2] = {T + batch * in_ct, T + batch * in_ct + batch * ct_l};
+  uint64_t* X = acc[1] + batch * ct_l;
+  auto add_const = [&](uint64_t* ct, int lvl, int64_t v) {
+    ConstAddArgs ca;
+    ca.prime = ctx->d_prime;
+    ca.log_n = (int)ctx->log_n;
+    for (int i = 0; i <= lvl; ++i) ca.v[i] = signed_mod(v, ctx->mod[i]);
+    return launch_add_const(ctx, stream, ct, 2ull * (lvl + 1) * N, lvl + 1, ca, batch);
+  };
+  // acc = c_d * x: times round(c_d * q_l) on every limb, then rescale
+  {
+    ConstMulArgs cm;
+    cm.in = d_ct_in;
+    cm.out = T;
+    cm.in_bstride = in_ct;
+    cm.out_bstride = in_ct;
+    cm.prime = ctx->d_prime;
+    cm.nl = level + 1;
+    cm.log_n = (int)ctx->log_n;
+    for (int i = 0; i <= level; ++i) {
+      cm.k[i][0] = signed_mod(kmul, ctx->mod[i]);
+      cm.k[i][1] = host::shoup(cm.k[i][0], ctx->mod[i]);
+    }
+    if ((rc = launch_const_mul(ctx, stream, cm, batch))) return rc;
+  }
+  uint64_t* dst = d == 1 ? d_ct_out : acc[0];
+  const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
+  if ((rc = ensure_workspace(ctx, rs_per * std::min(batch, kMaxChunk)))) return rc;
+  if ((rc = rescale_batch(ctx, stream, T, in_ct, dst, ct_l, batch, level, ctx->ws, ctx->ws_words))) return rc;
+  int l = level - 1;
+  if ((rc = add_const(dst, l, kadd[d - 1]))) return rc;
+  // Horner steps: acc = rescale(relin(acc * x)) + c_k
+  for (int k = d - 2, cur = 0; k >= 0; --k, cur ^= 1) {
+    const uint64_t lsz = (uint64_t)(l + 1) * N;
+    // x restricted to limbs 0..l of each component
+    CKKS_HIP_CHECK(hipMemcpy2DAsync(X, lsz * 8, d_ct_in, (uint64_t)(level + 1) * N * 8, lsz * 8, 2ull * batch,
+                                    hipMemcpyDeviceToDevice, stream));
+    uint64_t* next = k == 0 ? d_ct_out : acc[cur ^ 1];
+    if ((rc = ckks_mul_relin_rescale(ctx, acc[cur], X, d_rlk, next, batch, l, 0, stream))) return rc;
+    --l;
+    if ((rc = add_const(next, l, kadd[k]))) return rc;
+  }
+  return CKKS_OK;
 }
 
 int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,

@@ -277,6 +277,50 @@ def test_rotate_errors(lib, orc, c3small):
         assert e.value.code == lib.CKKS_EINVAL
 
 
+# ---------------------------------------------------------------- polynomial evaluation
+
+@pytest.mark.parametrize("coeffs,level", [
+    ([1.0, 1.0, 0.5, 1 / 6, 1 / 24, 1 / 120, 1 / 720, 1 / 5040], 23),
+    ([-1.75, 0.3, 1.9, -0.6], 9),
+    ([0.25, -1.5], 4),
+    ([0.1, 0.0, 2.5], 3),
+], ids=["exp7_l23", "cubic_l9", "affine_l4", "quad_l3"])
+def test_poly_eval_parity(lib, orc, c3small, coeffs, level):
+    """Horner evaluation on 3 ciphertexts; item 0 a real encryption at scale
+    2^54 that decrypts to the polynomial of its slots."""
+    from helpers import encrypt_slots, relin_key, secret
+
+    ctx, P = c3small
+    d = len(coeffs) - 1
+    announce("poly_eval degree=%d level=%d" % (d, level))
+    s, s_ntt = secret(orc, P, 11, 192)
+    rlk = relin_key(orc, P, s_ntt, 11, tag="gpu/pe/rlk")
+    scale = 2.0 ** 54
+    cts = S.uniform_limbs(S.stream(level, "gpu/pe/ct"), P.q[: level + 1], P.N, lead=(3, 2))
+    z = S.uniform_slots(S.stream(level, "gpu/pe/z"), P.N // 2, complex_values=False)
+    cts[0] = encrypt_slots(orc, P, s_ntt, z, scale, level, 11, "gpu/pe/enc")
+    out = empty_dev((3, 2, level - d + 1, P.N))
+    s_out = lib.ckks_poly_eval(ctx, to_dev(cts), 3, level, scale, coeffs, to_dev(rlk), out)
+    got = to_host(out)
+    ref, ref_scale = orc.poly_eval(P, level, cts, scale, coeffs, rlk)
+    assert s_out == ref_scale
+    assert np.array_equal(got, ref)
+    dec = orc.decrypt(P, level - d, got[0], s_ntt, s_out).real
+    assert np.max(np.abs(dec - sum(c * z ** k for k, c in enumerate(coeffs)))) < 2 ** -30
+
+
+def test_poly_eval_errors(lib, orc, c3small):
+    ctx, P = c3small
+    x = empty_dev((1, 2, 3, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    y = empty_dev((1, 2, 3, P.N))
+    for level, coeffs, code in [(2, [1.0] * 4, lib.CKKS_ERANGE), (2, [1.0], lib.CKKS_ERANGE),
+                                (2, [0.0, 2.0 ** 40], lib.CKKS_EINVAL)]:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_poly_eval(ctx, x, 1, level, 2.0 ** 54, coeffs, k, y)
+        assert e.value.code == code
+
+
 # ---------------------------------------------------------------- rescale, multiply
 
 @pytest.mark.parametrize("level", [23, 1])
