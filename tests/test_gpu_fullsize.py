@@ -6,6 +6,8 @@ C3: the 32-ciphertext rotation batch (N=2^16, L=24, K=8, dnum=3), with item 0
 C5: 48 ciphertext pairs: multiply + relinearise + rescale, then rotate-and-sum
     over the 15 power-of-two offsets, with pair 0 real (decrypt = slot sum).
 C4: the BSGS matvec at level 12 with 12 x 3 x 8 x 8 diagonals (15.7 GB).
+Polynomial evaluation: degree 7 on the 48 ciphertexts of a C5 batch at level
+    23 (scale 2^54), with item 0 a real encryption (decrypts to p(slots)).
 """
 import numpy as np
 import pytest
@@ -127,3 +129,25 @@ def test_c4_full_ptmatvec(lib, orc, full):
         assert (got[:, :, t, :] < m).all()
     ref = orc.ptmatvec(P, level, x, diag0[None], gb, kb, gg, kg)
     assert np.array_equal(got[0], ref[0])
+
+
+def test_poly_eval_full(lib, orc, full):
+    ctx, P = full
+    B, level, scale = 48, P.L - 1, 2.0 ** 54
+    coeffs = [1.0, 1.0, 0.5, 1 / 6, 1 / 24, 1 / 120, 1 / 720, 1 / 5040]
+    d = len(coeffs) - 1
+    announce("poly_eval full: degree %d on %d ciphertexts at N=2^16" % (d, B))
+    s, s_ntt = secret(orc, P, 12, 192)
+    rlk = relin_key(orc, P, s_ntt, 12, tag="full/pe/rlk")
+    cts = S.uniform_limbs(S.stream(12, "full/pe/ct"), P.q, P.N, lead=(B, 2))
+    z = S.uniform_slots(S.stream(12, "full/pe/z"), P.N // 2, complex_values=False)
+    cts[0] = encrypt_slots(orc, P, s_ntt, z, scale, level, 12, "full/pe/enc")
+    out = empty_dev((B, 2, level - d + 1, P.N))
+    s_out = lib.ckks_poly_eval(ctx, to_dev(cts), B, level, scale, coeffs, to_dev(rlk), out)
+    got = to_host(out)
+    for b in (0, B - 1):
+        ref, ref_scale = orc.poly_eval(P, level, cts[b:b + 1], scale, coeffs, rlk)
+        assert s_out == ref_scale
+        assert np.array_equal(got[b], ref[0]), b
+    dec = orc.decrypt(P, level - d, got[0], s_ntt, s_out).real
+    assert np.max(np.abs(dec - sum(c * z ** k for k, c in enumerate(coeffs)))) < 2 ** -30
