@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libckks_mi355x.so")
-SOURCES = ["ctx.hip", "ntt.hip", "kernels.hip", "keyswitch.hip", "ops.hip"]
+SOURCES = ["ctx.hip", "ntt.hip", "kernels.hip", "keyswitch.hip", "rescale.hip", "ops.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

@@ -30,18 +30,6 @@ struct ModDownArgs {
   int level, next, L, K;
 };
 
-struct RescaleArgs {
-  const uint64_t* ct;  // [2][level+1][N] per item
-  const uint64_t* v;   // [2][N] per item: iNTT of limb `level`
-  uint64_t* w;         // [2][level][N] per item
-  uint64_t* out;       // [2][level][N] per item
-  uint64_t ct_bstride, v_bstride, w_bstride, out_bstride;
-  const uint64_t* tab;  // rescale constants [L][L][4]
-  const PrimeConst* prime;
-  uint32_t n;
-  int level, L;
-};
-
 struct TensorArgs {
   const uint64_t *a, *b;  // [2][level+1][N] per item
   uint64_t* out;          // [3][level+1][N] per item
@@ -113,10 +101,12 @@ int launch_automorph_coeff(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* 
                            uint64_t pstride, uint32_t ginv);
 int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch);
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch);
-int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
-int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch);
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
+// Rescale of `batch` items by limb `level`: v = iNTT of that limb per item
+// and component ([2][N], canonical), w scratch [2][level][N], out [2][level][N].
+int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
+                  uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level);
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
 int launch_add_const(Ctx* c, hipStream_t s, uint64_t* x, uint64_t bstride, int nl, ConstAddArgs& a, int batch);
 int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,

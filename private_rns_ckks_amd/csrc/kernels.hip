@@ -147,38 +147,6 @@ __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   }
 }
 
-// Rescale, step 1: v = iNTT(c[l]) (canonical, 1/N applied) for both components;
-// w_i = (vbar mod q_i) * [q_l^-1]_{q_i}, vbar the centered lift of v.
-__global__ __launch_bounds__(256) void rescale_prep_kernel(RescaleArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int comp = blockIdx.y;
-  const uint64_t v = a.v[blockIdx.z * a.v_bstride + (uint64_t)comp * a.n + c];
-  const uint64_t ql = a.prime[a.level].q;
-  const bool neg = v > (ql - 1) / 2;
-  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * a.level * a.n + c;
-  for (int i = 0; i < a.level; ++i) {
-    const PrimeConst pc = a.prime[i];
-    const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
-    uint64_t t = v >= pc.q ? reduce64(v, pc.q, pc.inv1) : v;
-    if (neg) t = sub_mod(t, rs[2], pc.q);
-    w[(uint64_t)i * a.n] = reduce_2q(mul_shoup(t, rs[0], rs[1], pc.q), pc.q);
-  }
-}
-
-// Rescale, step 2: out_i = c_i * [q_l^-1]_{q_i} - NTT(w)_i.
-__global__ __launch_bounds__(256) void rescale_combine_kernel(RescaleArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int i = blockIdx.y;
-  const PrimeConst pc = a.prime[i];
-  const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
-  for (int comp = 0; comp < 2; ++comp) {
-    const uint64_t cv = a.ct[blockIdx.z * a.ct_bstride + ((uint64_t)comp * (a.level + 1) + i) * a.n + c];
-    const uint64_t wv = a.w[blockIdx.z * a.w_bstride + ((uint64_t)comp * a.level + i) * a.n + c];
-    a.out[blockIdx.z * a.out_bstride + ((uint64_t)comp * a.level + i) * a.n + c] =
-        sub_mod(reduce_2q(mul_shoup(cv, rs[0], rs[1], pc.q), pc.q), wv, pc.q);
-  }
-}
-
 // d0 = a0 b0, d1 = a0 b1 + a1 b0, d2 = a1 b1 on limb blockIdx.y.
 __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -322,20 +290,6 @@ int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
     hipLaunchKernelGGL(moddown_conv_kernel<8>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(moddown_conv_kernel<16>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
-  LAUNCH_CHECK();
-  return CKKS_OK;
-}
-
-int launch_rescale_prep(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
-  TraceScope ts(c, s, "rescale", (double)batch * 2 * a.level * c->N);
-  hipLaunchKernelGGL(rescale_prep_kernel, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
-  LAUNCH_CHECK();
-  return CKKS_OK;
-}
-
-int launch_rescale_combine(Ctx* c, hipStream_t s, RescaleArgs& a, int batch) {
-  TraceScope ts(c, s, "rescale", (double)batch * 2 * a.level * c->N);
-  hipLaunchKernelGGL(rescale_combine_kernel, dim3(c->N / 256, a.level, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -66,27 +66,10 @@ int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride,
     for (int comp = 0; comp < 2; ++comp) jobs.add(comp * (level + 1) + level, comp, level);
     int rc = ntt_run(c, s, in + b0 * in_stride, V, in_stride, per, n, jobs, true, true);
     if (rc) return rc;
-    RescaleArgs ra;
-    memset(&ra, 0, sizeof(ra));
-    ra.ct = in + b0 * in_stride;
-    ra.v = V;
-    ra.w = W;
-    ra.out = out + b0 * out_stride;
-    ra.ct_bstride = in_stride;
-    ra.v_bstride = per;
-    ra.w_bstride = per;
-    ra.out_bstride = out_stride;
-    ra.tab = c->d_rescale;
-    ra.prime = c->d_prime;
-    ra.n = N;
-    ra.level = level;
-    ra.L = (int)c->L;
-    if ((rc = launch_rescale_prep(c, s, ra, n))) return rc;
-    jobs.n = 0;
-    for (int comp = 0; comp < 2; ++comp)
-      for (int i = 0; i < level; ++i) jobs.add(comp * level + i, comp * level + i, i);
-    if ((rc = ntt_run(c, s, W, W, per, per, n, jobs, false, false))) return rc;
-    if ((rc = launch_rescale_combine(c, s, ra, n))) return rc;
+    // conversion and final combination fused into the forward NTT of w
+    if ((rc = rescale_fused(c, s, in + b0 * in_stride, in_stride, V, per, W, per, out + b0 * out_stride, out_stride, n,
+                            level)))
+      return rc;
   }
   return CKKS_OK;
 }
