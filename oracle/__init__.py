@@ -95,6 +95,9 @@ def lib():
             "orc_mul_relin_rescale": (c_int, [pp, c_int, u64p, u64p, u64p, u64p, c_int, ctypes.c_uint]),
             "orc_ptmatvec": (c_int, [pp, c_int, u64p, c_int, u64p, c_int, c_int, c_int, u32p, ctypes.POINTER(u64p),
                                      u32p, ctypes.POINTER(u64p), u64p, ctypes.c_uint, c_int, c_int]),
+            "orc_ctmatvec": (c_int, [pp, c_int, u64p, c_int, u64p, c_int, c_int, c_int, u64p, u32p,
+                                     ctypes.POINTER(u64p), u32p, ctypes.POINTER(u64p), u64p, ctypes.c_uint, c_int,
+                                     c_int]),
             "orc_secret_ntt": (None, [pp, i8p, u64p]),
             "orc_make_switch_key": (None, [pp, u64p, u64p, u64p, i64p, u64p]),
             "orc_encrypt": (None, [pp, c_int, u64p, u64p, u64p, i64p, u64p]),
@@ -369,6 +372,30 @@ def ptmatvec(P: Params, level: int, x, diags, g_baby, evk_baby, g_giant, evk_gia
     a, b = o_range if o_range is not None else (0, n_out)
     u32p = ctypes.POINTER(ctypes.c_uint32)
     rc = lib().orc_ptmatvec(P.ref(), level, _u64(x), n_in, _u64(diags), n_out, n1, n2,
+                            gb.ctypes.data_as(u32p), _ptr_array(eb), gg.ctypes.data_as(u32p), _ptr_array(eg),
+                            _u64(y), flags, a, b)
+    if rc != 0:
+        raise ValueError("rescale at level 0")
+    return y
+
+
+def ctmatvec(P: Params, level: int, x, diags, rlk, g_baby, evk_baby, g_giant, evk_giant, flags: int = 0,
+             o_range=None):
+    """BSGS matvec with encrypted weights (the A x V product of attention);
+    diags: [n_out][n_in][n2][n1][2][l+1][N] ciphertexts, rlk the s^2 -> s key.
+    Tensor products of a giant-step group are summed and relinearised once.
+    Returns y [n_out][2][l or l+1][N]; o_range as in ptmatvec."""
+    x, diags, rlk = _arr(x), _arr(diags), _arr(rlk)
+    n_out, n_in, n2, n1 = diags.shape[:4]
+    lo = level + 1 if flags & NO_RESCALE else level
+    y = np.zeros((n_out, 2, lo, P.N), dtype=np.uint64)
+    gb = np.ascontiguousarray(np.asarray(list(g_baby) + [0], dtype=np.uint32))
+    gg = np.ascontiguousarray(np.asarray(list(g_giant) + [0], dtype=np.uint32))
+    eb = [_arr(e) for e in evk_baby] or [np.zeros(1, dtype=np.uint64)]
+    eg = [_arr(e) for e in evk_giant] or [np.zeros(1, dtype=np.uint64)]
+    a, b = o_range if o_range is not None else (0, n_out)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    rc = lib().orc_ctmatvec(P.ref(), level, _u64(x), n_in, _u64(diags), n_out, n1, n2, _u64(rlk),
                             gb.ctypes.data_as(u32p), _ptr_array(eb), gg.ctypes.data_as(u32p), _ptr_array(eg),
                             _u64(y), flags, a, b)
     if rc != 0:

@@ -2,8 +2,9 @@
  * ckks_oracle.c -- plain CPU reference ("oracle") for the RNS-CKKS rotation
  * hot path: negacyclic NTT, Galois automorphism, hybrid key switching
  * (ModUp, inner product with dnum key digits, ModDown), rotation, rescale,
- * ciphertext-ciphertext multiply with relinearisation, and the baby-step /
- * giant-step plaintext matrix-vector product.
+ * ciphertext-ciphertext multiply with relinearisation, the baby-step /
+ * giant-step matrix-vector product with plaintext or encrypted weights, and
+ * polynomial evaluation.
  *
  * THIS IS TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load it.  It shares no code, header,
@@ -742,6 +743,73 @@ int orc_ptmatvec(const orc_params *P, int level, const uint64_t *x, int n_in, co
     free(inner);
     free(acc);
     free(tmp);
+    free(rot);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Baby-step / giant-step matrix-vector product with encrypted weights   */
+/* ------------------------------------------------------------------ */
+
+/* The attention output A x V of the AEGIS summary ("Methodology",
+ * self-attention: the softmax weights are gathered, then multiplied with V)
+ * has both operands encrypted; the pages give no packing.  Reading: the
+ * diagonal method of ptmatvec with ciphertext diagonals, the tensor products
+ * of one giant-step group summed before a single relinearisation (the sum of
+ * tensor products is again a three-part ciphertext under 1, s, s^2):
+ *   baby_{c,b}  = Rot_b(x_c)                       (hoisted, as in ptmatvec)
+ *   T_{o,g}     = sum_c sum_b tensor(diag_{o,c,g,b}, baby_{c,b})
+ *   R_{o,g}     = (T0 + k0, T1 + k1),  (k0, k1) = KS_{s^2 -> s}(T2)
+ *   y_o         = sum_g Rot_g(R_{o,g})             (g = 0: no rotation)
+ * then rescale unless ORC_NO_RESCALE.  diags: [n_out][n_in][n2][n1][2][l+1][N]
+ * ciphertexts (entry (o,c,g,b) already rotated by the inverse giant step);
+ * rlk: the key for s^2.  Only outputs o in [o_begin, o_end) are computed. */
+int orc_ctmatvec(const orc_params *P, int level, const uint64_t *x, int n_in, const uint64_t *diags, int n_out,
+                 int n1, int n2, const uint64_t *rlk, const uint32_t *g_baby, const uint64_t *const *evk_baby,
+                 const uint32_t *g_giant, const uint64_t *const *evk_giant, uint64_t *y, unsigned flags,
+                 int o_begin, int o_end)
+{
+    uint64_t n = (uint64_t)1 << P->log_n;
+    int nq = level + 1;
+    uint64_t sz = (uint64_t)nq * n, csz = 2 * sz;
+    if (!(flags & ORC_NO_RESCALE) && level < 1) return -2;
+    uint64_t *baby = malloc(sizeof(uint64_t) * csz * n_in * n1);
+    for (int c = 0; c < n_in; c++) {
+        memcpy(baby + (uint64_t)(c * n1) * csz, x + (uint64_t)c * csz, sizeof(uint64_t) * csz);
+        if (n1 > 1)
+            orc_rotate_hoisted(P, level, x + (uint64_t)c * csz, n1 - 1, g_baby, evk_baby,
+                               baby + (uint64_t)(c * n1 + 1) * csz);
+    }
+    uint64_t *t = malloc(sizeof(uint64_t) * 3 * sz), *prod = malloc(sizeof(uint64_t) * 3 * sz);
+    uint64_t *rel = malloc(sizeof(uint64_t) * csz), *acc = malloc(sizeof(uint64_t) * csz);
+    uint64_t *rot = malloc(sizeof(uint64_t) * csz);
+    for (int o = o_begin; o < o_end; o++) {
+        memset(acc, 0, sizeof(uint64_t) * csz);
+        for (int g = 0; g < n2; g++) {
+            memset(t, 0, sizeof(uint64_t) * 3 * sz);
+            for (int c = 0; c < n_in; c++)
+                for (int b = 0; b < n1; b++) {
+                    const uint64_t *d = diags + ((((uint64_t)o * n_in + c) * n2 + g) * n1 + b) * csz;
+                    orc_tensor(P, level, d, baby + (uint64_t)(c * n1 + b) * csz, prod);
+                    for (int k = 0; k < 3; k++)
+                        orc_poly_add(t + k * sz, prod + k * sz, t + k * sz, nq, P->log_n, P->mod);
+                }
+            orc_keyswitch(P, level, t + 2 * sz, rlk, rel);
+            orc_poly_add(t, rel, rel, nq, P->log_n, P->mod);
+            orc_poly_add(t + sz, rel + sz, rel + sz, nq, P->log_n, P->mod);
+            if (g == 0) memcpy(rot, rel, sizeof(uint64_t) * csz);
+            else orc_rotate(P, level, rel, g_giant[g - 1], evk_giant[g - 1], rot, 0);
+            orc_poly_add(acc, rot, acc, nq, P->log_n, P->mod);
+            orc_poly_add(acc + sz, rot + sz, acc + sz, nq, P->log_n, P->mod);
+        }
+        if (flags & ORC_NO_RESCALE) memcpy(y + (uint64_t)o * csz, acc, sizeof(uint64_t) * csz);
+        else orc_rescale(P, level, acc, y + (uint64_t)o * 2 * level * n);
+    }
+    free(baby);
+    free(t);
+    free(prod);
+    free(rel);
+    free(acc);
     free(rot);
     return 0;
 }

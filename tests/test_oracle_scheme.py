@@ -9,7 +9,9 @@ Checks against what the mathematics fixes, never against the oracle itself:
     accumulate = ct + Rot;
   * mul/relinearise/rescale decrypts to the slot-wise product;
   * the BSGS matvec equals the float64 map y_o[s] = sum_c sum_t
-    D_{o,c,t}[s] * x_c[(s+t) mod n];
+    D_{o,c,t}[s] * x_c[(s+t) mod n], with plaintext and with encrypted
+    diagonals; with trivially encrypted diagonals (c1 = 0) the encrypted-
+    weight matvec gives the plaintext matvec's words exactly;
   * rotate-and-sum over all power-of-two offsets gives the slot sum in every slot;
   * Horner evaluation of p(x) = sum_k c_k x^k decrypts to p(z) slot-wise
     (float64 reference) at a scale equal to the primes' size.
@@ -196,6 +198,81 @@ def test_ptmatvec_matches_float_map(orc):
     # sampling a sub-range gives the same words
     y1 = orc.ptmatvec(P, level, x, diags, gb, kb, gg, kg, o_range=(1, 2))
     assert np.array_equal(y1[1], y[1])
+
+
+def _bsgs_setup(orc, seed, level, n_in, n_out, n1, n2):
+    P = config_params(orc, "C4", log_n=10)
+    n = P.N // 2
+    s, s_ntt = secret(orc, P, seed, 64)
+    scale = 2.0 ** 40
+    rng = S.stream(seed, "bsgs/x")
+    xs = [S.uniform_slots(rng, n, complex_values=False) for _ in range(n_in)]
+    x = np.stack([encrypt_slots(orc, P, s_ntt, xs[c], scale, level, seed, "x%d" % c) for c in range(n_in)])
+    D = S.normal_values(S.stream(seed, "bsgs/D"), (n_out, n_in, n1 * n2, n), 0.02)
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [galois_key(orc, P, s_ntt, g, seed, "kb%d" % i) for i, g in enumerate(gb)]
+    kg = [galois_key(orc, P, s_ntt, g, seed, "kg%d" % i) for i, g in enumerate(gg)]
+    return P, s_ntt, scale, xs, x, D, gb, gg, kb, kg
+
+
+def _float_map(D, xs, o, n1, n2):
+    ref = np.zeros(D.shape[-1])
+    for c in range(len(xs)):
+        for t in range(n1 * n2):
+            ref += D[o, c, t] * np.roll(xs[c].real, -t)
+    return ref
+
+
+def test_ctmatvec_matches_float_map(orc):
+    """Encrypted diagonals (each encrypted separately, pre-rotated by the
+    inverse giant step): decrypts to the same float64 map as the plaintext
+    matvec, at scale^2 before the rescale."""
+    level, n_in, n_out, n1, n2 = 12, 2, 2, 4, 3
+    P, s_ntt, scale, xs, x, D, gb, gg, kb, kg = _bsgs_setup(orc, 11, level, n_in, n_out, n1, n2)
+    diags = np.empty((n_out, n_in, n2, n1, 2, level + 1, P.N), dtype=np.uint64)
+    for o in range(n_out):
+        for c in range(n_in):
+            for g in range(n2):
+                for b in range(n1):
+                    pre = np.roll(D[o, c, n1 * g + b], n1 * g)  # Rot_{-n1 g}
+                    diags[o, c, g, b] = encrypt_slots(orc, P, s_ntt, pre, scale, level, 11, "d%d.%d.%d.%d" % (o, c, g, b))
+    rlk = relin_key(orc, P, s_ntt, 11)
+    y_pre = orc.ctmatvec(P, level, x, diags, rlk, gb, kb, gg, kg, flags=orc.NO_RESCALE)
+    y = orc.ctmatvec(P, level, x, diags, rlk, gb, kb, gg, kg)
+    for o in range(n_out):
+        ref = _float_map(D, xs, o, n1, n2)
+        assert rel_err(orc.decrypt(P, level, y_pre[o], s_ntt, scale * scale).real, ref) < 2 ** -20
+        assert np.array_equal(y[o], orc.rescale(P, level, y_pre[o]))
+        assert rel_err(orc.decrypt(P, level - 1, y[o], s_ntt, scale * scale / P.q[level]).real, ref) < 2 ** -10
+    y1 = orc.ctmatvec(P, level, x, diags, rlk, gb, kb, gg, kg, o_range=(1, 2))
+    assert np.array_equal(y1[1], y[1])
+
+
+def test_ctmatvec_trivial_diagonals_give_ptmatvec_words(orc):
+    """A diagonal encrypted trivially, (pt, 0), makes every d2 zero, and the
+    key switch of zero is zero: the result must be the plaintext matvec's
+    words, bit for bit."""
+    level, n_in, n_out, n1, n2 = 6, 2, 2, 3, 2
+    P = config_params(orc, "C4", log_n=9)
+    rng = S.stream(12, "bsgs/triv")
+    x = S.uniform_limbs(rng, P.q[: level + 1], P.N, lead=(n_in, 2))
+    pts = S.uniform_limbs(rng, P.q[: level + 1], P.N, lead=(n_out, n_in, n2, n1))
+    ct_diags = np.zeros((n_out, n_in, n2, n1, 2, level + 1, P.N), dtype=np.uint64)
+    ct_diags[:, :, :, :, 0] = pts
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [S.uniform_limbs(S.stream(i, "bsgs/triv/kb"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n1 - 1)]
+    kg = [S.uniform_limbs(S.stream(i, "bsgs/triv/kg"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n2 - 1)]
+    rlk = S.uniform_limbs(S.stream(12, "bsgs/triv/rlk"), P.mods, P.N, lead=(P.dnum, 2))
+    for flags in (0, orc.NO_RESCALE):
+        a = orc.ctmatvec(P, level, x, ct_diags, rlk, gb, kb, gg, kg, flags=flags)
+        b = orc.ptmatvec(P, level, x, pts, gb, kb, gg, kg, flags=flags)
+        assert np.array_equal(a, b)
+    # a nonzero c1 must change the words (the d2 path is live)
+    ct_diags[0, 0, 0, 0, 1] = pts[0, 0, 0, 1]
+    a = orc.ctmatvec(P, level, x, ct_diags, rlk, gb, kb, gg, kg)
+    assert not np.array_equal(a[0], orc.ptmatvec(P, level, x, pts, gb, kb, gg, kg)[0])
 
 
 def test_rotate_and_sum_gives_slot_sum(orc):
