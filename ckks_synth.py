@@ -95,4 +95,8 @@ CONFIGS = {
     # Attention-shaped batch: 48 ct x ct products, relinearise, rescale, rotate-and-sum over 15 offsets.
     "C5": dict(log_n=16, L=24, q_bits=54, K=8, p_bits=60, dnum=3, h=192, sigma=3.2, scale=2.0 ** 40,
                batch=48, tokens=2048, hidden=768, rotsum_steps=15),
+    # Attention output A x V with encrypted weights: V as 3 ciphertexts (128 tokens x 768 hidden),
+    # 3 outputs, 64 ciphertext diagonals per (output, input) block, BSGS 8 x 8 at level 12.
+    "AV": dict(log_n=16, L=24, q_bits=54, K=8, p_bits=60, dnum=3, h=192, sigma=3.2, scale=2.0 ** 40,
+               level=12, n_in=3, n_out=3, n1=8, n2=8, tokens=128, hidden=768),
 }

@@ -130,7 +130,8 @@ typedef struct {
  * passes "intt_row_gather" (automorphism gather + inverse row pass),
  * "ntt_row_ip" (forward row pass + key inner product) and "ntt_row_combine"
  * (forward row pass + final combination), "automorph", "modup",
- * "moddown_conv", "rescale", "tensor", "ptmac", "add".  NULL or "" stops
+ * "moddown_conv", "rescale", "tensor", "ptmac", "ctmac", "add",
+ * "const_mul", "ip_gather".  NULL or "" stops
  * tracing.
  * Tracing adds two event records per traced launch and nothing else. */
 int ckks_trace_begin(ckks_ctx* ctx, const char* kernel);
@@ -235,6 +236,26 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
                   const uint32_t* baby_galois, const uint64_t* const* d_evk_baby, const uint32_t* giant_galois,
                   const uint64_t* const* d_evk_giant, uint64_t* d_y, int level, unsigned flags,
                   ckks_stream_t stream);
+
+/* Baby-step / giant-step matrix-vector product with encrypted weights: the
+ * attention output A x V, where the softmax weights A arrive encrypted
+ * (AEGIS page, "Methodology", self-attention: the weights are gathered and
+ * multiplied with V; no packing is given, so this is the diagonal method of
+ * ckks_ptmatvec with ciphertext diagonals).
+ *   d_x      [n_in][2][level+1][N] input ciphertexts (V)
+ *   d_diags  [n_out][n_in][n2][n1][2][level+1][N] ciphertexts (A's
+ *            diagonals); entry (o, c, g, b) is the diagonal for offset
+ *            n1*g + b, already rotated by the inverse of giant step g
+ *   d_rlk    [dnum][2][L+K][N] switching key for s^2
+ *   baby / giant  Galois elements and keys as in ckks_ptmatvec
+ *   d_y      [n_out][2][level][N] (level+1 with CKKS_NO_RESCALE)
+ * T_og = sum_c sum_b tensor(diag(o,c,g,b), Rot_b(x_c)) (three parts, summed
+ * before one relinearisation per (o, g)); y_o = sum_g Rot_g(relin(T_og)),
+ * then rescale.  Buffers and errors as in ckks_ptmatvec; K > 0. */
+int ckks_ctmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
+                  const uint64_t* d_rlk, const uint32_t* baby_galois, const uint64_t* const* d_evk_baby,
+                  const uint32_t* giant_galois, const uint64_t* const* d_evk_giant, uint64_t* d_y, int level,
+                  unsigned flags, ckks_stream_t stream);
 
 #ifdef __cplusplus
 }

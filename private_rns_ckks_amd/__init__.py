@@ -31,7 +31,8 @@ EXPORTED = [
     "ckks_find_primes", "ckks_params_validate", "ckks_strerror", "ckks_last_error",
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
     "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_hoisted", "ckks_rescale",
-    "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_ptmatvec", "ckks_trace_begin", "ckks_trace_end",
+    "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_ptmatvec", "ckks_ctmatvec", "ckks_trace_begin",
+    "ckks_trace_end",
 ]
 
 # Kernel whose launches take the largest share of a rotation batch (by
@@ -92,6 +93,7 @@ def _load():
         "ckks_poly_eval": (i, [vp, vp, i, i, ctypes.c_double, ctypes.POINTER(ctypes.c_double), i, vp, vp,
                                ctypes.POINTER(ctypes.c_double), vp]),
         "ckks_ptmatvec": (i, [vp, vp, i, vp, i, i, i, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
+        "ckks_ctmatvec": (i, [vp, vp, i, vp, i, i, i, vp, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
         "ckks_trace_begin": (i, [vp, ctypes.c_char_p]),
         "ckks_trace_end": (i, [vp, ctypes.POINTER(ckks_trace_stats)]),
     }
@@ -252,6 +254,16 @@ def ckks_ptmatvec(ctx, d_x, n_in, d_diags, n_out, n1, n2, baby_galois, d_evk_bab
     _check(_lib.ckks_ptmatvec(ctx.handle, _ptr(d_x), n_in, _ptr(d_diags), n_out, n1, n2, gb, _ptr_list(d_evk_baby),
                               gg, _ptr_list(d_evk_giant), _ptr(d_y), level, flags, _stream(stream)),
            "ckks_ptmatvec")
+
+
+def ckks_ctmatvec(ctx, d_x, n_in, d_diags, n_out, n1, n2, d_rlk, baby_galois, d_evk_baby, giant_galois, d_evk_giant,
+                  d_y, level, flags=0, stream=None):
+    gb = (ctypes.c_uint32 * max(1, n1 - 1))(*[int(v) for v in baby_galois])
+    gg = (ctypes.c_uint32 * max(1, n2 - 1))(*[int(v) for v in giant_galois])
+    _check(_lib.ckks_ctmatvec(ctx.handle, _ptr(d_x), n_in, _ptr(d_diags), n_out, n1, n2, _ptr(d_rlk), gb,
+                              _ptr_list(d_evk_baby), gg, _ptr_list(d_evk_giant), _ptr(d_y), level, flags,
+                              _stream(stream)),
+           "ckks_ctmatvec")
 
 
 def ckks_trace_begin(ctx, kernel):

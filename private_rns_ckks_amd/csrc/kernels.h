@@ -48,6 +48,15 @@ struct PtMacArgs {
   int level, n_in, n1, n2;
 };
 
+struct CtMacArgs {
+  const uint64_t* diags;  // [n_out][n_in][n2][n1][2][level+1][N] ciphertexts
+  const uint64_t* baby;   // [n1][n_in][2][level+1][N]
+  uint64_t* out;          // [n_out][n2][3][level+1][N]
+  const PrimeConst* prime;
+  uint32_t n;
+  int level, n_in, n1, n2;
+};
+
 struct ConstMulArgs {
   const uint64_t* in;  // [2][nl][N] per item
   uint64_t* out;       // [2][nl][N] per item
@@ -103,6 +112,7 @@ int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch);
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch);
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
+int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out);
 // Rescale of `batch` items by limb `level`: v = iNTT of that limb per item
 // and component ([2][N], canonical), w scratch [2][level][N], out [2][level][N].
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,

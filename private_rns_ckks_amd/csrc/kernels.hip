@@ -219,6 +219,61 @@ __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
   }
 }
 
+// Encrypted-weight BSGS inner sums, before relinearisation:
+//   T[o][g] = sum_c sum_b tensor(diag[o][c][g][b], baby[b][c])
+// with tensor(D, X) = (D0 X0, D0 X1 + D1 X0, D1 X1).  Same tiling and
+// workgroup order as ptmac_kernel; four split accumulators per group of 8
+// terms (the middle part keeps its two products apart, so no accumulator
+// takes more than 8 products).
+__global__ __launch_bounds__(256) void ctmac_kernel(CtMacArgs a) {
+  const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
+  const int o = (int)gp.tile, i = gp.job;
+  const uint32_t c = (uint32_t)gp.item * blockDim.x + threadIdx.x;
+  const RedConst pc = red_const((ConstPrime)a.prime, i);
+  const uint64_t limbs = (uint64_t)(a.level + 1);
+  const uint64_t off = (uint64_t)i * a.n + c;
+  const uint64_t ln = limbs * a.n;
+  const int terms = a.n_in * a.n1;
+  for (int g = 0; g < a.n2; ++g) {
+    uint64_t r0 = 0, r1 = 0, r2 = 0;
+    for (int t0 = 0; t0 < terms; t0 += 8) {
+      uint64_t d0[8], d1[8], x0[8], x1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        d0[k] = d1[k] = x0[k] = x1[k] = 0;
+        const int t = t0 + k;
+        if (t < terms) {
+          const int ci = t / a.n1, b = t % a.n1;
+          const uint64_t* d = a.diags + ((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * 2 * ln + off;
+          const uint64_t* x = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * ln + off;
+          d0[k] = d[0];
+          d1[k] = d[ln];
+          x0[k] = x[0];
+          x1[k] = x[ln];
+        }
+      }
+      Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0}, s1b = {0, 0, 0}, s2 = {0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t al = lo30(d0[k]), ah = hi30(d0[k]), bl = lo30(d1[k]), bh = hi30(d1[k]);
+        const uint32_t ul = lo30(x0[k]), uh = hi30(x0[k]), vl = lo30(x1[k]), vh = hi30(x1[k]);
+        acc3_mac(s0, al, ah, ul, uh);
+        acc3_mac(s1, al, ah, vl, vh);
+        acc3_mac(s1b, bl, bh, ul, uh);
+        acc3_mac(s2, bl, bh, vl, vh);
+      }
+      r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc3_reduce(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r2 = add_mod(r2, acc3_reduce(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+    }
+    uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 3 * ln;
+    out[off] = r0;
+    out[ln + off] = r1;
+    out[2 * ln + off] = r2;
+  }
+}
+
 __global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, uint64_t bstride, int nl,
                            const PrimeConst* prime, int log_n) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -304,6 +359,13 @@ int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ptmac", (double)n_out * a.n2 * (a.level + 1) * 2 * (a.n_in * a.n1 + 1) * c->N);
   hipLaunchKernelGGL(ptmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out) {
+  TraceScope ts(c, s, "ctmac", (double)n_out * a.n2 * (a.level + 1) * (4 * a.n_in * a.n1 + 3) * c->N);
+  hipLaunchKernelGGL(ctmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

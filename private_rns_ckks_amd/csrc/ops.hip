@@ -573,3 +573,123 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
 }
 
 }  // extern "C"
+
+// Relinearisation of `batch` three-part ciphertexts T (item b at
+// T + b*t_stride, [3][l+1][N]) into out (item b at out + b*out_stride,
+// [2][l+1][N]): (T0, T1) + KS_{s^2 -> s}(T2), in chunks over the lanes.
+static int relin_batch(Ctx* c, hipStream_t s, const uint64_t* T, uint64_t t_stride, uint64_t* out,
+                       uint64_t out_stride, int batch, int level, const uint64_t* rlk) {
+  const int nq = level + 1;
+  const uint64_t limb = (uint64_t)nq * c->N;
+  const uint64_t per = ks_ws_words(c, level);
+  const int chunk = g_chunk_default();
+  const int n_chunks = (batch + chunk - 1) / chunk;
+  const int lanes = std::min(n_chunks, g_lanes_default());
+  int rc;
+  if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
+  for (int k = 0; k < n_chunks && rc == CKKS_OK; ++k) {
+    const int b0 = k * chunk, n = std::min(chunk, batch - b0);
+    KSItem items[kMaxChunk];
+    for (int i = 0; i < n; ++i) {
+      KSItem& it = items[i];
+      const uint64_t* t = T + (b0 + i) * t_stride;
+      it.d = t + 2 * limb;
+      it.g = 0;
+      it.evk = rlk;
+      it.add[0] = t;
+      it.add[1] = t + limb;
+      it.add_g = 0;
+      it.accum = nullptr;
+      it.out = out + (b0 + i) * out_stride;
+    }
+    rc = ks_chunk(c, lane_stream(c, s, lanes, k), level, n, items, t_stride, t_stride, 0, out_stride, nq,
+                  c->ws + per * chunk * (k % lanes));
+  }
+  return join_lanes(c, s, lanes, rc);
+}
+
+extern "C" {
+
+int ckks_ctmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,
+                  const uint64_t* d_rlk, const uint32_t* baby_galois, const uint64_t* const* d_evk_baby,
+                  const uint32_t* giant_galois, const uint64_t* const* d_evk_giant, uint64_t* d_y, int level,
+                  unsigned flags, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_x || !d_diags || !d_rlk || !d_y || n_in < 1 || n_out < 1 || n1 < 1 || n2 < 1)
+    return set_error(CKKS_EINVAL, "NULL pointer or bad size");
+  if ((n1 > 1 && (!baby_galois || !d_evk_baby)) || (n2 > 1 && (!giant_galois || !d_evk_giant)))
+    return set_error(CKKS_EINVAL, "missing rotation keys");
+  if (misaligned(d_x) || misaligned(d_diags) || misaligned(d_rlk) || misaligned(d_y))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
+  for (int b = 1; b < n1; ++b)
+    if (!d_evk_baby[b - 1] || misaligned(d_evk_baby[b - 1])) return set_error(CKKS_EINVAL, "NULL or misaligned key pointer");
+  for (int g = 1; g < n2; ++g)
+    if (!d_evk_giant[g - 1] || misaligned(d_evk_giant[g - 1]))
+      return set_error(CKKS_EINVAL, "NULL or misaligned key pointer");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (flags & ~CKKS_NO_RESCALE) return set_error(CKKS_EINVAL, "unknown flag");
+  const bool rescale = !(flags & CKKS_NO_RESCALE);
+  if (rescale && level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation and rotation need special primes");
+  for (int b = 1; b < n1; ++b)
+    if ((rc = check_galois(ctx, baby_galois[b - 1]))) return rc;
+  for (int g = 1; g < n2; ++g)
+    if ((rc = check_galois(ctx, giant_galois[g - 1]))) return rc;
+  const uint32_t N = ctx->N;
+  const int nq = level + 1;
+  const uint64_t ct = 2ull * nq * N, t3 = 3ull * nq * N;
+  // baby [n1][n_in] ciphertexts, tensor sums [n_out][n2] (three parts),
+  // relinearised [n_out][n2], rotated [n_out][n2]: context-owned, kept
+  const uint64_t n_baby = ct * n1 * n_in, n_rel = ct * n_out * n2;
+  if ((rc = ensure_aux(ctx, n_baby + t3 * n_out * n2 + 2 * n_rel))) return rc;
+  uint64_t* baby = ctx->aux;
+  uint64_t* T = baby + n_baby;
+  uint64_t* rel = T + t3 * n_out * n2;
+  uint64_t* rot = rel + n_rel;
+  rc = CKKS_OK;
+  do {
+    if (hipMemcpyAsync(baby, d_x, ct * n_in * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+      rc = set_error(CKKS_EHIP, "copy");
+      break;
+    }
+    if (n1 > 1 && (rc = rotate_hoisted(ctx, stream, d_x, ct, n_in, level, n1 - 1, baby_galois, d_evk_baby,
+                                       baby + (uint64_t)n_in * ct, ct, (uint64_t)n_in * ct)))
+      break;
+    CtMacArgs cm;
+    cm.diags = d_diags;
+    cm.baby = baby;
+    cm.out = T;
+    cm.prime = ctx->d_prime;
+    cm.n = N;
+    cm.level = level;
+    cm.n_in = n_in;
+    cm.n1 = n1;
+    cm.n2 = n2;
+    if ((rc = launch_ctmac(ctx, stream, cm, n_out))) break;
+    if ((rc = relin_batch(ctx, stream, T, t3, rel, ct, n_out * n2, level, d_rlk))) break;
+    std::vector<uint32_t> gg(n_out * n2);
+    std::vector<const uint64_t*> kg(n_out * n2);
+    for (int o = 0; o < n_out; ++o)
+      for (int g = 0; g < n2; ++g) {
+        gg[o * n2 + g] = g == 0 ? 1u : giant_galois[g - 1];
+        kg[o * n2 + g] = g == 0 ? nullptr : d_evk_giant[g - 1];
+      }
+    if ((rc = rotate_batch(ctx, stream, rel, rot, ct, n_out * n2, level, gg.data(), kg.data(), 0))) break;
+    for (int g = 1; g < n2 && !rc; ++g)
+      rc = launch_add(ctx, stream, rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
+    if (rc) break;
+    if (rescale) {
+      const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
+      if ((rc = ensure_workspace(ctx, rs_per * std::min(n_out, kMaxChunk)))) break;
+      rc = rescale_batch(ctx, stream, rot, ct * n2, d_y, 2ull * level * N, n_out, level, ctx->ws, ctx->ws_words);
+    } else {
+      for (int o = 0; o < n_out && !rc; ++o)
+        if (hipMemcpyAsync(d_y + o * ct, rot + o * n2 * ct, ct * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+          rc = set_error(CKKS_EHIP, "copy");
+    }
+  } while (0);
+  return rc;
+}
+
+}  // extern "C"

@@ -8,6 +8,8 @@ C5: 48 ciphertext pairs: multiply + relinearise + rescale, then rotate-and-sum
 C4: the BSGS matvec at level 12 with 12 x 3 x 8 x 8 diagonals (15.7 GB).
 Polynomial evaluation: degree 7 on the 48 ciphertexts of a C5 batch at level
     23 (scale 2^54), with item 0 a real encryption (decrypts to p(slots)).
+A x V: the encrypted-weight BSGS matvec at level 12 with 3 x 3 x 8 x 8
+    ciphertext diagonals (7.9 GB).
 """
 import numpy as np
 import pytest
@@ -151,3 +153,37 @@ def test_poly_eval_full(lib, orc, full):
         assert np.array_equal(got[b], ref[0]), b
     dec = orc.decrypt(P, level - d, got[0], s_ntt, s_out).real
     assert np.max(np.abs(dec - sum(c * z ** k for k, c in enumerate(coeffs)))) < 2 ** -30
+
+
+def test_av_full_ctmatvec(lib, orc, full):
+    ctx, P = full
+    c = S.CONFIGS["AV"]
+    level, n_in, n_out, n1, n2 = c["level"], c["n_in"], c["n_out"], c["n1"], c["n2"]
+    nq = level + 1
+    announce("A x V full: ctmatvec %d outputs, %d ciphertext diagonals at level %d"
+             % (n_out, n_out * n_in * n1 * n2, level))
+    torch = torch_cuda()
+    x = S.uniform_limbs(S.stream(7, "full/av/x"), P.q[:nq], P.N, lead=(n_in, 2))
+    d_diags = torch.empty((n_out, n_in, n2, n1, 2, nq, P.N), dtype=torch.int64, device="cuda")
+    diag0 = None
+    for o in range(n_out):
+        blk = S.uniform_limbs(S.stream(o, "full/av/diag"), P.q[:nq], P.N, lead=(n_in, n2, n1, 2))
+        d_diags[o].copy_(torch.from_numpy(blk.view(np.int64)))
+        if o == 0:
+            diag0 = blk
+        del blk
+    rlk = S.uniform_limbs(S.stream(7, "full/av/rlk"), P.mods, P.N, lead=(P.dnum, 2))
+    gb = [P.galois(bb) for bb in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [S.uniform_limbs(S.stream(i, "full/av/kb"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n1 - 1)]
+    kg = [S.uniform_limbs(S.stream(i, "full/av/kg"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n2 - 1)]
+    d_y = empty_dev((n_out, 2, level, P.N))
+    lib.ckks_ctmatvec(ctx, to_dev(x), n_in, d_diags, n_out, n1, n2, to_dev(rlk), gb, [to_dev(k) for k in kb], gg,
+                      [to_dev(k) for k in kg], d_y, level)
+    got = to_host(d_y)
+    del d_diags
+    torch.cuda.empty_cache()
+    for t, m in enumerate(P.q[:level]):
+        assert (got[:, :, t, :] < m).all()
+    ref = orc.ctmatvec(P, level, x, diag0[None], rlk, gb, kb, gg, kg)
+    assert np.array_equal(got[0], ref[0])

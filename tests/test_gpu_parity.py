@@ -377,6 +377,51 @@ def test_ptmatvec_parity(lib, orc, c3small, shape):
         assert np.array_equal(to_host(y), ref)
 
 
+@pytest.mark.parametrize("shape", [(12, 2, 2, 3, 3), (5, 1, 3, 2, 1), (20, 3, 1, 1, 4), (8, 3, 2, 5, 2)],
+                         ids=lambda s: "l%d_in%d_out%d_n1%d_n2%d" % s)
+def test_ctmatvec_parity(lib, orc, c3small, shape):
+    """Encrypted-weight BSGS: partial 8-term groups, a single baby or giant
+    step, 15 terms."""
+    ctx, P = c3small
+    level, n_in, n_out, n1, n2 = shape
+    announce("ctmatvec %s" % (shape,))
+    x = S.uniform_limbs(S.stream(5, "gpu/cmv/x"), P.q[: level + 1], P.N, lead=(n_in, 2))
+    diags = S.uniform_limbs(S.stream(5, "gpu/cmv/d"), P.q[: level + 1], P.N, lead=(n_out, n_in, n2, n1, 2))
+    rlk = S.uniform_limbs(S.stream(5, "gpu/cmv/rlk"), P.mods, P.N, lead=(P.dnum, 2))
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [S.uniform_limbs(S.stream(i, "gpu/cmv/kb"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n1 - 1)]
+    kg = [S.uniform_limbs(S.stream(i, "gpu/cmv/kg"), P.mods, P.N, lead=(P.dnum, 2)) for i in range(n2 - 1)]
+    for flags in (0, 2):
+        lo = level + 1 if flags else level
+        y = empty_dev((n_out, 2, lo, P.N))
+        lib.ckks_ctmatvec(ctx, to_dev(x), n_in, to_dev(diags), n_out, n1, n2, to_dev(rlk), gb,
+                          [to_dev(k) for k in kb], gg, [to_dev(k) for k in kg], y, level, flags)
+        ref = orc.ctmatvec(P, level, x, diags, rlk, gb, kb, gg, kg, flags)
+        assert np.array_equal(to_host(y), ref)
+
+
+def test_ctmatvec_trivial_diagonals_equal_ptmatvec(lib, orc, c3small):
+    """Diagonals (pt, 0) through ckks_ctmatvec give ckks_ptmatvec's words."""
+    ctx, P = c3small
+    level, n_in, n_out, n1, n2 = 9, 2, 2, 4, 2
+    announce("ctmatvec trivial diagonals")
+    x = S.uniform_limbs(S.stream(6, "gpu/cmv/tx"), P.q[: level + 1], P.N, lead=(n_in, 2))
+    pts = S.uniform_limbs(S.stream(6, "gpu/cmv/tp"), P.q[: level + 1], P.N, lead=(n_out, n_in, n2, n1))
+    cd = np.zeros((n_out, n_in, n2, n1, 2, level + 1, P.N), dtype=np.uint64)
+    cd[:, :, :, :, 0] = pts
+    rlk = S.uniform_limbs(S.stream(6, "gpu/cmv/trlk"), P.mods, P.N, lead=(P.dnum, 2))
+    gb = [P.galois(b) for b in range(1, n1)]
+    gg = [P.galois(n1 * g) for g in range(1, n2)]
+    kb = [to_dev(S.uniform_limbs(S.stream(i, "gpu/cmv/tkb"), P.mods, P.N, lead=(P.dnum, 2))) for i in range(n1 - 1)]
+    kg = [to_dev(S.uniform_limbs(S.stream(i, "gpu/cmv/tkg"), P.mods, P.N, lead=(P.dnum, 2))) for i in range(n2 - 1)]
+    y1 = empty_dev((n_out, 2, level, P.N))
+    y2 = empty_dev((n_out, 2, level, P.N))
+    lib.ckks_ctmatvec(ctx, to_dev(x), n_in, to_dev(cd), n_out, n1, n2, to_dev(rlk), gb, kb, gg, kg, y1, level)
+    lib.ckks_ptmatvec(ctx, to_dev(x), n_in, to_dev(pts), n_out, n1, n2, gb, kb, gg, kg, y2, level)
+    assert np.array_equal(to_host(y1), to_host(y2))
+
+
 def test_repeatable(lib, orc, c3small):
     """Same call twice gives identical words (no races between tiles)."""
     ctx, P = c3small
