@@ -272,10 +272,12 @@ def uniform_dev(torch, moduli, N, lead):
 
 
 def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
-    """Wall time of the other two workload recipes on the same parameters:
+    """Wall time of the other workload recipes on the same parameters:
     C4, the BSGS matrix-vector product (3 inputs at level 12, 12 outputs, 8 x 8
-    steps, 15.7 GB of diagonals), and C5, 48 ciphertext products with
-    relinearisation and rescale followed by 15 rotate-and-sum steps."""
+    steps, 15.7 GB of diagonals); C5, 48 ciphertext products with
+    relinearisation and rescale followed by 15 rotate-and-sum steps; a
+    degree-7 polynomial on the 48 ciphertexts; A x V, the BSGS product with
+    576 ciphertext diagonals (7.9 GB)."""
     N = 1 << S.CONFIGS["C4"]["log_n"]
     dnum = S.CONFIGS["C4"]["dnum"]
     res = {}
@@ -321,11 +323,33 @@ def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
         lib.ckks_poly_eval(ctx, a_top, B, level, 2.0 ** 54, coeffs, rlk, pe_out, stream)
 
     res["poly_eval_deg7_ms"] = round(timed(torch, stream, run_pe, reps), 3)
+    del a, b, a_top, keys, bufs, pe_out
+    torch.cuda.empty_cache()
+    # attention output A x V with encrypted weights (ckks_ctmatvec)
+    av = S.CONFIGS["AV"]
+    level, n_in, n_out, n1, n2 = av["level"], av["n_in"], av["n_out"], av["n1"], av["n2"]
+    nq = level + 1
+    x = uniform_dev(torch, q[:nq], N, (n_in, 2))
+    diags = uniform_dev(torch, q[:nq], N, (n_out, n_in, n2, n1, 2))
+    kb = [uniform_dev(torch, q + p, N, (dnum, 2)) for _ in range(n1 - 1)]
+    kg = [uniform_dev(torch, q + p, N, (dnum, 2)) for _ in range(n2 - 1)]
+    gb = [pow(5, b, 2 * N) for b in range(1, n1)]
+    gg = [pow(5, n1 * g, 2 * N) for g in range(1, n2)]
+    y = torch.empty((n_out, 2, level, N), dtype=torch.int64, device="cuda")
+
+    def run_av():
+        lib.ckks_ctmatvec(ctx, x, n_in, diags, n_out, n1, n2, rlk, gb, kb, gg, kg, y, level, 0, stream)
+
+    res["av_ctmatvec_ms"] = round(timed(torch, stream, run_av, reps), 3)
+    del x, diags, kb, kg, y
+    torch.cuda.empty_cache()
     res["note"] = "C4: one ckks_ptmatvec call; C5: ckks_mul_relin_rescale on 48 pairs + 15 accumulate rotations " \
                   "of the 48 products (768 key switches); poly_eval: degree-7 Horner evaluation on 48 ciphertexts " \
-                  "at level 23 (6 products each); device-generated uniform words, %d timed reps" % reps
-    log("C4 ptmatvec %.2f ms, C5 %.2f ms, poly_eval %.2f ms" % (res["c4_ptmatvec_ms"], res["c5_mul_rotsum_ms"],
-                                                             res["poly_eval_deg7_ms"]))
+                  "at level 23 (6 products each); av: one ckks_ctmatvec call (A x V, 3 inputs, 3 outputs, 576 " \
+                  "ciphertext diagonals at level 12, 24 relinearisations); device-generated uniform words, " \
+                  "%d timed reps" % reps
+    log("C4 ptmatvec %.2f ms, C5 %.2f ms, poly_eval %.2f ms, A x V %.2f ms"
+        % (res["c4_ptmatvec_ms"], res["c5_mul_rotsum_ms"], res["poly_eval_deg7_ms"], res["av_ctmatvec_ms"]))
     return res
 
 
