@@ -274,6 +274,147 @@ __global__ __launch_bounds__(256) void ctmac_kernel(CtMacArgs a) {
   }
 }
 
+// The same sums with the loops swapped, for n2 <= MAXG: the baby-step words
+// of a group of 8 (c, b) terms are loaded once and used for every giant step,
+// whose running sums stay in registers; only the diagonals stream.
+template <int MAXG>
+__global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
+  const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
+  const int o = (int)gp.tile, i = gp.job;
+  const uint32_t c = (uint32_t)gp.item * blockDim.x + threadIdx.x;
+  const RedConst pc = red_const((ConstPrime)a.prime, i);
+  const uint64_t limbs = (uint64_t)(a.level + 1);
+  const uint64_t off = (uint64_t)i * a.n + c;
+  const uint64_t ln = limbs * a.n;
+  const int terms = a.n_in * a.n1;
+  uint64_t r0[MAXG], r1[MAXG];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) r0[g] = r1[g] = 0;
+  for (int t0 = 0; t0 < terms; t0 += 8) {
+    uint32_t c0l[8], c0h[8], c1l[8], c1h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = t0 + k;
+      uint64_t x0 = 0, x1 = 0;
+      if (t < terms) {
+        const int ci = t / a.n1, b = t % a.n1;
+        const uint64_t* ct = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * ln + off;
+        x0 = ct[0];
+        x1 = ct[ln];
+      }
+      c0l[k] = lo30(x0);
+      c0h[k] = hi30(x0);
+      c1l[k] = lo30(x1);
+      c1h[k] = hi30(x1);
+    }
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g < a.n2) {
+        uint64_t pt[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = t0 + k;
+          pt[k] = 0;
+          if (t < terms) {
+            const int ci = t / a.n1, b = t % a.n1;
+            pt[k] = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * ln + off];
+          }
+        }
+        Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t pl = lo30(pt[k]), ph = hi30(pt[k]);
+          acc3_mac(s0, pl, ph, c0l[k], c0h[k]);
+          acc3_mac(s1, pl, ph, c1l[k], c1h[k]);
+        }
+        r0[g] = add_mod(r0[g], acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) {
+    if (g < a.n2) {
+      uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 2 * ln;
+      out[off] = r0[g];
+      out[ln + off] = r1[g];
+    }
+  }
+}
+
+// ctmac_kernel with the loops swapped as in ptmac_regs_kernel (n2 <= MAXG).
+template <int MAXG>
+__global__ __launch_bounds__(256) void ctmac_regs_kernel(CtMacArgs a) {
+  const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
+  const int o = (int)gp.tile, i = gp.job;
+  const uint32_t c = (uint32_t)gp.item * blockDim.x + threadIdx.x;
+  const RedConst pc = red_const((ConstPrime)a.prime, i);
+  const uint64_t limbs = (uint64_t)(a.level + 1);
+  const uint64_t off = (uint64_t)i * a.n + c;
+  const uint64_t ln = limbs * a.n;
+  const int terms = a.n_in * a.n1;
+  uint64_t r0[MAXG], r1[MAXG], r2[MAXG];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) r0[g] = r1[g] = r2[g] = 0;
+  for (int t0 = 0; t0 < terms; t0 += 8) {
+    uint32_t ul[8], uh[8], vl[8], vh[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = t0 + k;
+      uint64_t x0 = 0, x1 = 0;
+      if (t < terms) {
+        const int ci = t / a.n1, b = t % a.n1;
+        const uint64_t* x = a.baby + ((uint64_t)b * a.n_in + ci) * 2 * ln + off;
+        x0 = x[0];
+        x1 = x[ln];
+      }
+      ul[k] = lo30(x0);
+      uh[k] = hi30(x0);
+      vl[k] = lo30(x1);
+      vh[k] = hi30(x1);
+    }
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (g < a.n2) {
+        uint64_t d0[8], d1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = t0 + k;
+          d0[k] = d1[k] = 0;
+          if (t < terms) {
+            const int ci = t / a.n1, b = t % a.n1;
+            const uint64_t* d = a.diags + ((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * 2 * ln + off;
+            d0[k] = d[0];
+            d1[k] = d[ln];
+          }
+        }
+        Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0}, s1b = {0, 0, 0}, s2 = {0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t al = lo30(d0[k]), ah = hi30(d0[k]), bl = lo30(d1[k]), bh = hi30(d1[k]);
+          acc3_mac(s0, al, ah, ul[k], uh[k]);
+          acc3_mac(s1, al, ah, vl[k], vh[k]);
+          acc3_mac(s1b, bl, bh, ul[k], uh[k]);
+          acc3_mac(s2, bl, bh, vl[k], vh[k]);
+        }
+        r0[g] = add_mod(r0[g], acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc3_reduce(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r2[g] = add_mod(r2[g], acc3_reduce(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) {
+    if (g < a.n2) {
+      uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 3 * ln;
+      out[off] = r0[g];
+      out[ln + off] = r1[g];
+      out[2 * ln + off] = r2[g];
+    }
+  }
+}
+
 __global__ void add_kernel(const uint64_t* x, const uint64_t* y, uint64_t* out, uint64_t bstride, int nl,
                            const PrimeConst* prime, int log_n) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -358,14 +499,20 @@ int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
 
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ptmac", (double)n_out * a.n2 * (a.level + 1) * 2 * (a.n_in * a.n1 + 1) * c->N);
-  hipLaunchKernelGGL(ptmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  if (a.n2 <= 8)
+    hipLaunchKernelGGL(ptmac_regs_kernel<8>, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(ptmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ctmac", (double)n_out * a.n2 * (a.level + 1) * (4 * a.n_in * a.n1 + 3) * c->N);
-  hipLaunchKernelGGL(ctmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  if (a.n2 <= 8)
+    hipLaunchKernelGGL(ctmac_regs_kernel<8>, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(ctmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

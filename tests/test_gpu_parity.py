@@ -354,11 +354,13 @@ def test_mul_relin_rescale_parity(lib, orc, c3small, flags):
     assert np.array_equal(to_host(out), orc.mul_relin_rescale(P, level, a, b, rlk, flags))
 
 
-@pytest.mark.parametrize("shape", [(12, 2, 3, 4, 3), (5, 1, 2, 3, 1), (20, 5, 2, 1, 4), (8, 3, 4, 5, 2)],
+@pytest.mark.parametrize("shape", [(12, 2, 3, 4, 3), (5, 1, 2, 3, 1), (20, 5, 2, 1, 4), (8, 3, 4, 5, 2),
+                                   (6, 1, 2, 2, 9)],
                          ids=lambda s: "l%d_in%d_out%d_n1%d_n2%d" % s)
 def test_ptmatvec_parity(lib, orc, c3small, shape):
-    """BSGS shapes with partial 8-term groups, a single baby or giant step and
-    more than 8 (c, b) terms."""
+    """BSGS shapes with partial 8-term groups, a single baby or giant step,
+    more than 8 (c, b) terms, and more than 8 giant steps (the kernel that
+    keeps the giant-step sums in memory order instead of registers)."""
     ctx, P = c3small
     level, n_in, n_out, n1, n2 = shape
     announce("ptmatvec %s" % (shape,))
@@ -377,11 +379,12 @@ def test_ptmatvec_parity(lib, orc, c3small, shape):
         assert np.array_equal(to_host(y), ref)
 
 
-@pytest.mark.parametrize("shape", [(12, 2, 2, 3, 3), (5, 1, 3, 2, 1), (20, 3, 1, 1, 4), (8, 3, 2, 5, 2)],
+@pytest.mark.parametrize("shape", [(12, 2, 2, 3, 3), (5, 1, 3, 2, 1), (20, 3, 1, 1, 4), (8, 3, 2, 5, 2),
+                                   (6, 1, 2, 2, 9)],
                          ids=lambda s: "l%d_in%d_out%d_n1%d_n2%d" % s)
 def test_ctmatvec_parity(lib, orc, c3small, shape):
     """Encrypted-weight BSGS: partial 8-term groups, a single baby or giant
-    step, 15 terms."""
+    step, 15 terms, 9 giant steps."""
     ctx, P = c3small
     level, n_in, n_out, n1, n2 = shape
     announce("ctmatvec %s" % (shape,))
