@@ -94,6 +94,7 @@ struct RowIPArgs {
   const uint64_t* tw;  // forward twiddles
   const PrimeConst* prime;
   int log_n, level, next, beta, alpha, L, K;
+  int shared_key;  // every item uses the same key: order the grid items first
 };
 
 // A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     RowIPArgs a) {
   __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
   __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
-  const GridPos gp = row_grid_pos();
+  const GridPos gp = a.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
   const int t = gp.job;
   const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
   const PrimeConst& pc = a.prime[keyl];
@@ -751,7 +752,11 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ip.T_bstride = T_stride;
     ip.acc = A;
     ip.acc_bstride = per;
-    for (int i = 0; i < n_items; ++i) ip.evk[i] = it[i].evk;
+    ip.shared_key = 1;
+    for (int i = 0; i < n_items; ++i) {
+      ip.evk[i] = it[i].evk;
+      if (it[i].evk != it[0].evk) ip.shared_key = 0;
+    }
     ip.tw = c->d_tw_fwd;
     ip.prime = c->d_prime;
     ip.log_n = log_n;

@@ -288,17 +288,30 @@ __device__ __forceinline__ uint32_t xcd_part_start(uint32_t c, uint32_t n) {
   const uint32_t m = n / kXcds, r = n % kXcds;
   return c < r ? c * (m + 1) : r * (m + 1) + (c - r) * m;
 }
+// ITEMS_FIRST puts the items of one (tile, job) next to each other instead:
+// for the key inner product, whose items often share one key (a
+// relinearisation key, or one rotation key for a whole batch), so that each
+// key tile is fetched once for all of them.
+template <bool ITEMS_FIRST = false>
 __device__ __forceinline__ GridPos row_grid_pos() {
   const uint32_t gx = gridDim.x, gy = gridDim.y, gz = gridDim.z;
   const uint32_t b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const uint32_t logical = xcd_part_start(b % kXcds, gx * gy * gz) + b / kXcds;
   GridPos p;
-  p.tile = logical % gx;
-  const uint32_t rest = logical / gx;
-  p.item = (int)(rest % gz);
+  uint32_t jl;
+  if (ITEMS_FIRST) {
+    p.item = (int)(logical % gz);
+    p.tile = (logical / gz) % gx;
+    jl = logical / gz / gx;
+  } else {
+    p.tile = logical % gx;
+    const uint32_t rest = logical / gx;
+    p.item = (int)(rest % gz);
+    jl = rest / gz;
+  }
   // jobs in the order 0, 8, 16, ..., 1, 9, 17, ...: every XCD gets jobs from
   // across the range (the special primes, at the end, cost more per limb)
-  const uint32_t jl = rest / gz, m = gy / kXcds, r = gy % kXcds;
+  const uint32_t m = gy / kXcds, r = gy % kXcds;
   uint32_t cls, idx;
   if (jl < r * (m + 1)) {
     cls = jl / (m + 1);

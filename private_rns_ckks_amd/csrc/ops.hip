@@ -97,16 +97,55 @@ int join_lanes(Ctx* c, hipStream_t s, int lanes, int rc) {
 
 hipStream_t lane_stream(Ctx* c, hipStream_t s, int lanes, int k) { return lanes > 1 ? c->lane[k % lanes] : s; }
 
+// Key switching of rotation pieces: each piece is up to g_chunk_default()
+// items at in + i*stride / out + i*stride (i < n), all rotated by g with one
+// key.  Piece k runs on internal stream k % lanes with its own workspace, so
+// one piece's memory-bound kernels overlap another's arithmetic-bound ones.
+struct RotPiece {
+  const uint64_t* in;
+  uint64_t* out;
+  uint64_t stride;
+  int n;
+  const uint32_t* g;           // item m: g[m * step]
+  const uint64_t* const* evk;  // item m: evk[m * step]
+  int step;                    // 1: per-item elements and keys, 0: one for all
+};
+
+static int rotate_pieces(Ctx* c, hipStream_t s, const std::vector<RotPiece>& pieces, int level, unsigned flags) {
+  const int nq = level + 1;
+  const uint64_t per = ks_ws_words(c, level);
+  const int chunk = g_chunk_default();
+  int rc;
+  const int lanes = (int)std::min<size_t>(pieces.size(), g_lanes_default());
+  if (pieces.empty()) return CKKS_OK;
+  if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
+  for (size_t k = 0; k < pieces.size() && rc == CKKS_OK; ++k) {
+    const RotPiece& pc = pieces[k];
+    KSItem items[kMaxChunk];
+    for (int m = 0; m < pc.n; ++m) {
+      KSItem& it = items[m];
+      it.d = pc.in + m * pc.stride + (uint64_t)nq * c->N;  // c1
+      it.g = pc.g[m * pc.step];
+      it.evk = pc.evk[m * pc.step];
+      it.add[0] = pc.in + m * pc.stride;  // c0, gathered through g
+      it.add[1] = nullptr;
+      it.add_g = it.g;
+      it.accum = (flags & CKKS_ROT_ACCUMULATE) ? pc.in + m * pc.stride : nullptr;
+      it.out = pc.out + m * pc.stride;
+    }
+    rc = ks_chunk(c, lane_stream(c, s, lanes, (int)k), level, pc.n, items, pc.stride, pc.stride, pc.stride,
+                  pc.stride, nq, c->ws + per * chunk * (k % lanes));
+  }
+  return join_lanes(c, s, lanes, rc);
+}
+
 // Batched rotation with contiguous input/output (item b at base + b*stride).
-// Items with g != 1 are key-switched in chunks (runs of consecutive items of
-// at most g_chunk_default()); with several lanes, chunk k runs on internal
-// stream k % lanes with its own workspace, so one chunk's memory-bound kernels
-// overlap another's arithmetic-bound ones.
+// Items with g == 1 are copied (or doubled when accumulating); the others are
+// key-switched in pieces of consecutive items (at most g_chunk_default()).
 int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint64_t stride, int batch, int level,
                  const uint32_t* g, const uint64_t* const* evk, unsigned flags) {
   const int nq = level + 1;
   const uint64_t ct_words = 2ull * nq * c->N;
-  const uint64_t per = ks_ws_words(c, level);
   const int chunk = g_chunk_default();
   int rc;
   std::vector<int> idx;
@@ -122,34 +161,37 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
     }
   }
   // consecutive runs of non-identity items share a stride
-  std::vector<std::pair<size_t, size_t>> pieces;
+  std::vector<RotPiece> pieces;
   for (size_t p = 0; p < idx.size();) {
     size_t q = p + 1;
     while (q < idx.size() && q - p < (size_t)chunk && idx[q] == idx[q - 1] + 1) ++q;
-    pieces.emplace_back(p, q);
+    const int b = idx[p];
+    pieces.push_back(RotPiece{in + b * stride, out + b * stride, stride, (int)(q - p), g + b, evk + b, 1});
     p = q;
   }
-  const int lanes = (int)std::min<size_t>(pieces.size(), g_lanes_default());
-  if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
-  for (size_t k = 0; k < pieces.size() && rc == CKKS_OK; ++k) {
-    const size_t p = pieces[k].first, q = pieces[k].second;
-    KSItem items[kMaxChunk];
-    for (size_t m = p; m < q; ++m) {
-      const int b = idx[m];
-      KSItem& it = items[m - p];
-      it.d = in + b * stride + (uint64_t)nq * c->N;  // c1
-      it.g = g[b];
-      it.evk = evk[b];
-      it.add[0] = in + b * stride;  // c0, gathered through g
-      it.add[1] = nullptr;
-      it.add_g = g[b];
-      it.accum = (flags & CKKS_ROT_ACCUMULATE) ? in + b * stride : nullptr;
-      it.out = out + b * stride;
+  return rotate_pieces(c, s, pieces, level, flags);
+}
+
+// Giant steps of a BSGS product: rot[o][g] = Rot_g(inner[o][g]) for g >= 1
+// (items at base + (o*n2 + g)*ct), in pieces of outputs that share one giant
+// step, so the items of a piece share their key.
+static int rotate_giant_steps(Ctx* c, hipStream_t s, const uint64_t* inner, uint64_t* rot, uint64_t ct, int n_out,
+                              int n2, int level, const uint32_t* giant_galois, const uint64_t* const* d_evk_giant) {
+  const int chunk = g_chunk_default();
+  std::vector<RotPiece> pieces;
+  for (int g = 1; g < n2; ++g)
+    for (int o0 = 0; o0 < n_out; o0 += chunk) {
+      RotPiece pc;
+      pc.in = inner + ((uint64_t)o0 * n2 + g) * ct;
+      pc.out = rot + ((uint64_t)o0 * n2 + g) * ct;
+      pc.stride = (uint64_t)n2 * ct;
+      pc.n = std::min(chunk, n_out - o0);
+      pc.g = giant_galois + (g - 1);
+      pc.evk = d_evk_giant + (g - 1);
+      pc.step = 0;
+      pieces.push_back(pc);
     }
-    rc = ks_chunk(c, lane_stream(c, s, lanes, (int)k), level, (int)(q - p), items, stride, stride, stride, stride,
-                  nq, c->ws + per * chunk * (k % lanes));
-  }
-  return join_lanes(c, s, lanes, rc);
+  return rotate_pieces(c, s, pieces, level, 0);
 }
 
 // Hoisted rotations: input c (at in + c*in_stride, [2][l+1][N]) rotated by
@@ -547,17 +589,15 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
     pm.n1 = n1;
     pm.n2 = n2;
     if ((rc = launch_ptmac(ctx, stream, pm, n_out))) break;
-    std::vector<uint32_t> gg(n_out * n2);
-    std::vector<const uint64_t*> kg(n_out * n2);
-    for (int o = 0; o < n_out; ++o)
-      for (int g = 0; g < n2; ++g) {
-        gg[o * n2 + g] = g == 0 ? 1u : giant_galois[g - 1];
-        kg[o * n2 + g] = g == 0 ? nullptr : d_evk_giant[g - 1];
-      }
-    if ((rc = rotate_batch(ctx, stream, inner, rot, ct, n_out * n2, level, gg.data(), kg.data(), 0))) break;
-    // sum over giant steps into rot[o][0]
+    if ((rc = rotate_giant_steps(ctx, stream, inner, rot, ct, n_out, n2, level, giant_galois, d_evk_giant))) break;
+    // sum over giant steps into rot[o][0] (giant step 0 is not rotated)
+    if (n2 == 1) {
+      for (int o = 0; o < n_out && !rc; ++o)
+        if (hipMemcpyAsync(rot + o * ct, inner + o * ct, ct * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+          rc = set_error(CKKS_EHIP, "copy");
+    }
     for (int g = 1; g < n2 && !rc; ++g)
-      rc = launch_add(ctx, stream, rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
+      rc = launch_add(ctx, stream, g == 1 ? inner : rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
     if (rc) break;
     if (rescale) {
       const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
@@ -668,16 +708,14 @@ int ckks_ctmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
     cm.n2 = n2;
     if ((rc = launch_ctmac(ctx, stream, cm, n_out))) break;
     if ((rc = relin_batch(ctx, stream, T, t3, rel, ct, n_out * n2, level, d_rlk))) break;
-    std::vector<uint32_t> gg(n_out * n2);
-    std::vector<const uint64_t*> kg(n_out * n2);
-    for (int o = 0; o < n_out; ++o)
-      for (int g = 0; g < n2; ++g) {
-        gg[o * n2 + g] = g == 0 ? 1u : giant_galois[g - 1];
-        kg[o * n2 + g] = g == 0 ? nullptr : d_evk_giant[g - 1];
-      }
-    if ((rc = rotate_batch(ctx, stream, rel, rot, ct, n_out * n2, level, gg.data(), kg.data(), 0))) break;
+    if ((rc = rotate_giant_steps(ctx, stream, rel, rot, ct, n_out, n2, level, giant_galois, d_evk_giant))) break;
+    if (n2 == 1) {
+      for (int o = 0; o < n_out && !rc; ++o)
+        if (hipMemcpyAsync(rot + o * ct, rel + o * ct, ct * 8, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+          rc = set_error(CKKS_EHIP, "copy");
+    }
     for (int g = 1; g < n2 && !rc; ++g)
-      rc = launch_add(ctx, stream, rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
+      rc = launch_add(ctx, stream, g == 1 ? rel : rot, rot + g * ct, rot, n_out, nq, 2, ct * n2);
     if (rc) break;
     if (rescale) {
       const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
