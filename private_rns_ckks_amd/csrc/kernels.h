@@ -31,9 +31,10 @@ struct ModDownArgs {
 };
 
 struct TensorArgs {
-  const uint64_t *a, *b;  // [2][level+1][N] per item
+  const uint64_t *a, *b;  // [2][level+1][N] per item (b: component stride b_comp)
   uint64_t* out;          // [3][level+1][N] per item
   uint64_t in_bstride, out_bstride;
+  uint64_t b_bstride, b_comp;  // b's item and component strides (b may hold more limbs)
   const PrimeConst* prime;
   uint32_t n;
   int level;
@@ -66,11 +67,6 @@ struct ConstMulArgs {
   int nl, log_n;
 };
 
-struct ConstAddArgs {
-  const PrimeConst* prime;
-  uint64_t v[64];  // per limb: constant mod q_i
-  int log_n;
-};
 
 struct KSItem {
   const uint64_t* d;       // NTT-form input polynomial [level+1][N]
@@ -116,9 +112,9 @@ int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out);
 // Rescale of `batch` items by limb `level`: v = iNTT of that limb per item
 // and component ([2][N], canonical), w scratch [2][level][N], out [2][level][N].
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
-                  uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level);
+                  uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
+                  const uint64_t* add0 = nullptr);
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
-int launch_add_const(Ctx* c, hipStream_t s, uint64_t* x, uint64_t bstride, int nl, ConstAddArgs& a, int batch);
 int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
                int ncomp, uint64_t bstride);
 

@@ -155,9 +155,9 @@ __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
   const uint64_t lim = (uint64_t)(a.level + 1) * a.n;
   const uint64_t off = (uint64_t)i * a.n + c;
   const uint64_t* x = a.a + blockIdx.z * a.in_bstride;
-  const uint64_t* y = a.b + blockIdx.z * a.in_bstride;
+  const uint64_t* y = a.b + blockIdx.z * a.b_bstride;
   uint64_t* d = a.out + blockIdx.z * a.out_bstride;
-  const uint64_t a0 = x[off], a1 = x[lim + off], b0 = y[off], b1 = y[lim + off];
+  const uint64_t a0 = x[off], a1 = x[lim + off], b0 = y[off], b1 = y[a.b_comp + off];
   const uint32_t a0l = lo30(a0), a0h = hi30(a0), a1l = lo30(a1), a1h = hi30(a1);
   const uint32_t b0l = lo30(b0), b0h = hi30(b0), b1l = lo30(b1), b1h = hi30(b1);
   Acc3 m0 = {0, 0, 0}, m1 = {0, 0, 0}, m2 = {0, 0, 0};
@@ -434,15 +434,6 @@ __global__ void const_mul_kernel(ConstMulArgs a) {
   a.out[blockIdx.z * a.out_bstride + off] = reduce_4q(mul_shoup_lazy(v, a.k[i][0], a.k[i][1], q), q);
 }
 
-// The constant polynomial v_i (per limb) added to component 0 in place: in NTT
-// form a constant is that constant in every word.
-__global__ void add_const_kernel(uint64_t* x, uint64_t bstride, ConstAddArgs a) {
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int i = blockIdx.y;
-  const uint64_t off = blockIdx.z * bstride + ((uint64_t)i << a.log_n) + c;
-  x[off] = add_mod(x[off], a.v[i], a.prime[i].q);
-}
-
 }  // namespace
 
 #define LAUNCH_CHECK() CKKS_HIP_CHECK(hipGetLastError())
@@ -529,13 +520,6 @@ int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch) {
   TraceScope ts(c, s, "const_mul", (double)batch * 2 * a.nl * c->N);
   hipLaunchKernelGGL(const_mul_kernel, dim3(c->N / 256, 2 * a.nl, batch), dim3(256), 0, s, a);
-  LAUNCH_CHECK();
-  return CKKS_OK;
-}
-
-int launch_add_const(Ctx* c, hipStream_t s, uint64_t* x, uint64_t bstride, int nl, ConstAddArgs& a, int batch) {
-  TraceScope ts(c, s, "add", 0);
-  hipLaunchKernelGGL(add_const_kernel, dim3(c->N / 256, nl, batch), dim3(256), 0, s, x, bstride, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -54,7 +54,7 @@ int check_galois(const Ctx* c, uint32_t g) {
 
 // Rescale of `batch` items: in [2][level+1][N] at in + b*in_stride -> out [2][level][N].
 int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride, uint64_t* out, uint64_t out_stride,
-                  int batch, int level, uint64_t* ws, uint64_t ws_words) {
+                  int batch, int level, uint64_t* ws, uint64_t ws_words, const uint64_t* add0 = nullptr) {
   const uint32_t N = c->N;
   const uint64_t per = (uint64_t)N * (2 + 2 * level);
   const int chunk = (int)std::max<uint64_t>(1, std::min<uint64_t>(kMaxChunk, ws_words / per));
@@ -68,7 +68,7 @@ int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride,
     if (rc) return rc;
     // conversion and final combination fused into the forward NTT of w
     if ((rc = rescale_fused(c, s, in + b0 * in_stride, in_stride, V, per, W, per, out + b0 * out_stride, out_stride, n,
-                            level)))
+                            level, add0)))
       return rc;
   }
   return CKKS_OK;
@@ -96,6 +96,66 @@ int join_lanes(Ctx* c, hipStream_t s, int lanes, int rc) {
 }
 
 hipStream_t lane_stream(Ctx* c, hipStream_t s, int lanes, int k) { return lanes > 1 ? c->lane[k % lanes] : s; }
+
+// Multiply, relinearise and (when `rescale`) rescale a batch: a item b at
+// a + b*2(l+1)N; b item b at b + b*b_bstride with component stride b_comp (so
+// b may be a higher-level ciphertext read at its first l+1 limbs).  add0:
+// optional per-limb constant added to component 0 of the rescaled output.
+static int mul_relin_rescale(Ctx* ctx, hipStream_t stream, const uint64_t* d_a, const uint64_t* d_b,
+                             uint64_t b_bstride,
+                             uint64_t b_comp, const uint64_t* d_rlk, uint64_t* d_out, int batch, int level,
+                             bool rescale, const uint64_t* add0) {
+  if (batch == 0) return CKKS_OK;
+  const uint32_t N = ctx->N;
+  const int nq = level + 1;
+  const uint64_t ct = 2ull * nq * N;
+  const int chunk = g_chunk_default();
+  const int n_chunks = (batch + chunk - 1) / chunk;
+  const int lanes = std::min(n_chunks, g_lanes_default());
+  const uint64_t ks = ks_ws_words(ctx, level);
+  // per chunk: tensor output [3][nq][N] per item, relinearised [2][nq][N] per item, then key-switch scratch
+  const uint64_t tens = 3ull * nq * N, rel = ct;
+  const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
+  const uint64_t region = chunk * (tens + rel + std::max(ks, rs_per));  // one lane's workspace
+  int rc;
+  if ((rc = ensure_workspace(ctx, region * lanes)) || (rc = fork_lanes(ctx, stream, lanes))) return rc;
+  for (int k = 0; k < n_chunks && rc == CKKS_OK; ++k) {
+    const int b0 = k * chunk, n = std::min(chunk, batch - b0);
+    const hipStream_t ls = lane_stream(ctx, stream, lanes, k);
+    uint64_t* D = ctx->ws + region * (k % lanes);
+    uint64_t* R = D + chunk * tens;
+    uint64_t* S = R + chunk * rel;
+    TensorArgs ta;
+    ta.a = d_a + b0 * ct;
+    ta.b = d_b + b0 * b_bstride;
+    ta.out = D;
+    ta.in_bstride = ct;
+    ta.b_bstride = b_bstride;
+    ta.b_comp = b_comp;
+    ta.out_bstride = tens;
+    ta.prime = ctx->d_prime;
+    ta.n = N;
+    ta.level = level;
+    if ((rc = launch_tensor(ctx, ls, ta, n))) break;
+    KSItem items[kMaxChunk];
+    for (int i = 0; i < n; ++i) {
+      KSItem& it = items[i];
+      it.d = D + i * tens + 2ull * nq * N;
+      it.g = 0;
+      it.evk = d_rlk;
+      it.add[0] = D + i * tens;
+      it.add[1] = D + i * tens + (uint64_t)nq * N;
+      it.add_g = 0;
+      it.accum = nullptr;
+      it.out = rescale ? R + i * rel : d_out + (b0 + i) * ct;
+    }
+    if ((rc = ks_chunk(ctx, ls, level, n, items, tens, tens, 0, rel, nq, S))) break;
+    if (rescale)
+      rc = rescale_batch(ctx, ls, R, rel, d_out + b0 * 2ull * level * N, 2ull * level * N, n, level, S,
+                         chunk * std::max(ks, rs_per), add0);
+  }
+  return join_lanes(ctx, stream, lanes, rc);
+}
 
 // Key switching of rotation pieces: each piece is up to g_chunk_default()
 // items at in + i*stride / out + i*stride (i < n), all rotated by g with one
@@ -394,53 +454,9 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
   const bool rescale = !(flags & CKKS_NO_RESCALE);
   if (rescale && level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
   if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation needs special primes");
-  if (batch == 0) return CKKS_OK;
-  const uint32_t N = ctx->N;
-  const int nq = level + 1;
-  const uint64_t ct = 2ull * nq * N;
-  const int chunk = g_chunk_default();
-  const int n_chunks = (batch + chunk - 1) / chunk;
-  const int lanes = std::min(n_chunks, g_lanes_default());
-  const uint64_t ks = ks_ws_words(ctx, level);
-  // per chunk: tensor output [3][nq][N] per item, relinearised [2][nq][N] per item, then key-switch scratch
-  const uint64_t tens = 3ull * nq * N, rel = ct;
-  const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
-  const uint64_t region = chunk * (tens + rel + std::max(ks, rs_per));  // one lane's workspace
-  if ((rc = ensure_workspace(ctx, region * lanes)) || (rc = fork_lanes(ctx, stream, lanes))) return rc;
-  for (int k = 0; k < n_chunks && rc == CKKS_OK; ++k) {
-    const int b0 = k * chunk, n = std::min(chunk, batch - b0);
-    const hipStream_t ls = lane_stream(ctx, stream, lanes, k);
-    uint64_t* D = ctx->ws + region * (k % lanes);
-    uint64_t* R = D + chunk * tens;
-    uint64_t* S = R + chunk * rel;
-    TensorArgs ta;
-    ta.a = d_a + b0 * ct;
-    ta.b = d_b + b0 * ct;
-    ta.out = D;
-    ta.in_bstride = ct;
-    ta.out_bstride = tens;
-    ta.prime = ctx->d_prime;
-    ta.n = N;
-    ta.level = level;
-    if ((rc = launch_tensor(ctx, ls, ta, n))) break;
-    KSItem items[kMaxChunk];
-    for (int i = 0; i < n; ++i) {
-      KSItem& it = items[i];
-      it.d = D + i * tens + 2ull * nq * N;
-      it.g = 0;
-      it.evk = d_rlk;
-      it.add[0] = D + i * tens;
-      it.add[1] = D + i * tens + (uint64_t)nq * N;
-      it.add_g = 0;
-      it.accum = nullptr;
-      it.out = rescale ? R + i * rel : d_out + (b0 + i) * ct;
-    }
-    if ((rc = ks_chunk(ctx, ls, level, n, items, tens, tens, 0, rel, nq, S))) break;
-    if (rescale)
-      rc = rescale_batch(ctx, ls, R, rel, d_out + b0 * 2ull * level * N, 2ull * level * N, n, level, S,
-                         chunk * std::max(ks, rs_per));
-  }
-  return join_lanes(ctx, stream, lanes, rc);
+  const uint64_t ct = 2ull * (level + 1) * ctx->N;
+  return mul_relin_rescale(ctx, stream, d_a, d_b, ct, (uint64_t)(level + 1) * ctx->N, d_rlk, d_out, batch, level,
+                           rescale, nullptr);
 }
 
 // round(x) for |x| < 2^62, the same rounding (llround) as the reference
@@ -483,19 +499,10 @@ int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level,
   if (batch == 0) return CKKS_OK;
   const uint32_t N = ctx->N;
   const uint64_t in_ct = 2ull * (level + 1) * N, ct_l = 2ull * level * N;
-  // operand buffers: the constant product at level `level`, two accumulators
-  // and the input restricted to the accumulator's limbs (level - 1 and below)
-  if ((rc = ensure_aux(ctx, batch * (in_ct + 3 * ct_l)))) return rc;
+  // operand buffers: the constant product at level `level` and two accumulators
+  if ((rc = ensure_aux(ctx, batch * (in_ct + 2 * ct_l)))) return rc;
   uint64_t* T = ctx->aux;
   uint64_t* acc[2] = {T + batch * in_ct, T + batch * in_ct + batch * ct_l};
-  uint64_t* X = acc[1] + batch * ct_l;
-  auto add_const = [&](uint64_t* ct, int lvl, int64_t v) {
-    ConstAddArgs ca;
-    ca.prime = ctx->d_prime;
-    ca.log_n = (int)ctx->log_n;
-    for (int i = 0; i <= lvl; ++i) ca.v[i] = signed_mod(v, ctx->mod[i]);
-    return launch_add_const(ctx, stream, ct, 2ull * (lvl + 1) * N, lvl + 1, ca, batch);
-  };
   // acc = c_d * x: times round(c_d * q_l) on every limb, then rescale
   {
     ConstMulArgs cm;
@@ -515,19 +522,25 @@ int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level,
   uint64_t* dst = d == 1 ? d_ct_out : acc[0];
   const uint64_t rs_per = (uint64_t)N * (2 + 2 * level);
   if ((rc = ensure_workspace(ctx, rs_per * std::min(batch, kMaxChunk)))) return rc;
-  if ((rc = rescale_batch(ctx, stream, T, in_ct, dst, ct_l, batch, level, ctx->ws, ctx->ws_words))) return rc;
+  // the constants enter in NTT form (the same value in every word of a limb),
+  // added to component 0 by the final store of each rescale
+  uint64_t cv[64];
+  auto consts = [&](int lvl, int64_t v) {
+    for (int i = 0; i <= lvl; ++i) cv[i] = signed_mod(v, ctx->mod[i]);
+    return cv;
+  };
+  if ((rc = rescale_batch(ctx, stream, T, in_ct, dst, ct_l, batch, level, ctx->ws, ctx->ws_words,
+                          consts(level - 1, kadd[d - 1]))))
+    return rc;
   int l = level - 1;
-  if ((rc = add_const(dst, l, kadd[d - 1]))) return rc;
-  // Horner steps: acc = rescale(relin(acc * x)) + c_k
+  // Horner steps: acc = rescale(relin(acc * x)) + c_k, with x read at its
+  // first l+1 limbs in place
   for (int k = d - 2, cur = 0; k >= 0; --k, cur ^= 1) {
-    const uint64_t lsz = (uint64_t)(l + 1) * N;
-    // x restricted to limbs 0..l of each component
-    CKKS_HIP_CHECK(hipMemcpy2DAsync(X, lsz * 8, d_ct_in, (uint64_t)(level + 1) * N * 8, lsz * 8, 2ull * batch,
-                                    hipMemcpyDeviceToDevice, stream));
     uint64_t* next = k == 0 ? d_ct_out : acc[cur ^ 1];
-    if ((rc = ckks_mul_relin_rescale(ctx, acc[cur], X, d_rlk, next, batch, l, 0, stream))) return rc;
+    if ((rc = mul_relin_rescale(ctx, stream, acc[cur], d_ct_in, in_ct, (uint64_t)(level + 1) * N, d_rlk, next,
+                                batch, l, true, consts(l - 1, kadd[k]))))
+      return rc;
     --l;
-    if ((rc = add_const(next, l, kadd[k]))) return rc;
   }
   return CKKS_OK;
 }

@@ -1,7 +1,8 @@
 // Rescale of a batch by its top limb q_l with the basis conversion fused
 // into the forward NTT's column pass and the final combination into its row
 // pass (the converted limbs make one round trip through memory instead of
-// three).  Per item, component and limb i < l, with v = iNTT(c_l) canonical
+// three).  Optionally a per-limb constant (a constant polynomial in NTT form)
+// is added to component 0 by the same final store.  Per item, component and limb i < l, with v = iNTT(c_l) canonical
 // and vbar its centred lift:
 //   w_i   = (vbar mod q_i) * [q_l^-1]_{q_i}
 //   out_i = c_i * [q_l^-1]_{q_i} - NTT(w_i)          (mod q_i)
@@ -26,6 +27,8 @@ struct RescalePassArgs {
   const PrimeConst* prime;
   const uint64_t* tw;  // forward twiddles
   int log_n, level, L;
+  int has_add;
+  uint64_t add0[64];  // has_add: added to component 0 of limb i (a constant in NTT form)
 };
 
 // Column-pass input: w_i computed from v on load.
@@ -76,12 +79,12 @@ struct RescaleCombineIO {
   const uint64_t* w;
   const uint64_t* ct;
   uint64_t* out;
-  uint64_t q, qinv, qinvp;
+  uint64_t q, qinv, qinvp, add;
   __device__ __forceinline__ uint64_t load(uint32_t j) const { return w[j]; }
   __device__ __forceinline__ void after_load(uint32_t, uint64_t) const {}
   __device__ __forceinline__ Ops fetch(uint32_t j) const { return Ops{ct[j]}; }
   __device__ __forceinline__ void store(uint32_t j, uint64_t x, const Ops& o) const {
-    out[j] = sub_mod(reduce_2q(mul_shoup(o.c, qinv, qinvp, q), q), x, q);
+    out[j] = add_mod(sub_mod(reduce_2q(mul_shoup(o.c, qinv, qinvp, q), q), x, q), add, q);
   }
 };
 
@@ -101,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void rescale_row_kernel(RescalePassArgs a
   io.q = pc.q;
   io.qinv = rs[0];
   io.qinvp = rs[1];
+  io.add = (a.has_add && comp == 0) ? a.add0[i] : 0;
   Finish fin{1, 0, 0, pc.inv1};
   run_pass<RA, RB, false, false, LOGN>(io, lds, gp.tile, a.log_n, a.tw + ((uint64_t)i << (a.log_n + 1)), pc.q, fin);
 }
@@ -108,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void rescale_row_kernel(RescalePassArgs a
 }  // namespace
 
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
-                  uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level) {
+                  uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
+                  const uint64_t* add0) {
   const uint32_t N = c->N;
   const int log_n = (int)c->log_n;
   const int lr = logb_row(log_n), lc = logb_col(log_n);
@@ -128,6 +133,11 @@ int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride
   a.log_n = log_n;
   a.level = level;
   a.L = (int)c->L;
+  if (add0) {
+    if (level > 64) return set_error(CKKS_EINTERNAL, "too many limbs for a fused constant");
+    a.has_add = 1;
+    for (int i = 0; i < level; ++i) a.add0[i] = add0[i];
+  }
   auto fc = CKKS_PICK_PASS(rescale_col_kernel, log_n, lc);
   auto fr = CKKS_PICK_PASS(rescale_row_kernel, log_n, lr);
   if (!fc || !fr) return set_error(CKKS_EINTERNAL, "unsupported N");
