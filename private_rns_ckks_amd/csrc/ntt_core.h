@@ -90,6 +90,18 @@ __device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t 
   y = mul_shoup_lazy(d, w, wp, q);
 }
 
+// Gentleman-Sande without reducing the sum, for q < 2^54: with every word of
+// the pass below m before the stage, the sum stays below 2m, x + m - y lies in
+// (0, 2m) and the product below 4q, so m doubles per stage.  From words below
+// 4q, 8 stages end below 2^10 q < 2^64; the pass reduces once at its end.
+__device__ __forceinline__ void gs_butterfly_lazy(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q,
+                                                  uint64_t m) {
+  const uint64_t s = x + y;
+  const uint64_t d = x + m - y;
+  x = s;
+  y = mul_shoup_lazy(d, w, wp, q);
+}
+
 // R stages in registers on the 2^R words x[] of one thread; the words are
 // rows base + (i << pos) of column col.  Global stage of sub-stage s is
 // s0 + logb - pos - R + s.
@@ -99,7 +111,8 @@ __device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t 
 // with scalar loads into SGPRs.
 typedef const __attribute__((address_space(4))) uint64_t* ConstTw;
 
-template <int R, bool INV, bool LAZY, bool COLFAST, bool UTW = false>
+// KDONE: stages of this pass already done (bound of the lazy inverse).
+template <int R, bool INV, bool LAZY, bool COLFAST, bool UTW = false, int KDONE = 0>
 __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int pos, int col, int logb, uint32_t tile,
                                            uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
   constexpr int E = 1 << R;
@@ -123,7 +136,8 @@ __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int 
       }
 #pragma unroll
       for (int m = 0; m < half; ++m) {
-        if (INV) gs_butterfly(x[i0 + m], x[i0 + m + half], w, wp, q);
+        if (INV && LAZY) gs_butterfly_lazy(x[i0 + m], x[i0 + m + half], w, wp, q, (4 * q) << (KDONE + ss));
+        else if (INV) gs_butterfly(x[i0 + m], x[i0 + m + half], w, wp, q);
         else ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w, wp, q);
       }
     }
@@ -216,8 +230,12 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
     uint64_t x[1 << R2];
 #pragma unroll
     for (int i = 0; i < (1 << R2); ++i) x[i] = lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)];
-    round_regs<R2, INV, LAZY, COLFAST, COLFAST && INV>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
-    if (fin.mode == 1) {
+    round_regs<R2, INV, LAZY, COLFAST, COLFAST && INV, R1>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
+    if (INV && LAZY && fin.mode != 2) {
+      // lazy inverse: words below 2^10 q, reduced once (the next pass, or the caller, takes them below q)
+#pragma unroll
+      for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);
+    } else if (fin.mode == 1) {
       if (INV) {
 #pragma unroll
         for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_4q(x[i], q);
@@ -262,7 +280,7 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
 template <int RA, int RB, bool INV, bool COLFAST, int LOGN, class IO>
 __device__ __forceinline__ void run_pass(const IO& io, uint64_t* lds, uint32_t tile, int log_n,
                                          const uint64_t* tw, uint64_t q, const Finish& fin) {
-  if (!INV && q < (1ull << 57))
+  if (INV ? q < (1ull << 54) : q < (1ull << 57))
     pass_body<RA, RB, INV, COLFAST, true, LOGN>(io, lds, tile, log_n, tw, q, fin);
   else
     pass_body<RA, RB, INV, COLFAST, false, LOGN>(io, lds, tile, log_n, tw, q, fin);

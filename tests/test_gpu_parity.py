@@ -425,6 +425,39 @@ def test_ctmatvec_trivial_diagonals_equal_ptmatvec(lib, orc, c3small):
     assert np.array_equal(to_host(y1), to_host(y2))
 
 
+def test_matvec_errors(lib, orc, c3small):
+    """Both BSGS products reject bad arguments on the host, before any launch."""
+    ctx, P = c3small
+    x = empty_dev((1, 2, 24, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    pd = empty_dev((1, 1, 2, 2, 24, P.N))
+    cd = empty_dev((1, 1, 2, 2, 2, 24, P.N))
+    y = empty_dev((1, 2, 24, P.N))
+    g5, g25 = P.galois(1), P.galois(2)
+    cases = [  # (n_in, level, baby g, giant g, baby keys, flags, code)
+        (1, 24, [g5], [g25], [k], 0, lib.CKKS_ERANGE),
+        (1, 0, [g5], [g25], [k], 0, lib.CKKS_ERANGE),
+        (1, 23, [g5], [g25], [k], 4, lib.CKKS_EINVAL),
+        (1, 23, [6], [g25], [k], 0, lib.CKKS_EINVAL),
+        (1, 23, [g5], [g25], [None], 0, lib.CKKS_EINVAL),
+        (0, 23, [g5], [g25], [k], 0, lib.CKKS_EINVAL),
+    ]
+    for n_in, level, gb, gg, kb, flags, code in cases:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_ptmatvec(ctx, x, n_in, pd, 1, 2, 2, gb, kb, gg, [k], y, level, flags)
+        assert e.value.code == code
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_ctmatvec(ctx, x, n_in, cd, 1, 2, 2, k, gb, kb, gg, [k], y, level, flags)
+        assert e.value.code == code
+    for bad in (pd.view(-1)[1:],):
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_ptmatvec(ctx, x, 1, bad, 1, 2, 2, [g5], [k], [g25], [k], y, 23)
+        assert e.value.code == lib.CKKS_EINVAL
+    with pytest.raises(lib.CKKSError) as e:
+        lib.ckks_ctmatvec(ctx, x, 1, cd, 1, 2, 2, k.view(-1)[1:], [g5], [k], [g25], [k], y, 23)
+    assert e.value.code == lib.CKKS_EINVAL
+
+
 def test_repeatable(lib, orc, c3small):
     """Same call twice gives identical words (no races between tiles)."""
     ctx, P = c3small
