@@ -458,6 +458,21 @@ def test_matvec_errors(lib, orc, c3small):
     assert e.value.code == lib.CKKS_EINVAL
 
 
+def test_empty_batches(lib, orc, c3small):
+    """Batch 0 is a no-op for every batched call: no error, output untouched."""
+    ctx, P = c3small
+    torch = torch_cuda()
+    x = empty_dev((1, 2, 24, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    y = torch.full((1, 2, 24, P.N), 7, dtype=torch.int64, device="cuda")
+    lib.ckks_rotate(ctx, x, y, 0, 23, [], [])
+    lib.ckks_rescale(ctx, x, y, 0, 23)
+    lib.ckks_mul_relin_rescale(ctx, x, x, k, y, 0, 23)
+    lib.ckks_poly_eval(ctx, x, 0, 23, 2.0 ** 54, [0.5, 1.0], k, y)
+    torch.cuda.synchronize()
+    assert bool((y == 7).all())
+
+
 def test_repeatable(lib, orc, c3small):
     """Same call twice gives identical words (no races between tiles)."""
     ctx, P = c3small
