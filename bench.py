@@ -92,6 +92,23 @@ def copy_probe(torch):
     del a, b
 
 
+def copy_bandwidth(torch, reps=10):
+    """Measured device-copy rate (bytes read + written per second) of 1 GiB."""
+    a = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * (1 << 30) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
     """The CPU oracle on a bounded sample of the batch (same words)."""
     import oracle
@@ -227,6 +244,11 @@ def main():
     workloads = None
     if not args.no_workloads:
         workloads = workload_bench(lib, S, torch, ctx, q, p, stream)
+        workloads.update(c1_bench(lib, S, torch, np, stream))
+    copy_gbps = copy_bandwidth(torch)
+    if ntt:
+        for d in ("fwd", "inv"):
+            ntt[d + "_copy_frac"] = round(ntt[d + "_GBps"] / copy_gbps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -254,6 +276,8 @@ def main():
         "roofline": roof,
         "hbm_roofline_frac": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
         "alu_roofline_frac": round(value * OPS_PER_HROT * lib.OPS_PER_MODMUL / 1e12 / VALU_PEAK_TOPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "hbm_frac_vs_copy": round(value * BYTES_PER_HROT / 1e9 / copy_gbps, 4),
         "ntt": ntt,
         "workloads": workloads,
         "cpu_baseline": cpu,
@@ -346,11 +370,35 @@ def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
     res["note"] = "C4: one ckks_ptmatvec call; C5: ckks_mul_relin_rescale on 48 pairs + 15 accumulate rotations " \
                   "of the 48 products (768 key switches); poly_eval: degree-7 Horner evaluation on 48 ciphertexts " \
                   "at level 23 (6 products each); av: one ckks_ctmatvec call (A x V, 3 inputs, 3 outputs, 576 " \
-                  "ciphertext diagonals at level 12, 24 relinearisations); device-generated uniform words, " \
-                  "%d timed reps" % reps
+                  "ciphertext diagonals at level 12, 24 relinearisations); c1: one ckks_rotate of a C1 " \
+                  "ciphertext (N=2^12) by 1 and by 7, time per rotation over 20 reps; device-generated uniform " \
+                  "words, %d timed reps" % reps
     log("C4 ptmatvec %.2f ms, C5 %.2f ms, poly_eval %.2f ms, A x V %.2f ms"
         % (res["c4_ptmatvec_ms"], res["c5_mul_rotsum_ms"], res["poly_eval_deg7_ms"], res["av_ctmatvec_ms"]))
     return res
+
+
+def c1_bench(lib, S, torch, np, stream, reps=20):
+    """The tiny configuration (N=2^12, 4 x 30-bit + 1 x 60-bit primes, dnum=4):
+    one ciphertext rotated by 1 and by 7 in one call; time per rotation."""
+    cfg = S.CONFIGS["C1"]
+    N = 1 << cfg["log_n"]
+    q = lib.ckks_find_primes(cfg["log_n"], cfg["q_bits"], cfg["L"])
+    p = lib.ckks_find_primes(cfg["log_n"], cfg["p_bits"], cfg["K"])
+    ctx = lib.Context(cfg["log_n"], q, p, cfg["dnum"], device=0)
+    level = cfg["L"] - 1
+    ks = list(cfg["rotations"])
+    ct = uniform_dev(torch, q, N, (1, 2)).expand(len(ks), 2, len(q), N).contiguous()
+    keys = [uniform_dev(torch, q + p, N, (cfg["dnum"], 2)) for _ in ks]
+    gs = [pow(5, k, 2 * N) for k in ks]
+    out = torch.empty_like(ct)
+
+    def run():
+        lib.ckks_rotate(ctx, ct, out, len(ks), level, gs, keys, 0, stream)
+
+    t = timed(torch, stream, run, reps)
+    ctx.close()
+    return {"c1_rotate_us": round(t * 1e3 / len(ks), 2)}
 
 
 def timed(torch, stream, fn, reps):
