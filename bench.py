@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--no-workloads", action="store_true", help="skip the C4 / C5 timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first copy 1 GiB three times (reference for HBM byte counters)")
+    ap.add_argument("--ntt-only", action="store_true",
+                    help="time only the C2 batched NTT and print its figures (for profiling the transform)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -169,6 +171,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+    if args.ntt_only:
+        print(json.dumps({"ntt": ntt_bench(lib, S, torch, np, args)}), flush=True)
+        return 0
     q = lib.ckks_find_primes(cfg["log_n"], cfg["q_bits"], L)
     p = lib.ckks_find_primes(cfg["log_n"], cfg["p_bits"], K)
     ctx = lib.Context(cfg["log_n"], q, p, dnum, device=0)
