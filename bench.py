@@ -129,14 +129,35 @@ def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
         oracle.rotate_batch(P, level, cts[lo:hi], gs[lo:hi], keys[lo:hi])
         dt += time.perf_counter() - t0
         done += hi - lo
+    cores = oracle.num_threads()
+    # one-thread figure on one rotation of the sample
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    oracle.rotate_batch(P, level, cts[1:2], gs[1:2], keys[1:2])
+    t_one = time.perf_counter() - t0
+    oracle.set_num_threads(cores)
     return {
         "value": k / dt,
         "unit": "HRot/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": "%d rotations of the C3 batch (items 1..%d cycled), same words as the GPU run, "
                   "plain __int128 %% oracle with OpenMP over limbs/coefficients; %.1f s" % (k, B - 1, dt),
+        "value_1thread": round(1.0 / t_one, 4),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    """Host CPU model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

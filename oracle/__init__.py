@@ -103,6 +103,7 @@ def lib():
             "orc_encrypt": (None, [pp, c_int, u64p, u64p, u64p, i64p, u64p]),
             "orc_decrypt_coeff": (None, [pp, c_int, u64p, u64p, u64p]),
             "orc_num_threads": (c_int, []),
+            "orc_set_num_threads": (None, [c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -138,6 +139,11 @@ def _ptr_array(arrs):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP thread count of the oracle's parallel loops."""
+    lib().orc_set_num_threads(int(n))
 
 
 def is_prime(n: int) -> bool:
