@@ -95,6 +95,7 @@ struct RowIPArgs {
   const PrimeConst* prime;
   int log_n, level, next, beta, alpha, L, K;
   int shared_key;  // every item uses the same key: order the grid items first
+  int items_per_wg, n_items;  // a workgroup runs items z*items_per_wg .. (twiddles staged once)
 };
 
 // A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
@@ -198,7 +199,7 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
 
 template <int LOGB, int LOGN, bool LAZY>
 __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, ulonglong2* twl, const PrimeConst& pc,
-                                            int keyl, const GridPos& gp) {
+                                            int keyl, const GridPos& gp, bool stage) {
   typedef IPRounds<LOGB> G;
   const int log_n = LOGN ? LOGN : a.log_n;
   const uint32_t s0 = (uint32_t)logb_col(log_n);
@@ -212,7 +213,7 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
-  ip_stage_twiddles<LOGB>(twl, tw, tile, s0);  // read after the barrier that opens each digit's transform
+  if (stage) ip_stage_twiddles<LOGB>(twl, tw, tile, s0);  // read after the barrier that opens each digit's transform
   // Montgomery products are below 2m, so four of them sum below 8m < 2^63
   uint64_t accb[8], acca[8];
 #pragma unroll
@@ -286,14 +287,19 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     RowIPArgs a) {
   __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
   __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
-  const GridPos gp = a.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
-  const int t = gp.job;
+  const GridPos g0 = a.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
+  const int t = g0.job;
   const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
   const PrimeConst& pc = a.prime[keyl];
-  if (pc.q < (1ull << 57))
-    row_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp);
-  else
-    row_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp);
+  for (int k = 0; k < a.items_per_wg; ++k) {
+    GridPos gp = g0;
+    gp.item = g0.item * a.items_per_wg + k;
+    if (gp.item >= a.n_items) break;
+    if (pc.q < (1ull << 57))
+      row_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp, k == 0);
+    else
+      row_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp, k == 0);
+  }
 }
 
 typedef void (*RowIPFn)(RowIPArgs);
@@ -776,7 +782,13 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     units += (double)next * N * (2.0 * beta + 2);  // products and final reductions
     TraceScope ts(c, s, "ntt_row_ip", units * n_items);
     const int logkc = ip_logkc(lr);
-    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), next, n_items), dim3(1u << (lr - 3 + logkc)), 0, s, ip);
+    // two items per workgroup: the tile's twiddles are staged once for both
+    // (half the twiddle traffic); more items leave too few workgroups
+    const int ipw = 2;
+    ip.items_per_wg = ipw;
+    ip.n_items = n_items;
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), next, (n_items + ipw - 1) / ipw), dim3(1u << (lr - 3 + logkc)), 0,
+                       s, ip);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   return ks_back(c, s, level, n_items, it, A, W, per, add_stride, accum_stride, out_stride, out_comp_limbs);
