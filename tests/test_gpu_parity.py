@@ -425,6 +425,45 @@ def test_ctmatvec_trivial_diagonals_equal_ptmatvec(lib, orc, c3small):
     assert np.array_equal(to_host(y1), to_host(y2))
 
 
+def _fuzz_cases(n=6, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        log_n = int(rng.integers(10, 13))
+        L = int(rng.integers(2, 13))
+        dnum = int(rng.integers(1, min(L, 4) + 1))
+        K = -(-L // dnum)
+        q_bits = int(rng.choice([30, 40, 54]))
+        p_bits = int(rng.choice([q_bits + 6, 60]))
+        level = int(rng.integers(0, L))
+        batch = int(rng.integers(1, 7))
+        ks = [int(k) for k in rng.integers(0, 1 << (log_n - 1), size=batch)]
+        acc = int(rng.integers(0, 2))
+        cases.append((log_n, L, q_bits, K, p_bits, dnum, level, tuple(ks), acc))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fuzz_cases(), ids=lambda c: "logn%d_L%d_q%d_K%d_dnum%d_l%d_b%d" % (
+    c[0], c[1], c[2], c[3], c[5], c[6], len(c[7])))
+def test_rotate_fuzz(lib, orc, case):
+    """Seeded random parameter sets (30/40/54-bit primes, special primes of
+    36 to 60 bits, 1 to 4 digits), levels, offsets and the accumulate flag:
+    words equal the oracle's."""
+    log_n, L, q_bits, K, p_bits, dnum, level, ks, acc = case
+    announce("rotate fuzz %s" % (case,))
+    ctx, P = make_pair(lib, orc, log_n, L, q_bits, K, p_bits, dnum)
+    B = len(ks)
+    cts = S.uniform_limbs(S.stream(log_n * 100 + L, "gpu/fuzz/ct"), P.q[: level + 1], P.N, lead=(B, 2))
+    gs = [P.galois(k) for k in ks]
+    keys = [S.uniform_limbs(S.stream(b, "gpu/fuzz/k"), P.mods, P.N, lead=(P.dnum, 2)) for b in range(B)]
+    out = empty_dev(cts.shape)
+    flags = lib.CKKS_ROT_ACCUMULATE if acc else 0
+    lib.ckks_rotate(ctx, to_dev(cts), out, B, level, gs, [to_dev(k) for k in keys], flags)
+    ref = orc.rotate_batch(P, level, cts, gs, keys, orc.ROT_ACCUMULATE if acc else 0)
+    assert np.array_equal(to_host(out), ref)
+    ctx.close()
+
+
 def test_matvec_errors(lib, orc, c3small):
     """Both BSGS products reject bad arguments on the host, before any launch."""
     ctx, P = c3small
