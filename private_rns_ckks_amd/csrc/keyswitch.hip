@@ -4,13 +4,14 @@
 // Per batch item, at level l (nq = l+1 ciphertext limbs, K special limbs,
 // beta digits):
 //   A  inverse row pass of the input polynomial; when rotating, the load
-//      gathers tau_g(c1) (NTT form) and also writes it out for step E
+//      gathers tau_g(c1) (NTT form)
 //   B  inverse column pass; its final multiply uses [qhat_i^-1 N^-1]_{q_i},
 //      so it produces the ModUp inputs y_i directly
 //   C  ModUp conversion sum_i y_i [qhat_i]_{m_t} mod m_t to every target limb
 //      t of every digit, then the forward column pass of those limbs
 //   D  forward row pass of the converted limbs fused with the inner product
-//      against the key digits (digit limbs read the NTT-form input)
+//      against the key digits (limbs inside their own digit read the
+//      NTT-form input, through tau_g when rotating)
 //   F  inverse NTT of the special limbs of both accumulators, final multiply
 //      by [phat_k^-1 N^-1]_{p_k}: the ModDown inputs y_k
 //   H  ModDown conversion sum_k y_k [1/p_k]_{q_i} - #{k: y_k > (p_k-1)/2}
@@ -30,27 +31,23 @@ namespace {
 using namespace nttc;
 
 // ---------------------------------------------------------------------------
-// A: inverse row pass with optional automorphism gather and side output
+// A: inverse row pass with optional automorphism gather
 struct GatherIO {
   typedef NoOps Ops;
   const uint64_t* src;
-  uint64_t* side;
   uint64_t* dst;
   uint32_t g;
   int log_n;
   __device__ __forceinline__ uint64_t load(uint32_t j) const { return g ? src[automorph_src(j, g, log_n)] : src[j]; }
-  __device__ __forceinline__ void after_load(uint32_t j, uint64_t v) const {
-    if (side) side[j] = v;
-  }
+  __device__ __forceinline__ void after_load(uint32_t, uint64_t) const {}
   __device__ __forceinline__ Ops fetch(uint32_t) const { return Ops(); }
   __device__ __forceinline__ void store(uint32_t j, uint64_t v, const Ops&) const { dst[j] = v; }
 };
 
 struct GatherArgs {
   const uint64_t* src;  // item b: src + b*src_bstride, limb i at + i*N
-  uint64_t* side;       // gathered copy (NTT form) or NULL
   uint64_t* dst;
-  uint64_t src_bstride, side_bstride, dst_bstride;
+  uint64_t src_bstride, dst_bstride;
   const uint64_t* tw;
   const PrimeConst* prime;
   uint32_t g[kMaxChunk];
@@ -66,7 +63,6 @@ __global__ __launch_bounds__(kThreads) void intt_row_gather_kernel(GatherArgs a)
   const uint64_t off = (uint64_t)limb << a.log_n;
   GatherIO io;
   io.src = a.src + item * a.src_bstride + off;
-  io.side = a.side ? a.side + item * a.side_bstride + off : nullptr;
   io.dst = a.dst + item * a.dst_bstride + off;
   io.g = a.g[item];
   io.log_n = a.log_n;
@@ -94,6 +90,7 @@ struct RowIPArgs {
   const uint64_t* tw;  // forward twiddles
   const PrimeConst* prime;
   int log_n, level, next, beta, alpha, L, K;
+  uint32_t g[kMaxChunk];  // item b's input limbs are read through tau_g (0: as they are)
   int shared_key;  // every item uses the same key: order the grid items first
   int items_per_wg, n_items;  // a workgroup runs items z*items_per_wg .. (twiddles staged once)
 };
@@ -221,14 +218,20 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
   for (int j = 0; j < a.beta; ++j) {
     const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
     uint64_t x[8];
-    if (in_digit) {  // NTT-form input limb, in [0, q)
-      const ulonglong2* src =
-          reinterpret_cast<const ulonglong2*>(a.T + item * a.T_bstride + ((uint64_t)t << log_n) + w0);
+    if (in_digit) {  // NTT-form input limb, in [0, q); a rotation gathers tau_g of it here
+      const uint64_t* limb = a.T + item * a.T_bstride + ((uint64_t)t << log_n);
+      const uint32_t g = a.g[item];
+      if (g) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const ulonglong2 v = src[i];
-        x[2 * i] = v.x;
-        x[2 * i + 1] = v.y;
+        for (int i = 0; i < 8; ++i) x[i] = limb[automorph_src(w0 + i, g, log_n)];
+      } else {
+        const ulonglong2* src = reinterpret_cast<const ulonglong2*>(limb + w0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const ulonglong2 v = src[i];
+          x[2 * i] = v.x;
+          x[2 * i + 1] = v.y;
+        }
       }
     } else {  // forward row pass of the converted limb; outputs stay lazy (< 65q, or < 8q)
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
 // ---------------------------------------------------------------------------
 size_t ws_words(const Ctx* c, int level) {
   const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
-  return n * (nq /*T*/ + nq /*Y*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
+  return n * (nq /*Y*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
 }
 
 // Steps F to I for n_items accumulators A (item i at A + i*per, [2][next][N]
@@ -575,7 +578,6 @@ int ks_decompose(Ctx* c, hipStream_t s, int level, int n_in, const uint64_t* c1,
     memset(&ga, 0, sizeof(ga));
     ga.src = c1;
     ga.src_bstride = c1_stride;
-    ga.side = nullptr;
     ga.dst = Y;
     ga.dst_bstride = dec_stride;
     ga.tw = c->d_tw_inv;
@@ -675,22 +677,18 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
   const int log_n = (int)c->log_n;
   const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
   const uint64_t per = ws_words(c, level);
-  uint64_t* T = ws;
-  uint64_t* Y = T + (uint64_t)nq * N;
+  uint64_t* Y = ws;
   uint64_t* E = Y + (uint64_t)nq * N;
   uint64_t* A = E + (uint64_t)beta * next * N;
   uint64_t* W = A + (uint64_t)2 * next * N;
   const int lr = logb_row(log_n), lc = logb_col(log_n);
   int rc;
-  const bool rot = it[0].g != 0;
 
   // A: inverse row pass (gather tau_g(c1) when rotating)
   {
     GatherArgs ga;
     ga.src = it[0].d;
     ga.src_bstride = d_stride;
-    ga.side = rot ? T : nullptr;
-    ga.side_bstride = per;
     ga.dst = Y;
     ga.dst_bstride = per;
     ga.tw = c->d_tw_inv;
@@ -703,8 +701,8 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_items), dim3(kThreads), 0, s, ga);
     CKKS_HIP_CHECK(hipGetLastError());
   }
-  const uint64_t* Tsrc = rot ? T : it[0].d;
-  const uint64_t T_stride = rot ? per : d_stride;
+  const uint64_t* Tsrc = it[0].d;
+  const uint64_t T_stride = d_stride;
   // B: inverse column pass, times [qhat_i^-1 N^-1]: the ModUp inputs y_i
   {
     NttJobs jobs;
@@ -756,6 +754,7 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     ip.E_bstride = per;
     ip.T = Tsrc;
     ip.T_bstride = T_stride;
+    for (int i = 0; i < n_items; ++i) ip.g[i] = it[i].g;
     ip.acc = A;
     ip.acc_bstride = per;
     ip.shared_key = 1;
