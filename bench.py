@@ -173,6 +173,9 @@ def main():
                     help="first copy 1 GiB three times (reference for HBM byte counters)")
     ap.add_argument("--ntt-only", action="store_true",
                     help="time only the C2 batched NTT and print its figures (for profiling the transform)")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure the device calibration probes (instruction and modular-primitive rates, copy "
+                         "rate by size) and print them as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -192,6 +195,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+    if args.probe:
+        print(json.dumps({"probe": calibration(lib, copy_sizes_mib=PROBE_COPY_MIB)}), flush=True)
+        return 0
     if args.ntt_only:
         print(json.dumps({"ntt": ntt_bench(lib, S, torch, np, args)}), flush=True)
         return 0
@@ -311,6 +317,25 @@ def main():
     print(json.dumps(out), flush=True)
     ctx.close()
     return 0
+
+
+PROBE_COPY_MIB = (16, 32, 64, 128, 192, 256, 384, 512, 1024, 2048)
+
+
+def calibration(lib, copy_sizes_mib=(1024,)):
+    """Measured device ceilings (include/ckks_probe.h): every ALU probe in
+    lane-operations per second, and the copy rate (bytes read + written per
+    second) at each size in MiB."""
+    out = {}
+    for name in lib.ckks_probe_list():
+        if name == "copy":
+            continue
+        rate, _ = lib.ckks_probe_rate(name)
+        out[name] = round(rate / 1e12, 4)
+    out["unit"] = "T lane-ops/s"
+    out["copy_GBps"] = {str(m): round(lib.ckks_probe_rate("copy", copy_bytes=m << 20)[0] / 1e9, 1)
+                        for m in copy_sizes_mib}
+    return out
 
 
 def uniform_dev(torch, moduli, N, lead):

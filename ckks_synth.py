@@ -21,6 +21,7 @@ import numpy as np
 __all__ = [
     "stream",
     "uniform_limbs",
+    "top_limbs",
     "ternary_secret",
     "rounded_gaussian",
     "uniform_slots",
@@ -41,6 +42,16 @@ def uniform_limbs(rng: np.random.Generator, moduli, n: int, lead=()) -> np.ndarr
     out = np.empty(lead + (len(moduli), n), dtype=np.uint64)
     for t, m in enumerate(moduli):
         out[..., t, :] = rng.integers(0, int(m), size=lead + (n,), dtype=np.uint64)
+    return out
+
+
+def top_limbs(rng: np.random.Generator, moduli, n: int, lead=(), span: int = 1 << 16) -> np.ndarray:
+    """Like uniform_limbs, but every word of limb t lies in [moduli[t] - span, moduli[t]): the top of
+    the residue range, where lazy (partially reduced) intermediate values come closest to overflowing."""
+    lead = tuple(lead)
+    out = np.empty(lead + (len(moduli), n), dtype=np.uint64)
+    for t, m in enumerate(moduli):
+        out[..., t, :] = np.uint64(int(m) - 1) - rng.integers(0, min(span, int(m)), size=lead + (n,), dtype=np.uint64)
     return out
 
 

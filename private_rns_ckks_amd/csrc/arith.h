@@ -62,6 +62,35 @@ __device__ __forceinline__ uint64_t mul_shoup_lazy(uint64_t a, uint64_t w, uint6
 
 __device__ __forceinline__ uint64_t reduce_2q(uint64_t a, uint64_t q) { return a >= q ? a - q : a; }
 
+// The two halves of a 64-bit word as opaque 32-bit values.  In some kernels
+// the compiler folds the partial products of mul_shoup_lazy back into a
+// 64x64-bit multiply and lowers that as a longer multiply-add chain (about
+// twice the instructions of the split form); taking the halves through an
+// empty asm statement keeps the split form.  No instruction is emitted.
+__device__ __forceinline__ void split_opaque(uint64_t a, uint32_t& lo, uint32_t& hi) {
+  lo = (uint32_t)a;
+  hi = (uint32_t)(a >> 32);
+  asm("" : "+v"(lo), "+v"(hi));
+}
+
+// mul_shoup_lazy with both multiplicands split opaquely (same result).
+__device__ __forceinline__ uint64_t mul_shoup_lazy_split(uint64_t a, uint64_t w, uint64_t wp, uint64_t q) {
+  uint32_t a0, a1;
+  split_opaque(a, a0, a1);
+  const uint32_t p0 = (uint32_t)wp, p1 = (uint32_t)(wp >> 32);
+  const uint64_t s = (uint64_t)__umulhi(a0, p1) + (uint64_t)__umulhi(a1, p0);
+  const uint64_t qh = mad64(a1, p1, s);
+  const uint64_t nq = 0 - q;
+  uint32_t q0, q1;
+  split_opaque(qh, q0, q1);
+  const uint32_t w0 = (uint32_t)w, w1 = (uint32_t)(w >> 32);
+  const uint32_t n0 = (uint32_t)nq, n1 = (uint32_t)(nq >> 32);
+  uint64_t r = mad64(a0, w0, 0);
+  r = mad64(q0, n0, r);
+  const uint32_t h = (uint32_t)(r >> 32) + a0 * w1 + a1 * w0 + q0 * n1 + q1 * n0;
+  return ((uint64_t)h << 32) | (uint32_t)r;
+}
+
 // [0, 4q) -> [0, q)
 __device__ __forceinline__ uint64_t reduce_4q(uint64_t a, uint64_t q) {
   a = a >= 2 * q ? a - 2 * q : a;
@@ -99,9 +128,12 @@ __device__ __forceinline__ uint64_t reduce128(U128 x, uint64_t q, uint64_t r64, 
   return reduce_2q(s, q);
 }
 
-// Montgomery product a*b*2^-64 mod m in [0, 2m) for a, b < m < 2^62, m odd,
-// mp = -m^-1 mod 2^64.  P + u*m with u = lo(P)*mp is divisible by 2^64 and
-// its low words cancel, so the carry out of the low half is (lo(P) != 0).
+// Montgomery product a*b*2^-64 mod m for odd m < 2^63, mp = -m^-1 mod 2^64.
+// P + u*m with u = lo(P)*mp is divisible by 2^64 and its low words cancel,
+// so the carry out of the low half is (lo(P) != 0).  The result is below
+// a*b/2^64 + m, so it lies in [0, 2m) whenever b < m, for ANY 64-bit a (the
+// key-switch inner product multiplies lazy NTT outputs, up to 70q, by
+// canonical key words).
 __device__ __forceinline__ uint64_t mont_mul_lazy(uint64_t a, uint64_t b, uint64_t m, uint64_t mp) {
   const uint64_t lo = a * b;
   const uint64_t hi = mulhi64(a, b);

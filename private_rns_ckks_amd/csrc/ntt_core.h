@@ -87,7 +87,7 @@ __device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t 
   const uint64_t s = x + y;
   const uint64_t d = x + four_q - y;
   x = s >= four_q ? s - four_q : s;
-  y = mul_shoup_lazy(d, w, wp, q);
+  y = mul_shoup_lazy_split(d, w, wp, q);
 }
 
 // Gentleman-Sande without reducing the sum, for q < 2^54: with every word of
@@ -99,7 +99,7 @@ __device__ __forceinline__ void gs_butterfly_lazy(uint64_t& x, uint64_t& y, uint
   const uint64_t s = x + y;
   const uint64_t d = x + m - y;
   x = s;
-  y = mul_shoup_lazy(d, w, wp, q);
+  y = mul_shoup_lazy_split(d, w, wp, q);
 }
 
 // R stages in registers on the 2^R words x[] of one thread; the words are

@@ -330,6 +330,18 @@ using namespace ckks;
 // device buffers are read and written with 16-byte vector accesses
 static bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
 
+// True when the word ranges [a, a + a_words) and [b, b + b_words) share a
+// byte.  Outputs are written by some workgroups while other workgroups still
+// read (and gather) the inputs, so an output that overlaps an input or a key
+// would race; such calls are rejected before any launch.
+static bool overlap(const void* a, uint64_t a_words, const void* b, uint64_t b_words) {
+  if (!a || !b || !a_words || !b_words) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + b_words * 8 && b0 < a0 + a_words * 8;
+}
+#define REJECT_OVERLAP(a, an, b, bn, what) \
+  if (overlap((a), (an), (b), (bn))) return set_error(CKKS_EINVAL, "output overlaps " what)
+
 #define CTX_OR_FAIL(ctx)                                             \
   if (!(ctx)) return set_error(CKKS_EINVAL, "ctx is NULL");         \
   if (hipSetDevice((ctx)->device) != hipSuccess) return set_error(CKKS_EHIP, "hipSetDevice failed")
@@ -366,6 +378,7 @@ int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npo
   if (domain != 0 && domain != 1) return set_error(CKKS_EINVAL, "domain must be 0 (NTT) or 1 (coefficient)");
   if (npoly == 0) return CKKS_OK;
   const uint64_t pstride = (uint64_t)(level + 1) * ctx->N;
+  REJECT_OVERLAP(d_out, pstride * npoly, d_in, pstride * npoly, "the input");
   if (domain == 0) return launch_automorph_ntt(ctx, stream, d_in, d_out, npoly, level + 1, pstride, galois_elt);
   return launch_automorph_coeff(ctx, stream, d_in, d_out, npoly, level + 1, pstride,
                                 inv_mod_2n(galois_elt, 2 * ctx->N));
@@ -380,6 +393,9 @@ int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk,
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (ctx->K == 0) return set_error(CKKS_EPARAM, "key switching needs special primes");
+  const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * ctx->N;
+  REJECT_OVERLAP(d_out, 2ull * (level + 1) * ctx->N, d_poly, (uint64_t)(level + 1) * ctx->N, "the input");
+  REJECT_OVERLAP(d_out, 2ull * (level + 1) * ctx->N, d_evk, key_words, "the key");
   if ((rc = ensure_workspace(ctx, ks_ws_words(ctx, level)))) return rc;
   KSItem it;
   memset(&it, 0, sizeof(it));
@@ -405,6 +421,11 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
   if (misaligned(d_ct_in) || misaligned(d_ct_out))
     return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
   if (batch > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
+  const uint64_t ct_words = 2ull * (level + 1) * ctx->N * batch;
+  const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * ctx->N;
+  REJECT_OVERLAP(d_ct_out, ct_words, d_ct_in, ct_words, "the input");
+  for (int b = 0; b < batch; ++b)
+    if (galois_elts[b] != 1) REJECT_OVERLAP(d_ct_out, ct_words, d_evks[b], key_words, "a key");
   return rotate_batch(ctx, stream, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
                       flags);
 }
@@ -426,6 +447,10 @@ int ckks_rotate_hoisted(ckks_ctx* ctx, const uint64_t* d_ct_in, int n_in, int le
   }
   if (n_rot > 0 && ctx->K == 0) return set_error(CKKS_EPARAM, "rotation needs special primes");
   const uint64_t ct = 2ull * (level + 1) * ctx->N;
+  const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * ctx->N;
+  REJECT_OVERLAP(d_ct_out, ct * n_in * n_rot, d_ct_in, ct * n_in, "the input");
+  for (int r = 0; r < n_rot; ++r)
+    if (galois_elts[r] != 1) REJECT_OVERLAP(d_ct_out, ct * n_in * n_rot, d_evks[r], key_words, "a key");
   return rotate_hoisted(ctx, stream, d_ct_in, ct, n_in, level, n_rot, galois_elts, d_evks, d_ct_out, n_rot * ct, ct);
 }
 
@@ -436,6 +461,7 @@ int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch
   int rc = check_level(ctx, level);
   if (rc) return rc;
   if (level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
+  REJECT_OVERLAP(d_out, 2ull * level * ctx->N * batch, d_in, 2ull * (level + 1) * ctx->N * batch, "the input");
   const uint64_t per = (uint64_t)ctx->N * (2 + 2 * level);
   if ((rc = ensure_workspace(ctx, per * std::min(batch, kMaxChunk)))) return rc;
   return rescale_batch(ctx, stream, d_in, 2ull * (level + 1) * ctx->N, d_out, 2ull * level * ctx->N, batch, level,
@@ -455,6 +481,11 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
   if (rescale && level == 0) return set_error(CKKS_ERANGE, "cannot rescale at level 0");
   if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation needs special primes");
   const uint64_t ct = 2ull * (level + 1) * ctx->N;
+  const uint64_t out_words = 2ull * (rescale ? level : level + 1) * ctx->N * batch;
+  const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * ctx->N;
+  REJECT_OVERLAP(d_out, out_words, d_a, ct * batch, "an input");
+  REJECT_OVERLAP(d_out, out_words, d_b, ct * batch, "an input");
+  REJECT_OVERLAP(d_out, out_words, d_rlk, key_words, "the key");
   return mul_relin_rescale(ctx, stream, d_a, d_b, ct, (uint64_t)(level + 1) * ctx->N, d_rlk, d_out, batch, level,
                            rescale, nullptr);
 }
@@ -499,6 +530,9 @@ int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level,
   if (batch == 0) return CKKS_OK;
   const uint32_t N = ctx->N;
   const uint64_t in_ct = 2ull * (level + 1) * N, ct_l = 2ull * level * N;
+  const uint64_t out_words = 2ull * (level - degree + 1) * N * batch;
+  REJECT_OVERLAP(d_ct_out, out_words, d_ct_in, in_ct * batch, "the input");
+  REJECT_OVERLAP(d_ct_out, out_words, d_rlk, (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * N, "the key");
   // operand buffers: the constant product at level `level` and two accumulators
   if ((rc = ensure_aux(ctx, batch * (in_ct + 2 * ct_l)))) return rc;
   uint64_t* T = ctx->aux;
@@ -573,6 +607,14 @@ int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
   const uint32_t N = ctx->N;
   const int nq = level + 1;
   const uint64_t ct = 2ull * nq * N;
+  {
+    const uint64_t y_words = 2ull * (rescale ? level : nq) * N * n_out;
+    const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * N;
+    REJECT_OVERLAP(d_y, y_words, d_x, ct * n_in, "the input");
+    REJECT_OVERLAP(d_y, y_words, d_diags, (uint64_t)nq * N * n_out * n_in * n1 * n2, "the diagonals");
+    for (int b = 1; b < n1; ++b) REJECT_OVERLAP(d_y, y_words, d_evk_baby[b - 1], key_words, "a key");
+    for (int g = 1; g < n2; ++g) REJECT_OVERLAP(d_y, y_words, d_evk_giant[g - 1], key_words, "a key");
+  }
   // baby [n1][n_in] ciphertexts, inner [n_out][n2], rotated [n_out][n2]: in
   // the context's operand buffer, kept between calls
   const uint64_t n_baby = ct * n1 * n_in, n_inner = ct * n_out * n2;
@@ -692,6 +734,15 @@ int ckks_ctmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* 
   const uint32_t N = ctx->N;
   const int nq = level + 1;
   const uint64_t ct = 2ull * nq * N, t3 = 3ull * nq * N;
+  {
+    const uint64_t y_words = 2ull * (rescale ? level : nq) * N * n_out;
+    const uint64_t key_words = (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * N;
+    REJECT_OVERLAP(d_y, y_words, d_x, ct * n_in, "the input");
+    REJECT_OVERLAP(d_y, y_words, d_diags, ct * n_out * n_in * n1 * n2, "the diagonals");
+    REJECT_OVERLAP(d_y, y_words, d_rlk, key_words, "the key");
+    for (int b = 1; b < n1; ++b) REJECT_OVERLAP(d_y, y_words, d_evk_baby[b - 1], key_words, "a key");
+    for (int g = 1; g < n2; ++g) REJECT_OVERLAP(d_y, y_words, d_evk_giant[g - 1], key_words, "a key");
+  }
   // baby [n1][n_in] ciphertexts, tensor sums [n_out][n2] (three parts),
   // relinearised [n_out][n2], rotated [n_out][n2]: context-owned, kept
   const uint64_t n_baby = ct * n1 * n_in, n_rel = ct * n_out * n2;

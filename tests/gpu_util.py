@@ -33,6 +33,14 @@ def empty_dev(shape):
     return torch.empty(tuple(shape), dtype=torch.int64, device="cuda")
 
 
+def misaligned_dev(shape):
+    """A device tensor of `shape` whose data starts 8 bytes past a 16-byte boundary."""
+    torch = torch_cuda()
+    n = int(np.prod(shape))
+    buf = torch.empty(n + 2, dtype=torch.int64, device="cuda")
+    return buf[1:1 + n].view(tuple(shape))
+
+
 def to_host(t):
     torch = torch_cuda()
     torch.cuda.synchronize()

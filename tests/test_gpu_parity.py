@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import ckks_synth as S
-from gpu_util import announce, config_pair, empty_dev, make_pair, to_dev, to_host, torch_cuda
+from gpu_util import announce, config_pair, empty_dev, make_pair, misaligned_dev, to_dev, to_host, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,28 @@ KS_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("shape", KS_SHAPES, ids=lambda s: "logn%d_L%d_q%d_K%d_dnum%d" % (s[0], s[1], s[2], s[3],
+                                                                                          s[5]))
+def test_rotate_shapes(lib, orc, shape, flags):
+    """Rotations (the automorphism gathered inside the key switch, with and
+    without accumulation) over every key-switch shape: log N 10..15, one-limb
+    and 10-12-limb digits, 10-12 special primes, 59-bit ciphertext primes."""
+    log_n, L, q_bits, K, p_bits, dnum, levels = shape
+    ctx, P = make_pair(lib, orc, log_n, L, q_bits, K, p_bits, dnum)
+    for level in levels:
+        announce("rotate shape %s level=%d flags=%d" % (shape[:6], level, flags))
+        ks = [1, 3, P.N // 2 - 5]
+        cts = S.uniform_limbs(S.stream(level, "gpu/rots/ct"), P.q[: level + 1], P.N, lead=(len(ks), 2))
+        gs = [P.galois(k) for k in ks]
+        keys = [S.uniform_limbs(S.stream(b, "gpu/rots/k"), P.mods, P.N, lead=(P.dnum, 2)) for b in range(len(ks))]
+        out = empty_dev(cts.shape)
+        lib.ckks_rotate(ctx, to_dev(cts), out, len(ks), level, gs, [to_dev(k) for k in keys], flags)
+        ref = orc.rotate_batch(P, level, cts, gs, keys, orc.ROT_ACCUMULATE if flags else 0)
+        assert np.array_equal(to_host(out), ref), level
+    ctx.close()
+
+
 @pytest.mark.parametrize("shape", KS_SHAPES, ids=lambda s: "logn%d_L%d_K%d_dnum%d" % (s[0], s[1], s[3], s[5]))
 def test_keyswitch_shapes(lib, orc, shape):
     log_n, L, q_bits, K, p_bits, dnum, levels = shape
@@ -262,19 +284,84 @@ def test_rotate_hoisted_c1_encrypted(lib, orc, c1):
 def test_rotate_errors(lib, orc, c3small):
     ctx, P = c3small
     x = empty_dev((1, 2, 24, P.N))
+    y = empty_dev((1, 2, 24, P.N))
     k = empty_dev((3, 2, 32, P.N))
     for args, code in [((1, 24, [5], [k]), lib.CKKS_ERANGE), ((1, 23, [6], [k]), lib.CKKS_EINVAL),
-                       ((1, 23, [2 * P.N + 1], [k]), lib.CKKS_EINVAL), ((1, -1, [5], [k]), lib.CKKS_ERANGE),
-                       ((1, 23, [5], [None]), lib.CKKS_EINVAL)]:
+                       ((1, 23, [2 * P.N + 1], [k]), lib.CKKS_EINVAL), ((1, -1, [5], [k]), lib.CKKS_ERANGE)]:
         with pytest.raises(lib.CKKSError) as e:
-            lib.ckks_rotate(ctx, x, x, *args)
+            lib.ckks_rotate(ctx, x, y, *args)
         assert e.value.code == code
     # buffers must be 16-byte aligned; rejected on the host before any launch
-    out = empty_dev((1, 2, 24, P.N))
-    for a_in, keys in [(x, [k.view(-1)[1:]]), (x.view(-1)[1:], [k])]:
+    for a_in, keys in [(x, [misaligned_dev(k.shape)]), (misaligned_dev(x.shape), [k])]:
         with pytest.raises(lib.CKKSError) as e:
-            lib.ckks_rotate(ctx, a_in, out, 1, 23, [5], keys)
+            lib.ckks_rotate(ctx, a_in, y, 1, 23, [5], keys)
         assert e.value.code == lib.CKKS_EINVAL
+    # an output overlapping the input or a key races with the kernels that read them
+    for out, keys in [(x, [k]), (x.view(-1)[P.N:].view(-1)[: 2 * 24 * P.N].view(1, 2, 24, P.N), [k]),
+                      (k.view(-1)[: 2 * 24 * P.N].view(1, 2, 24, P.N), [k])]:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_rotate(ctx, x, out, 1, 23, [5], keys)
+        assert e.value.code == lib.CKKS_EINVAL
+
+
+def test_binding_argument_checks(lib, orc, c3small):
+    """The binding rejects what the library cannot see (list lengths, tensor
+    sizes, devices, a missing key) on the host, before any call."""
+    torch = torch_cuda()
+    ctx, P = c3small
+    x = empty_dev((2, 2, 24, P.N))
+    y = empty_dev((2, 2, 24, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    bad = [
+        lambda: lib.ckks_rotate(ctx, x, y, 2, 23, [5], [k, k]),             # one Galois element for two items
+        lambda: lib.ckks_rotate(ctx, x, y, 2, 23, [5, 25], [k]),            # one key for two items
+        lambda: lib.ckks_rotate(ctx, x, y, 3, 23, [5, 25, 5], [k, k, k]),   # batch larger than the tensors
+        lambda: lib.ckks_rotate(ctx, x, y, 1, 23, [5], [k.view(-1)[: P.N]]),  # short key
+        lambda: lib.ckks_rotate(ctx, x, y, 1, 23, [5], [None]),             # missing key
+        lambda: lib.ckks_rotate(ctx, x.cpu(), y, 1, 23, [5], [k]),          # host tensor
+        lambda: lib.ckks_rotate(ctx, x, y[:, :, :, :8], 1, 23, [5], [k]),   # non-contiguous view
+        lambda: lib.ckks_keyswitch(ctx, x, k, y.view(-1)[: P.N], 23),       # short output
+        lambda: lib.ckks_rescale(ctx, x, y, 3, 23),
+        lambda: lib.ckks_mul_relin_rescale(ctx, x, x.view(-1)[:5], k, y, 1, 23),
+        lambda: lib.ckks_ntt(ctx, x, 5, 0, 24, 0),                          # 5 x 24 limbs in a 4 x 24 tensor
+        lambda: lib.ckks_rotate_hoisted(ctx, x, 1, 23, [5, 25], [k], y),
+        lambda: lib.ckks_ptmatvec(ctx, x, 1, empty_dev((1, 1, 2, 2, 24, P.N)), 1, 2, 2, [5], [], [25], [k], y, 23),
+        lambda: lib.ckks_ctmatvec(ctx, x, 1, empty_dev((1, 1, 2, 2, 24, P.N)), 1, 2, 2, k, [5], [k], [25], [k], y,
+                                  23),  # plaintext-sized diagonals for ciphertext diagonals
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(lib.ArgumentError):
+            f()
+    torch.cuda.synchronize()
+    # a missing key is allowed for the identity element (a copy)
+    lib.ckks_rotate(ctx, x, y, 1, 23, [1], [None])
+
+
+def test_overlap_rejected(lib, orc, c3small):
+    """Every call with an output rejects outputs that overlap its inputs or keys (CKKS_EINVAL)."""
+    ctx, P = c3small
+    x = empty_dev((2, 2, 24, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    ks = [k.view(-1)[: 2 * 24 * P.N * 2].view(2, 2, 24, P.N)]
+    calls = [
+        lambda: lib.ckks_automorph(ctx, x, x, 2, 23, 5, 0),
+        lambda: lib.ckks_keyswitch(ctx, x[0, 1], k, x[0], 23),
+        lambda: lib.ckks_keyswitch(ctx, x[0, 1], k, ks[0][0], 23),
+        lambda: lib.ckks_rotate_hoisted(ctx, x[:1], 1, 23, [5, 25], [k, k], x),
+        lambda: lib.ckks_rescale(ctx, x, x, 2, 23),
+        lambda: lib.ckks_mul_relin_rescale(ctx, x, x, k, x, 1, 23, lib.CKKS_NO_RESCALE),
+        lambda: lib.ckks_mul_relin_rescale(ctx, x[:1], x[1:], k, ks[0][:1], 1, 23, lib.CKKS_NO_RESCALE),
+        lambda: lib.ckks_poly_eval(ctx, x, 1, 23, 2.0 ** 54, [0.5, 1.0], k, x),
+        lambda: lib.ckks_ptmatvec(ctx, x[:1], 1, empty_dev((1, 1, 2, 2, 24, P.N)), 1, 2, 2, [5], [k], [25], [k],
+                                  x[:1], 23, lib.CKKS_NO_RESCALE),
+        lambda: lib.ckks_ctmatvec(ctx, x[:1], 1, empty_dev((1, 1, 2, 2, 2, 24, P.N)), 1, 2, 2, k, [5], [k], [25],
+                                  [k], ks[0][:1], 23, lib.CKKS_NO_RESCALE),
+    ]
+    for i, f in enumerate(calls):
+        with pytest.raises(lib.CKKSError) as e:
+            f()
+        assert e.value.code == lib.CKKS_EINVAL, i
+        assert "overlap" in lib.ckks_last_error(), i
 
 
 # ---------------------------------------------------------------- polynomial evaluation
@@ -425,17 +512,19 @@ def test_ctmatvec_trivial_diagonals_equal_ptmatvec(lib, orc, c3small):
     assert np.array_equal(to_host(y1), to_host(y2))
 
 
-def _fuzz_cases(n=6, seed=2024):
+def _fuzz_cases(n=10, seed=2025):
+    """Random parameter sets; every other case sits at a level in the upper
+    half of its range (at least L/2), where more digits are active."""
     rng = np.random.default_rng(seed)
     cases = []
-    for _ in range(n):
-        log_n = int(rng.integers(10, 13))
-        L = int(rng.integers(2, 13))
+    for i in range(n):
+        log_n = int(rng.integers(10, 14))
+        L = int(rng.integers(2, 17))
         dnum = int(rng.integers(1, min(L, 4) + 1))
         K = -(-L // dnum)
-        q_bits = int(rng.choice([30, 40, 54]))
-        p_bits = int(rng.choice([q_bits + 6, 60]))
-        level = int(rng.integers(0, L))
+        q_bits = int(rng.choice([30, 40, 54, 55, 56, 57, 59]))
+        p_bits = int(rng.choice([min(q_bits + 6, 60), 60]))
+        level = int(rng.integers(L // 2, L)) if i % 2 == 0 else int(rng.integers(0, L))
         batch = int(rng.integers(1, 7))
         ks = [int(k) for k in rng.integers(0, 1 << (log_n - 1), size=batch)]
         acc = int(rng.integers(0, 2))
@@ -446,9 +535,10 @@ def _fuzz_cases(n=6, seed=2024):
 @pytest.mark.parametrize("case", _fuzz_cases(), ids=lambda c: "logn%d_L%d_q%d_K%d_dnum%d_l%d_b%d" % (
     c[0], c[1], c[2], c[3], c[5], c[6], len(c[7])))
 def test_rotate_fuzz(lib, orc, case):
-    """Seeded random parameter sets (30/40/54-bit primes, special primes of
-    36 to 60 bits, 1 to 4 digits), levels, offsets and the accumulate flag:
-    words equal the oracle's."""
+    """Seeded random parameter sets (30- to 59-bit ciphertext primes, special
+    primes of 36 to 60 bits, 1 to 4 digits), levels (half of them in the
+    upper half of the range), offsets and the accumulate flag: words equal the
+    oracle's."""
     log_n, L, q_bits, K, p_bits, dnum, level, ks, acc = case
     announce("rotate fuzz %s" % (case,))
     ctx, P = make_pair(lib, orc, log_n, L, q_bits, K, p_bits, dnum)
@@ -478,7 +568,6 @@ def test_matvec_errors(lib, orc, c3small):
         (1, 0, [g5], [g25], [k], 0, lib.CKKS_ERANGE),
         (1, 23, [g5], [g25], [k], 4, lib.CKKS_EINVAL),
         (1, 23, [6], [g25], [k], 0, lib.CKKS_EINVAL),
-        (1, 23, [g5], [g25], [None], 0, lib.CKKS_EINVAL),
         (0, 23, [g5], [g25], [k], 0, lib.CKKS_EINVAL),
     ]
     for n_in, level, gb, gg, kb, flags, code in cases:
@@ -488,13 +577,15 @@ def test_matvec_errors(lib, orc, c3small):
         with pytest.raises(lib.CKKSError) as e:
             lib.ckks_ctmatvec(ctx, x, n_in, cd, 1, 2, 2, k, gb, kb, gg, [k], y, level, flags)
         assert e.value.code == code
-    for bad in (pd.view(-1)[1:],):
-        with pytest.raises(lib.CKKSError) as e:
-            lib.ckks_ptmatvec(ctx, x, 1, bad, 1, 2, 2, [g5], [k], [g25], [k], y, 23)
-        assert e.value.code == lib.CKKS_EINVAL
     with pytest.raises(lib.CKKSError) as e:
-        lib.ckks_ctmatvec(ctx, x, 1, cd, 1, 2, 2, k.view(-1)[1:], [g5], [k], [g25], [k], y, 23)
+        lib.ckks_ptmatvec(ctx, x, 1, misaligned_dev(pd.shape), 1, 2, 2, [g5], [k], [g25], [k], y, 23)
     assert e.value.code == lib.CKKS_EINVAL
+    with pytest.raises(lib.CKKSError) as e:
+        lib.ckks_ctmatvec(ctx, x, 1, cd, 1, 2, 2, misaligned_dev(k.shape), [g5], [k], [g25], [k], y, 23)
+    assert e.value.code == lib.CKKS_EINVAL
+    for f in (lib.ckks_ptmatvec, ):  # a missing key is caught by the binding
+        with pytest.raises(lib.ArgumentError):
+            f(ctx, x, 1, pd, 1, 2, 2, [g5], [None], [g25], [k], y, 23)
 
 
 def test_empty_batches(lib, orc, c3small):
