@@ -173,6 +173,28 @@ int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk,
 int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
                 const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream);
 
+/* Allocation-free variant of ckks_rotate, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, checks and output words as
+ * ckks_rotate; the difference is where the key-switch workspace comes from
+ * and where the work runs:
+ *   - the workspace is a library-owned device array of
+ *     CKKS_NOALLOC_SCRATCH_BYTES per GPU (held from the first context
+ *     created on that GPU until the process ends), not a buffer grown with
+ *     hipMalloc; the call makes no allocation of any kind (device, host
+ *     pinned, streams or events; kernel tracing is off for it);
+ *   - every kernel runs on `stream` in order, in chunks of as many
+ *     ciphertexts as the scratch holds (no internal streams).
+ * CKKS_ERANGE if one ciphertext's workspace at `level` exceeds the scratch
+ * (at N = 2^16 with 24 + 8 primes and dnum = 3 one ciphertext at level 23
+ * takes 116 MiB).  All calls on one GPU share that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * wrong words.  Nothing in the scratch needs clearing between calls. */
+#define CKKS_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int ckks_rotate_noalloc(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                        const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags,
+                        ckks_stream_t stream);
+
 /* Hoisted rotations (AEGIS page, "Methodology", item 4: several rotations of
  * one ciphertext): each of the n_in ciphertexts of d_ct_in
  * ([n_in][2][level+1][N]) is rotated by every galois_elts[r] (host array,

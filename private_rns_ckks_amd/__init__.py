@@ -30,7 +30,8 @@ CKKS_NO_RESCALE = 2
 EXPORTED = [
     "ckks_find_primes", "ckks_params_validate", "ckks_strerror", "ckks_last_error",
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
-    "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_hoisted", "ckks_rescale",
+    "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_noalloc", "ckks_rotate_hoisted",
+    "ckks_rescale",
     "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_ptmatvec", "ckks_ctmatvec", "ckks_trace_begin",
     "ckks_trace_end", "ckks_probe_list", "ckks_probe_rate",
 ]
@@ -87,6 +88,7 @@ def _load():
         "ckks_automorph": (i, [vp, vp, vp, i, i, u32, i, vp]),
         "ckks_keyswitch": (i, [vp, vp, vp, vp, i, vp]),
         "ckks_rotate": (i, [vp, vp, vp, i, i, u32p, pp, ctypes.c_uint, vp]),
+        "ckks_rotate_noalloc": (i, [vp, vp, vp, i, i, u32p, pp, ctypes.c_uint, vp]),
         "ckks_rotate_hoisted": (i, [vp, vp, i, i, i, u32p, pp, vp, vp]),
         "ckks_rescale": (i, [vp, vp, vp, i, i, vp]),
         "ckks_mul_relin_rescale": (i, [vp, vp, vp, vp, vp, i, i, ctypes.c_uint, vp]),
@@ -280,6 +282,17 @@ def ckks_rotate(ctx, d_ct_in, d_ct_out, batch, level, galois_elts, d_evks, flags
     _check(_lib.ckks_rotate(ctx.handle, _dev(ctx, d_ct_in, n, "d_ct_in"), _dev(ctx, d_ct_out, n, "d_ct_out"), batch,
                             level, _u32_list(galois_elts), _key_list(ctx, d_evks, galois_elts, "d_evks"), flags,
                             _stream(stream)), "ckks_rotate")
+
+
+def ckks_rotate_noalloc(ctx, d_ct_in, d_ct_out, batch, level, galois_elts, d_evks, flags=0, stream=None):
+    """ckks_rotate with the library's fixed scratch: no allocation, everything on `stream`."""
+    _count(galois_elts, batch, "galois_elts")
+    _count(d_evks, batch, "d_evks")
+    n = _w(batch, 2, _lvl(ctx, level), ctx.N)
+    _check(_lib.ckks_rotate_noalloc(ctx.handle, _dev(ctx, d_ct_in, n, "d_ct_in"), _dev(ctx, d_ct_out, n, "d_ct_out"),
+                                    batch, level, _u32_list(galois_elts),
+                                    _key_list(ctx, d_evks, galois_elts, "d_evks"), flags, _stream(stream)),
+           "ckks_rotate_noalloc")
 
 
 def ckks_rotate_hoisted(ctx, d_ct_in, n_in, level, galois_elts, d_evks, d_ct_out, stream=None):

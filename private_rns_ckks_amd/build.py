@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libckks_mi355x.so")
-SOURCES = ["ctx.hip", "ntt.hip", "kernels.hip", "keyswitch.hip", "rescale.hip", "ops.hip", "probe.hip"]
+SOURCES = ["ctx.hip", "ntt.hip", "kernels.hip", "keyswitch.hip", "rescale.hip", "ops.hip", "noalloc.hip", "probe.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

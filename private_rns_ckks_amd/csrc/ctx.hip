@@ -6,6 +6,7 @@
 
 #include "host_math.h"
 #include "internal.h"
+#include "kernels.h"
 
 namespace ckks {
 
@@ -38,7 +39,7 @@ int ensure_workspace(Ctx* c, size_t words) { return grow(c->ws, c->ws_words, wor
 int ensure_aux(Ctx* c, size_t words) { return grow(c->aux, c->aux_words, words, "operand buffer"); }
 
 TraceScope::TraceScope(Ctx* c, hipStream_t s, const char* family, double units)
-    : c_(c), s_(s), on_(!c->trace.name.empty() && c->trace.name == family) {
+    : c_(c), s_(s), on_(!c->no_alloc && !c->trace.name.empty() && c->trace.name == family) {
   if (!on_) return;
   TraceState& t = c->trace;
   while (t.pool.size() < t.used + 2) {
@@ -311,7 +312,7 @@ int ckks_ctx_create(const ckks_params* params, int hip_device, ckks_ctx** out) {
   if (c->K) c->mod.insert(c->mod.end(), params->p, params->p + c->K);
   for (uint32_t i = 0; i < c->L + c->K; ++i)
     c->psi.push_back(params->psi ? params->psi[i] : host::smallest_primitive_root_2n(c->mod[i], (int)c->log_n));
-  if ((rc = build_tables(c)) || (rc = build_rescale(c))) {
+  if ((rc = build_tables(c)) || (rc = build_rescale(c)) || (rc = noalloc_init_device(hip_device))) {
     destroy(c);
     return rc;
   }

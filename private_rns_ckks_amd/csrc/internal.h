@@ -70,6 +70,9 @@ struct Ctx {
   uint64_t* aux = nullptr;        // intermediate operands of composite calls (BSGS matvec)
   size_t aux_words = 0;
   TraceState trace;
+  // Set while an allocation-free call runs: tracing records no events then
+  // (creating them could allocate).
+  bool no_alloc = false;
   // Internal streams (default priority) on which consecutive chunks of a
   // batch run concurrently, forked from and joined back to the caller's
   // stream with events; created on first use.

@@ -115,6 +115,20 @@ int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride
                   uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
                   const uint64_t* add0 = nullptr);
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
+
+// Argument checks of a batched rotation (shared by the entry points that
+// rotate): CKKS_OK or the error code, with the detail set.
+int rotate_check(Ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                 const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags);
+// A checked rotation batch run entirely on stream s with the caller's
+// workspace ws[ws_words] (chunks of as many items as fit, at most
+// kMaxChunk): no internal streams, no allocation.
+int rotate_fixed_ws(Ctx* ctx, hipStream_t s, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                    const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, uint64_t* ws,
+                    uint64_t ws_words);
+// Resolves the device address of the allocation-free scratch array on the
+// current device (once per device); called by context creation.
+int noalloc_init_device(int device);
 int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint64_t* out, int npoly, int nl,
                int ncomp, uint64_t bstride);
 

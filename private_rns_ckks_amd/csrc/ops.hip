@@ -171,14 +171,21 @@ struct RotPiece {
   int step;                    // 1: per-item elements and keys, 0: one for all
 };
 
-static int rotate_pieces(Ctx* c, hipStream_t s, const std::vector<RotPiece>& pieces, int level, unsigned flags) {
+// With fixed_ws the pieces run one after another on s with that workspace
+// (no internal streams, nothing allocated); otherwise on the lanes with the
+// context's workspace, grown as needed.
+static int rotate_pieces(Ctx* c, hipStream_t s, const std::vector<RotPiece>& pieces, int level, unsigned flags,
+                         int chunk, uint64_t* fixed_ws = nullptr) {
   const int nq = level + 1;
   const uint64_t per = ks_ws_words(c, level);
-  const int chunk = g_chunk_default();
-  int rc;
-  const int lanes = (int)std::min<size_t>(pieces.size(), g_lanes_default());
+  int rc = CKKS_OK;
+  const int lanes = fixed_ws ? 1 : (int)std::min<size_t>(pieces.size(), g_lanes_default());
   if (pieces.empty()) return CKKS_OK;
-  if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
+  uint64_t* ws = fixed_ws;
+  if (!fixed_ws) {
+    if ((rc = ensure_workspace(c, per * chunk * lanes)) || (rc = fork_lanes(c, s, lanes))) return rc;
+    ws = c->ws;
+  }
   for (size_t k = 0; k < pieces.size() && rc == CKKS_OK; ++k) {
     const RotPiece& pc = pieces[k];
     KSItem items[kMaxChunk];
@@ -194,7 +201,7 @@ static int rotate_pieces(Ctx* c, hipStream_t s, const std::vector<RotPiece>& pie
       it.out = pc.out + m * pc.stride;
     }
     rc = ks_chunk(c, lane_stream(c, s, lanes, (int)k), level, pc.n, items, pc.stride, pc.stride, pc.stride,
-                  pc.stride, nq, c->ws + per * chunk * (k % lanes));
+                  pc.stride, nq, ws + per * chunk * (k % lanes));
   }
   return join_lanes(c, s, lanes, rc);
 }
@@ -203,10 +210,13 @@ static int rotate_pieces(Ctx* c, hipStream_t s, const std::vector<RotPiece>& pie
 // Items with g == 1 are copied (or doubled when accumulating); the others are
 // key-switched in pieces of consecutive items (at most g_chunk_default()).
 int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint64_t stride, int batch, int level,
-                 const uint32_t* g, const uint64_t* const* evk, unsigned flags) {
+                 const uint32_t* g, const uint64_t* const* evk, unsigned flags, uint64_t* fixed_ws = nullptr,
+                 uint64_t fixed_words = 0) {
   const int nq = level + 1;
   const uint64_t ct_words = 2ull * nq * c->N;
-  const int chunk = g_chunk_default();
+  const int chunk = fixed_ws ? (int)std::min<uint64_t>(kMaxChunk, fixed_words / ks_ws_words(c, level))
+                             : g_chunk_default();
+  if (chunk < 1) return set_error(CKKS_EINTERNAL, "workspace smaller than one item");
   int rc;
   std::vector<int> idx;
   for (int b = 0; b < batch; ++b) {
@@ -229,7 +239,7 @@ int rotate_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t* out, uint6
     pieces.push_back(RotPiece{in + b * stride, out + b * stride, stride, (int)(q - p), g + b, evk + b, 1});
     p = q;
   }
-  return rotate_pieces(c, s, pieces, level, flags);
+  return rotate_pieces(c, s, pieces, level, flags, chunk, fixed_ws);
 }
 
 // Giant steps of a BSGS product: rot[o][g] = Rot_g(inner[o][g]) for g >= 1
@@ -251,7 +261,7 @@ static int rotate_giant_steps(Ctx* c, hipStream_t s, const uint64_t* inner, uint
       pc.step = 0;
       pieces.push_back(pc);
     }
-  return rotate_pieces(c, s, pieces, level, 0);
+  return rotate_pieces(c, s, pieces, level, 0, chunk);
 }
 
 // Hoisted rotations: input c (at in + c*in_stride, [2][l+1][N]) rotated by
@@ -405,9 +415,12 @@ int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk,
   return ks_chunk(ctx, stream, level, 1, &it, 0, 0, 0, 0, level + 1, ctx->ws);
 }
 
-int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
-                const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream) {
-  CTX_OR_FAIL(ctx);
+}  // extern "C"
+
+namespace ckks {
+
+int rotate_check(Ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                 const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags) {
   if (!d_ct_in || !d_ct_out || batch < 0 || (batch > 0 && (!galois_elts || !d_evks)))
     return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
   int rc = check_level(ctx, level);
@@ -426,6 +439,25 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
   REJECT_OVERLAP(d_ct_out, ct_words, d_ct_in, ct_words, "the input");
   for (int b = 0; b < batch; ++b)
     if (galois_elts[b] != 1) REJECT_OVERLAP(d_ct_out, ct_words, d_evks[b], key_words, "a key");
+  return CKKS_OK;
+}
+
+int rotate_fixed_ws(Ctx* ctx, hipStream_t s, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                    const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, uint64_t* ws,
+                    uint64_t ws_words) {
+  return rotate_batch(ctx, s, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
+                      flags, ws, ws_words);
+}
+
+}  // namespace ckks
+
+extern "C" {
+
+int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int batch, int level,
+                const uint32_t* galois_elts, const uint64_t* const* d_evks, unsigned flags, ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  int rc = rotate_check(ctx, d_ct_in, d_ct_out, batch, level, galois_elts, d_evks, flags);
+  if (rc) return rc;
   return rotate_batch(ctx, stream, d_ct_in, d_ct_out, 2ull * (level + 1) * ctx->N, batch, level, galois_elts, d_evks,
                       flags);
 }
