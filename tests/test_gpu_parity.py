@@ -297,10 +297,12 @@ def test_rotate_errors(lib, orc, c3small):
             lib.ckks_rotate(ctx, a_in, y, 1, 23, [5], keys)
         assert e.value.code == lib.CKKS_EINVAL
     # an output overlapping the input or a key races with the kernels that read them
-    for out, keys in [(x, [k]), (x.view(-1)[P.N:].view(-1)[: 2 * 24 * P.N].view(1, 2, 24, P.N), [k]),
-                      (k.view(-1)[: 2 * 24 * P.N].view(1, 2, 24, P.N), [k])]:
+    z = empty_dev((3, 2, 24, P.N))
+    shifted = z.view(-1)[P.N: P.N + 2 * 24 * P.N].view(1, 2, 24, P.N)  # overlaps z[0] by all but one limb
+    for a_in, out, keys in [(x, x, [k]), (z[:1], shifted, [k]),
+                            (x, k.view(-1)[: 2 * 24 * P.N].view(1, 2, 24, P.N), [k])]:
         with pytest.raises(lib.CKKSError) as e:
-            lib.ckks_rotate(ctx, x, out, 1, 23, [5], keys)
+            lib.ckks_rotate(ctx, a_in, out, 1, 23, [5], keys)
         assert e.value.code == lib.CKKS_EINVAL
 
 
