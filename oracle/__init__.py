@@ -90,6 +90,8 @@ def lib():
             "orc_rotate_hoisted": (None, [pp, c_int, u64p, c_int, u32p, ctypes.POINTER(u64p), u64p]),
             "orc_poly_eval": (c_int, [pp, c_int, u64p, c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double), c_int,
                                       u64p, u64p, ctypes.POINTER(ctypes.c_double)]),
+            "orc_poly_eval_tree": (c_int, [pp, c_int, u64p, c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                                           c_int, u64p, u64p, ctypes.POINTER(ctypes.c_double)]),
             "orc_rescale": (c_int, [pp, c_int, u64p, u64p]),
             "orc_tensor": (None, [pp, c_int, u64p, u64p, u64p]),
             "orc_mul_relin_rescale": (c_int, [pp, c_int, u64p, u64p, u64p, u64p, c_int, ctypes.c_uint]),
@@ -357,6 +359,32 @@ def poly_eval(P: Params, level: int, cts, scale: float, coeffs, rlk):
                              ctypes.byref(s))
     if rc == -2:
         raise ValueError("degree must be 1..level")
+    if rc == -3:
+        raise ValueError("a rounded constant reaches 2^62")
+    return out, s.value
+
+
+def tree_depth(degree: int) -> int:
+    """Levels consumed by poly_eval_tree: ceil(log2(degree + 1))."""
+    return degree.bit_length()
+
+
+def poly_eval_tree(P: Params, level: int, cts, scale: float, coeffs, rlk):
+    """p(x) = sum_k coeffs[k] x^k on [B][2][l+1][N] ciphertexts by the
+    power-basis baby-step / giant-step split with scales fixed top-down
+    (depth ceil(log2(d + 1))); returns ([B][2][l - depth + 1][N], output
+    scale = scale)."""
+    cts = _arr(cts)
+    B = cts.shape[0]
+    d = len(coeffs) - 1
+    lo = level - tree_depth(d) + 1 if d >= 1 else 1
+    out = np.empty((B, 2, max(lo, 1), P.N), dtype=np.uint64)
+    c = (ctypes.c_double * len(coeffs))(*[float(v) for v in coeffs])
+    s = ctypes.c_double(0.0)
+    rc = lib().orc_poly_eval_tree(P.ref(), level, _u64(cts), B, float(scale), c, d, _u64(_arr(rlk)), _u64(out),
+                                  ctypes.byref(s))
+    if rc == -2:
+        raise ValueError("degree must be 1..64 and the level at least ceil(log2(degree + 1))")
     if rc == -3:
         raise ValueError("a rounded constant reaches 2^62")
     return out, s.value

@@ -903,6 +903,182 @@ int orc_poly_eval(const orc_params *P, int level, const uint64_t *ct, int batch,
     return 0;
 }
 
+/* ceil(log2 k) for k >= 1 */
+static int ceil_log2(int k)
+{
+    int r = 0;
+    while ((1 << r) < k) r++;
+    return r;
+}
+
+/* Depth-efficient evaluation of p(x) = sum_{k<=d} c[k] x^k (power basis) on
+ * a ciphertext x ([2][l+1][N], NTT form, scale s), in E = ceil(log2(d+1))
+ * levels.  Reading: the pages name polynomial approximations of GELU and the
+ * softmax exponential (AEGIS summary, "Methodology" items 2-3; the Nimbus
+ * post on non-linear layers) and no evaluation scheme; this is the power-basis
+ * baby-step / giant-step split with every scale fixed top-down, so each
+ * addition meets equal levels and scales:
+ *   powers: y_0 = x; y_j = y_{j-1}^2 (multiply, relinearise, rescale) at level
+ *           l - j, scale s_j = s_{j-1}^2 / q_(l-j+1);
+ *   eval(c[0..n-1], target level t, target scale T), n the number of
+ *   coefficients up to the last nonzero one:
+ *     n = 0: zero; n = 1: the trivial ciphertext (round(c0 T), 0);
+ *     n = 2: K = round(c1 T q_(t+1) / s), x's limbs 0..t+1 times K, rescaled
+ *            by q_(t+1), plus round(c0 T);
+ *     n > 2: j = ceil(log2 n), g = 2^(j-1); p = hi(x) * x^g + lo(x) with
+ *            lo = c[0..g-1], hi = c[g..n-1]:
+ *            lo is evaluated at (t, T) (two or more coefficients) or enters
+ *            as the constant round(c0 T) (one);
+ *            hi with one coefficient c: K = round(c T q_(t+1) / s_(j-1)),
+ *            y_(j-1)'s limbs 0..t+1 times K, rescaled by q_(t+1);
+ *            otherwise hi is evaluated at (t+1, T q_(t+1) / s_(j-1)), then
+ *            multiplied by y_(j-1) read at its limbs 0..t+1, relinearised
+ *            and rescaled by q_(t+1);
+ *            the result is that term plus lo.
+ *   The output is eval(c, l - E, s): level l - E, scale s.
+ * Doubles are combined in the order written (left to right); rounding is
+ * llround.  Evaluation order does not change any word (sums mod q). */
+typedef struct {
+    const orc_params *P;
+    const uint64_t *rlk;
+    int level;
+    const uint64_t *y[8]; /* y_j: [2][level-j+1][N] */
+    double s[8];
+    int bad;
+} tree_eval;
+
+/* out += r, both components of [2][nl][N] */
+static void ct_add(uint64_t *out, const uint64_t *r, int nl, const orc_params *P)
+{
+    uint64_t sz = (uint64_t)nl << P->log_n;
+    orc_poly_add(out, r, out, nl, P->log_n, P->mod);
+    orc_poly_add(out + sz, r + sz, out + sz, nl, P->log_n, P->mod);
+}
+
+/* out ([2][t+1][N]) += K * (y restricted to limbs 0..t+1, level ly) rescaled by q_(t+1) */
+static void tree_scaled_add(const tree_eval *E, const uint64_t *y, int ly, int64_t K, int t, uint64_t *out)
+{
+    const orc_params *P = E->P;
+    uint64_t n = (uint64_t)1 << P->log_n, m = (uint64_t)(t + 2) * n;
+    uint64_t *g = malloc(sizeof(uint64_t) * 2 * m), *r = malloc(sizeof(uint64_t) * 2 * (t + 1) * n);
+    memcpy(g, y, sizeof(uint64_t) * m);
+    memcpy(g + m, y + (uint64_t)(ly + 1) * n, sizeof(uint64_t) * m);
+    poly_mul_int(g, t + 2, P->log_n, P->mod, K);
+    poly_mul_int(g + m, t + 2, P->log_n, P->mod, K);
+    orc_rescale(P, t + 1, g, r);
+    ct_add(out, r, t + 1, P);
+    free(g);
+    free(r);
+}
+
+static int tree_trim(const double *c, int n)
+{
+    while (n > 0 && c[n - 1] == 0.0) n--;
+    return n;
+}
+
+/* The constants eval() would round, checked against 2^62 without touching
+ * any ciphertext (same recursion). */
+static void tree_check_node(tree_eval *E, const double *c, int n, int t, double T)
+{
+    const orc_params *P = E->P;
+    if (n == 0) return;
+    if (n <= 2) {
+        if (n == 2) round_checked(c[1] * T * (double)P->mod[t + 1] / E->s[0], &E->bad);
+        round_checked(c[0] * T, &E->bad);
+        return;
+    }
+    int j = ceil_log2(n), g = 1 << (j - 1);
+    int n_lo = tree_trim(c, g), n_hi = n - g;
+    if (n_lo >= 2) tree_check_node(E, c, n_lo, t, T);
+    else if (n_lo == 1) round_checked(c[0] * T, &E->bad);
+    if (n_hi == 1) round_checked(c[g] * T * (double)P->mod[t + 1] / E->s[j - 1], &E->bad);
+    else tree_check_node(E, c + g, n_hi, t + 1, T * (double)P->mod[t + 1] / E->s[j - 1]);
+}
+
+/* out = p(x) at (t, T); out is [2][t+1][N] */
+static void tree_eval_node(tree_eval *E, const double *c, int n, int t, double T, uint64_t *out)
+{
+    const orc_params *P = E->P;
+    uint64_t n_w = (uint64_t)1 << P->log_n, sz = (uint64_t)2 * (t + 1) * n_w;
+    memset(out, 0, sizeof(uint64_t) * sz);
+    if (n == 0) return;
+    if (n <= 2) {
+        if (n == 2) {
+            int64_t K = round_checked(c[1] * T * (double)P->mod[t + 1] / E->s[0], &E->bad);
+            tree_scaled_add(E, E->y[0], E->level, K, t, out);
+        }
+        poly_add_int(out, t + 1, P->log_n, P->mod, round_checked(c[0] * T, &E->bad));
+        return;
+    }
+    int j = ceil_log2(n), g = 1 << (j - 1);
+    int n_lo = tree_trim(c, g), n_hi = n - g; /* c[n-1] != 0: n_hi >= 1 */
+    if (n_lo >= 2) {
+        tree_eval_node(E, c, n_lo, t, T, out);
+    } else if (n_lo == 1) {
+        poly_add_int(out, t + 1, P->log_n, P->mod, round_checked(c[0] * T, &E->bad));
+    }
+    const uint64_t *yg = E->y[j - 1];
+    int ly = E->level - (j - 1);
+    if (n_hi == 1) {
+        int64_t K = round_checked(c[g] * T * (double)P->mod[t + 1] / E->s[j - 1], &E->bad);
+        tree_scaled_add(E, yg, ly, K, t, out);
+        return;
+    }
+    /* hi at (t+1, T q_(t+1) / s_(j-1)), times y_(j-1) at level t+1 */
+    int m = t + 1;
+    uint64_t msz = (uint64_t)(m + 1) * n_w;
+    uint64_t *h = malloc(sizeof(uint64_t) * 2 * msz), *yb = malloc(sizeof(uint64_t) * 2 * msz);
+    uint64_t *prod = malloc(sizeof(uint64_t) * sz);
+    tree_eval_node(E, c + g, n_hi, m, T * (double)P->mod[m] / E->s[j - 1], h);
+    memcpy(yb, yg, sizeof(uint64_t) * msz);
+    memcpy(yb + msz, yg + (uint64_t)(ly + 1) * n_w, sizeof(uint64_t) * msz);
+    orc_mul_relin_rescale(P, m, h, yb, E->rlk, prod, 1, 0);
+    ct_add(out, prod, t + 1, P);
+    free(h);
+    free(yb);
+    free(prod);
+}
+
+/* Returns -2 if degree < 1, degree > 64 or level < ceil(log2(degree+1)),
+ * -3 if a constant reaches 2^62 (nothing written).  out: [batch][2][l-E+1][N]. */
+int orc_poly_eval_tree(const orc_params *P, int level, const uint64_t *ct, int batch, double scale, const double *c,
+                       int degree, const uint64_t *rlk, uint64_t *out, double *out_scale)
+{
+    int d = degree;
+    if (d < 1 || d > 64) return -2;
+    int depth = ceil_log2(d + 1);
+    if (level < depth) return -2;
+    uint64_t n = (uint64_t)1 << P->log_n;
+    int t = level - depth;
+    uint64_t osz = (uint64_t)2 * (t + 1) * n;
+    tree_eval E;
+    memset(&E, 0, sizeof(E));
+    E.P = P;
+    E.rlk = rlk;
+    E.level = level;
+    uint64_t *pw[8] = {0};
+    E.s[0] = scale;
+    for (int j = 1; j < depth; j++) E.s[j] = E.s[j - 1] * E.s[j - 1] / (double)P->mod[level - j + 1];
+    int nc = tree_trim(c, d + 1);
+    tree_check_node(&E, c, nc, t, scale);
+    if (E.bad) return -3;
+    for (int bi = 0; bi < batch; bi++) {
+        const uint64_t *x = ct + (uint64_t)bi * 2 * (level + 1) * n;
+        E.y[0] = x;
+        for (int j = 1; j < depth; j++) {
+            int lp = level - j + 1; /* level of y_(j-1) */
+            if (!pw[j]) pw[j] = malloc(sizeof(uint64_t) * 2 * (level - j + 1) * n);
+            orc_mul_relin_rescale(P, lp, E.y[j - 1], E.y[j - 1], rlk, pw[j], 1, 0);
+            E.y[j] = pw[j];
+        }
+        tree_eval_node(&E, c, nc, t, scale, out + (uint64_t)bi * osz);
+    }
+    for (int j = 1; j < depth; j++) free(pw[j]);
+    *out_scale = scale;
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* Keys, encryption, decryption (host-side set-up and checking)          */
 /* ------------------------------------------------------------------ */

@@ -88,8 +88,34 @@ def test_psi_is_smallest_primitive_2n_th_root(orc, log_n, bits, count):
         assert psi == best
 
 
+# Literal parameter values of the workload recipes, computed independently of
+# the oracle (sympy's primality test over the candidates 1 mod 2N below 2^bits,
+# and the minimum over all odd powers of a primitive 2N-th root from sympy's
+# primitive root): any change to the prime search or the root choice fails here.
+C1_Q = [1073692673, 1073668097, 1073651713, 1073643521]
+C1_P = [1152921504606830593]
+C3_Q = [18014398506729473, 18014398505943041, 18014398496243713, 18014398495457281, 18014398492704769,
+        18014398492311553, 18014398491918337, 18014398487068673, 18014398485495809, 18014398484316161,
+        18014398479204353, 18014398476451841, 18014398472519681, 18014398471864321, 18014398470946817,
+        18014398467407873, 18014398463868929, 18014398462427137, 18014398458888193, 18014398457184257,
+        18014398452203521, 18014398450892801, 18014398446305281, 18014398445387777]
+C3_P = [1152921504606584833, 1152921504598720513, 1152921504597016577, 1152921504595968001, 1152921504592822273,
+        1152921504592429057, 1152921504589938689, 1152921504586530817]
+
+
+def test_c1_literal_primes_and_psi(orc):
+    c = S.CONFIGS["C1"]
+    P = orc.Params.generate(c["log_n"], c["L"], c["q_bits"], c["K"], c["p_bits"], c["dnum"])
+    assert P.q == C1_Q and P.p == C1_P
+    assert P.psi[0] == 236231 and P.psi[P.L] == 116777451583545
+    assert P.galois(1) == 5 and P.galois(7) == 4397
+
+
 def test_c3_appendix_psi_values(orc):
-    # spot values cross-checked by the sympy enumeration above; kept to catch regressions quickly
     c = S.CONFIGS["C3"]
     P = orc.Params.generate(c["log_n"], c["L"], c["q_bits"], c["K"], c["p_bits"], c["dnum"])
+    assert P.q == C3_Q and P.p == C3_P
+    assert P.psi[0] == 197149534992 and P.psi[P.L] == 18043022392882
     assert P.alpha == 8 and P.beta(23) == 3 and P.beta(12) == 2 and P.beta(7) == 1
+    for m in C3_Q[:2] + C3_P[:1]:  # the literal values themselves, independently of the oracle
+        assert sympy.isprime(m) and m % (1 << 17) == 1

@@ -14,8 +14,15 @@ Checks against what the mathematics fixes, never against the oracle itself:
     weight matvec gives the plaintext matvec's words exactly;
   * rotate-and-sum over all power-of-two offsets gives the slot sum in every slot;
   * Horner evaluation of p(x) = sum_k c_k x^k decrypts to p(z) slot-wise
-    (float64 reference) at a scale equal to the primes' size.
+    (float64 reference) at a scale equal to the primes' size;
+  * the baby-step / giant-step evaluation (depth ceil(log2(d + 1))) decrypts
+    to p(z) as well, and fits of exp on [-4, 0] and GELU on [-4, 4] decrypt to
+    within their float64 approximation error of the functions; with primes
+    that are exact in float64, p(x) = x + c returns the input's limbs
+    (rescaling x*q_l by q_l is exact) plus the constant, and p(x) = c a
+    trivial ciphertext; at degree 1 the tree and Horner agree word for word.
 """
+import math
 import numpy as np
 import pytest
 
@@ -321,3 +328,140 @@ def test_poly_eval_rejects_bad_input(orc):
         orc.poly_eval(P, 2, ct[:, :, :3], 2.0 ** 25, [1.0] * 5, rlk)  # degree 4 > level 2
     with pytest.raises(ValueError):
         orc.poly_eval(P, 3, ct, 2.0 ** 25, [0.0, 2.0 ** 40], rlk)     # c * q reaches 2^62
+
+
+def _tree_setup(orc, seed):
+    P = config_params(orc, "C3", log_n=9)
+    s, s_ntt = secret(orc, P, seed, 64)
+    return P, s_ntt, relin_key(orc, P, s_ntt, seed)
+
+
+def _cheb_monomial(f, degree, lo, hi, drop=1e-12):
+    """Monomial coefficients (in x) of f's Chebyshev interpolant on [lo, hi];
+    coefficients below `drop` in magnitude set to zero."""
+    from numpy.polynomial import chebyshev as C, polynomial as Pm
+    p = C.Chebyshev.interpolate(f, degree, domain=[lo, hi]).convert(kind=Pm.Polynomial, domain=[-1, 1],
+                                                                   window=[-1, 1])
+    c = np.array(p.coef, dtype=np.float64)
+    c[np.abs(c) < drop] = 0.0
+    return [float(v) for v in c]
+
+
+def _gelu(x):
+    return 0.5 * x * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+
+
+@pytest.mark.parametrize("coeffs", [
+    [1.0, 1.0, 0.5, 1 / 6, 1 / 24, 1 / 120, 1 / 720, 1 / 5040],   # exp, degree 7 Taylor
+    [0.25, -1.5],                                                  # affine (depth 1)
+    [0.0, 0.5, 0.0, -0.125, 0.0, 0.03],                            # odd, degree 5, zero terms skipped
+    [-1.75, 0.3, 1.9, -0.6],                                       # cubic
+    [0.1 * (-1) ** k / (k + 1) for k in range(17)],                # degree 16: the x^16 giant step
+    [0.3, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, -0.7],                # x^8 alone: one-coefficient high part
+    [0.2 * (k % 3 - 1) for k in range(32)],                        # degree 31, zero runs
+], ids=["exp7", "affine", "odd5", "cubic", "deg16", "x8", "deg31"])
+def test_poly_eval_tree_decrypts_to_polynomial(orc, coeffs):
+    P, s_ntt, rlk = _tree_setup(orc, 10)
+    level = 23
+    z = S.uniform_slots(S.stream(10, "pt/z"), P.N // 2, complex_values=False)
+    scale = 2.0 ** 54
+    ct = encrypt_slots(orc, P, s_ntt, z, scale, level, 10, "pt/ct")
+    out, s_out = orc.poly_eval_tree(P, level, ct[None], scale, coeffs, rlk)
+    d = len(coeffs) - 1
+    depth = int(np.ceil(np.log2(d + 1)))
+    assert orc.tree_depth(d) == depth
+    assert out.shape == (1, 2, level - depth + 1, P.N)
+    assert s_out == scale
+    dec = orc.decrypt(P, level - depth, out[0], s_ntt, s_out)
+    ref = sum(c * z ** k for k, c in enumerate(coeffs))
+    assert np.max(np.abs(dec - ref)) < 2 ** -30
+
+
+def test_poly_eval_tree_exp_on_minus4_0(orc):
+    """Degree-11 fit of exp on [-4, 0] (the input range of the softmax
+    exponential): the decrypted output is within 2^-28 of the float64 fit and
+    within 1e-8 of exp."""
+    P, s_ntt, rlk = _tree_setup(orc, 11)
+    level = 23
+    coeffs = _cheb_monomial(np.exp, 11, -4.0, 0.0)
+    rng = S.stream(11, "exp/z")
+    x = -4.0 * rng.random(P.N // 2)
+    x[:3] = [-4.0, 0.0, -2.0]
+    scale = 2.0 ** 54
+    ct = encrypt_slots(orc, P, s_ntt, x.astype(np.complex128), scale, level, 11, "exp/ct")
+    out, s_out = orc.poly_eval_tree(P, level, ct[None], scale, coeffs, rlk)
+    assert out.shape[2] == level - 4 + 1                          # degree 11: depth 4
+    dec = orc.decrypt(P, level - 4, out[0], s_ntt, s_out).real
+    fit = np.polynomial.polynomial.polyval(x, coeffs)
+    assert np.max(np.abs(dec - fit)) < 2 ** -28
+    assert np.max(np.abs(dec - np.exp(x))) < 1e-8
+
+
+def test_poly_eval_tree_gelu_on_minus4_4(orc):
+    """Degree-15 fit of GELU(4u) for u = x/4 in [-1, 1] (its odd terms above
+    the first are zero and skipped): within 2^-30 of the float64 fit and
+    within 3e-4 of GELU(x) = x Phi(x)."""
+    P, s_ntt, rlk = _tree_setup(orc, 12)
+    level = 23
+    coeffs = _cheb_monomial(lambda u: _gelu(4.0 * u), 15, -1.0, 1.0)
+    # GELU(x) - x/2 = x erf(x / sqrt 2) / 2 is even: the odd terms above the
+    # first are conversion round-off
+    for k in range(3, 16, 2):
+        assert abs(coeffs[k]) < 1e-8
+        coeffs[k] = 0.0
+    rng = S.stream(12, "gelu/x")
+    x = 8.0 * rng.random(P.N // 2) - 4.0
+    x[:3] = [-4.0, 4.0, 0.0]
+    u = x / 4.0
+    scale = 2.0 ** 54
+    ct = encrypt_slots(orc, P, s_ntt, u.astype(np.complex128), scale, level, 12, "gelu/ct")
+    out, s_out = orc.poly_eval_tree(P, level, ct[None], scale, coeffs, rlk)
+    assert out.shape[2] == level - 4 + 1                          # degree 15: depth 4
+    dec = orc.decrypt(P, level - 4, out[0], s_ntt, s_out).real
+    fit = np.polynomial.polynomial.polyval(u, coeffs)
+    assert np.max(np.abs(dec - fit)) < 2 ** -30
+    assert np.max(np.abs(dec - _gelu(x))) < 3e-4
+
+
+def test_poly_eval_tree_exact_identities(orc):
+    """C1 primes (30 bits) are exact in float64, so K_1 = round(1 * s * q_l / s)
+    = q_l and rescaling x * q_l by q_l returns x's lower limbs word for word;
+    p(x) = c alone is the trivial ciphertext (round(c s) mod q_i, 0)."""
+    P = config_params(orc, "C1")
+    s, s_ntt = secret(orc, P, 13, 64)
+    rlk = relin_key(orc, P, s_ntt, 13)
+    level = 3
+    ct = S.uniform_limbs(S.stream(13, "id/ct"), P.q[: level + 1], P.N, lead=(2, 2))
+    scale = 2.0 ** 25
+    q = np.array(P.q[:level], dtype=np.uint64)[:, None]
+    out, _ = orc.poly_eval_tree(P, level, ct, scale, [0.0, 1.0], rlk)
+    assert np.array_equal(out, ct[:, :, :level])
+    out, _ = orc.poly_eval_tree(P, level, ct, scale, [0.75, 1.0], rlk)
+    k = np.uint64(round(0.75 * scale))
+    assert np.array_equal(out[:, 0], (ct[:, 0, :level] + k % q) % q)
+    assert np.array_equal(out[:, 1], ct[:, 1, :level])
+    out, _ = orc.poly_eval_tree(P, level, ct, scale, [-0.5, 0.0], rlk)
+    neg = np.uint64(round(0.5 * scale)) % q
+    assert np.array_equal(out[:, 0], np.broadcast_to((q - neg) % q, out[:, 0].shape))
+    assert not out[:, 1].any()
+
+
+def test_poly_eval_tree_degree1_matches_horner(orc):
+    P, s_ntt, rlk = _tree_setup(orc, 14)
+    ct = S.uniform_limbs(S.stream(14, "d1/ct"), P.q[:6], P.N, lead=(2, 2))
+    a, sa = orc.poly_eval(P, 5, ct, 2.0 ** 54, [0.3, -1.25], rlk)
+    b, sb = orc.poly_eval_tree(P, 5, ct, 2.0 ** 54, [0.3, -1.25], rlk)
+    assert np.array_equal(a, b) and sa == sb
+
+
+def test_poly_eval_tree_rejects_bad_input(orc):
+    P = config_params(orc, "C1")
+    s, s_ntt = secret(orc, P, 1, 64)
+    rlk = relin_key(orc, P, s_ntt, 1)
+    ct = S.uniform_limbs(S.stream(1, "pt/bad"), P.q, P.N, lead=(1, 2))
+    with pytest.raises(ValueError):
+        orc.poly_eval_tree(P, 3, ct, 2.0 ** 25, [1.0] * 10, rlk)         # degree 9: depth 4 > level 3
+    with pytest.raises(ValueError):
+        orc.poly_eval_tree(P, 3, ct, 2.0 ** 25, [1.0] * 66, rlk)         # degree 65
+    with pytest.raises(ValueError):
+        orc.poly_eval_tree(P, 3, ct, 2.0 ** 25, [0.0, 2.0 ** 40], rlk)   # constant reaches 2^62
