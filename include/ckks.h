@@ -128,8 +128,11 @@ typedef struct {
  * stream is bracketed by a HIP event pair on that stream.  Families:
  * "ntt_pass" (plain NTT / inverse NTT passes), the key switch's fused
  * passes "intt_row_gather" (automorphism gather + inverse row pass),
- * "ntt_row_ip" (forward row pass + key inner product) and "ntt_row_combine"
- * (forward row pass + final combination), "automorph", "modup",
+ * "ip_special" (forward row pass + key inner product on the special limbs +
+ * inverse row pass of the accumulators), "comb_ip" (forward row pass + key
+ * inner product on the ciphertext limbs + final combination) and
+ * "ntt_row_combine" (forward row pass + final combination, hoisted
+ * rotations), "automorph", "modup",
  * "moddown_conv", "rescale", "tensor", "ptmac", "ctmac", "add",
  * "const_mul", "ip_gather".  NULL or "" stops
  * tracing.
@@ -140,7 +143,13 @@ int ckks_trace_end(ckks_ctx* ctx, ckks_trace_stats* out);
 
 /* ---- hot path ------------------------------------------------------------ */
 
-/* Negacyclic NTT (inverse = 0) or inverse NTT with the 1/N factor
+/* Source: AEGIS summary (gist.science), "Problem", challenge 2: ciphertexts
+ * live as RNS residue polynomials (one per modulus of the chain) and the
+ * matrix products and non-linear layers run key switching and rotation on
+ * them; the negacyclic NTT per residue polynomial is the transform every one
+ * of those operations is built on (the pages name no transform; standard
+ * full-RNS CKKS).
+ * Negacyclic NTT (inverse = 0) or inverse NTT with the 1/N factor
  * (inverse = 1), in place, on d_data = [npoly][n_limb][N]; limb i of every
  * polynomial uses basis prime limb_begin + i.  Forward maps coefficient form
  * to NTT form (bit-reversed evaluation order), inverse maps back.
@@ -148,13 +157,22 @@ int ckks_trace_end(ckks_ctx* ctx, ckks_trace_stats* out);
 int ckks_ntt(ckks_ctx* ctx, uint64_t* d_data, int npoly, int limb_begin, int n_limb, int inverse,
              ckks_stream_t stream);
 
-/* Galois automorphism X -> X^g on d_in = [npoly][level+1][N] (limbs
+/* Source: AEGIS summary, "Problem", challenge 2 (rotations are frequent in
+ * the matrix products and non-linear layers) and "Methodology", item 4
+ * (rotations by several offsets, reordered); the automorphism X -> X^g is the
+ * slot permutation of a rotation.
+ * Galois automorphism X -> X^g on d_in = [npoly][level+1][N] (limbs
  * q_0..q_level) into d_out (same shape).  domain 0: NTT form (a permutation
  * of words); domain 1: coefficient form (a signed permutation). */
 int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npoly, int level, uint32_t galois_elt,
                    int domain, ckks_stream_t stream);
 
-/* Hybrid key switch of d_poly ([level+1][N], NTT form) with the switch key
+/* Source: AEGIS summary, "Problem", challenge 2 (key switching is needed by
+ * every matrix product and non-linear layer and couples all RNS components)
+ * and "Methodology", item 1 (the components that take part in one key switch
+ * are kept together on one device: the whole switch runs in one place, as
+ * here).
+ * Hybrid key switch of d_poly ([level+1][N], NTT form) with the switch key
  * d_evk ([dnum][2][L+K][N]) into d_out ([2][level+1][N], NTT form):
  * per active digit, ModUp (unsigned fast basis conversion to the other limbs
  * and the special primes), NTT, inner product with the key digit, then
@@ -163,7 +181,11 @@ int ckks_automorph(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int npo
 int ckks_keyswitch(ckks_ctx* ctx, const uint64_t* d_poly, const uint64_t* d_evk, uint64_t* d_out, int level,
                    ckks_stream_t stream);
 
-/* Batched homomorphic rotation: for b < batch, ciphertext b of d_ct_in
+/* Source: AEGIS summary, "Problem", challenge 2 (rotation with key
+ * switching in every matrix product and non-linear layer) and
+ * "Methodology", item 4 (several rotations with different offsets in flight
+ * at once: here a batch, one offset and key per ciphertext).
+ * Batched homomorphic rotation: for b < batch, ciphertext b of d_ct_in
  * ([batch][2][level+1][N]) is mapped by Galois element galois_elts[b]
  * (host array) and key-switched back with the switch key d_evks[b] (host
  * array of device pointers, each [dnum][2][L+K][N], the key for
@@ -187,7 +209,7 @@ int ckks_rotate(ckks_ctx* ctx, const uint64_t* d_ct_in, uint64_t* d_ct_out, int 
  *     ciphertexts as the scratch holds (no internal streams).
  * CKKS_ERANGE if one ciphertext's workspace at `level` exceeds the scratch
  * (at N = 2^16 with 24 + 8 primes and dnum = 3 one ciphertext at level 23
- * takes 116 MiB).  All calls on one GPU share that GPU's scratch: calls that
+ * takes 92 MiB: N x (24 + 3 x 32 + 2 x 8 + 2 x 24) words).  All calls on one GPU share that GPU's scratch: calls that
  * overlap in time on one GPU (other streams, other threads) race and give
  * wrong words.  Nothing in the scratch needs clearing between calls. */
 #define CKKS_NOALLOC_SCRATCH_BYTES (128ull << 20)
@@ -216,7 +238,10 @@ int ckks_rotate_hoisted(ckks_ctx* ctx, const uint64_t* d_ct_in, int n_in, int le
  * CKKS_ERANGE at level 0. */
 int ckks_rescale(ckks_ctx* ctx, const uint64_t* d_in, uint64_t* d_out, int batch, int level, ckks_stream_t stream);
 
-/* Batched ciphertext product: tensor (d0 = a0 b0, d1 = a0 b1 + a1 b0,
+/* Source: AEGIS summary, "Methodology", item 3 (self-attention: the product
+ * Q x K^T of two encrypted operands, followed by a polynomial softmax, which
+ * needs the product relinearised and rescaled).
+ * Batched ciphertext product: tensor (d0 = a0 b0, d1 = a0 b1 + a1 b0,
  * d2 = a1 b1), relinearisation with d_rlk (switch key s^2 -> s):
  * (d0, d1) + KS(d2), then rescale.  d_a, d_b: [batch][2][level+1][N];
  * d_out: [batch][2][level][N], or [batch][2][level+1][N] with
@@ -241,7 +266,43 @@ int ckks_mul_relin_rescale(ckks_ctx* ctx, const uint64_t* d_a, const uint64_t* d
 int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level, double scale, const double* coeffs,
                    int degree, const uint64_t* d_rlk, uint64_t* d_ct_out, double* out_scale, ckks_stream_t stream);
 
-/* Baby-step / giant-step ciphertext x plaintext matrix-vector product.
+/* Source: AEGIS summary, "Methodology", items 2-3 (the nonlinear layers,
+ * GELU and the softmax exponential, evaluated locally as polynomial
+ * approximations) and the Nimbus post on non-linear layers (the exponential's
+ * inputs concentrate on [-4, 0]); neither fixes an evaluation scheme.
+ * Polynomial p(x) = sum_{k<=degree} coeffs[k] x^k (host doubles, power
+ * basis) in E = ceil(log2(degree + 1)) levels (Horner's takes degree), by the
+ * baby-step / giant-step split with every scale fixed top-down:
+ *   powers y_0 = x, y_j = y_(j-1)^2 (multiply, relinearise with d_rlk,
+ *   rescale): level l - j, scale s_j = s_(j-1)^2 / q_(l-j+1);
+ *   eval(c[0..n-1], level t, scale T), n counting up to the last nonzero
+ *   coefficient:
+ *     n <= 1: the trivial ciphertext (llround(c0 T), 0);
+ *     n = 2:  x's limbs 0..t+1 times K = llround(c1 T q_(t+1) / s), rescaled
+ *             by q_(t+1), plus llround(c0 T);
+ *     n > 2:  g = 2^(ceil(log2 n) - 1), p = hi(x) y_j + lo(x) with
+ *             y_j = x^g, lo = c[0..g-1], hi = c[g..n-1]; lo is evaluated at
+ *             (t, T) (or is the constant llround(c0 T)); a one-coefficient hi
+ *             multiplies y_j's limbs 0..t+1 by llround(c T q_(t+1) / s_j) and
+ *             rescales; otherwise hi is evaluated at (t+1, T q_(t+1) / s_j),
+ *             multiplied by y_j at level t+1, relinearised and rescaled;
+ *   output = eval(c, l - E, scale): level l - E, scale `scale`.
+ * Doubles combine left to right as written; zero coefficients cost nothing.
+ * d_ct_in: [batch][2][level+1][N], NTT form; d_ct_out:
+ * [batch][2][level - E + 1][N].  CKKS_ERANGE unless 1 <= degree <= 64 and
+ * level >= E; CKKS_EINVAL when a constant reaches 2^62 (checked before any
+ * work is enqueued).  Needs K > 0.  The powers and intermediates live in a
+ * context-owned buffer grown on demand (growing it synchronises the device);
+ * otherwise the call only enqueues work on `stream`. */
+int ckks_poly_eval_tree(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level, double scale,
+                        const double* coeffs, int degree, const uint64_t* d_rlk, uint64_t* d_ct_out,
+                        double* out_scale, ckks_stream_t stream);
+
+/* Source: AEGIS summary, "Methodology", item 2 (FFN: each device multiplies
+ * its encrypted activations by the weight slices of one output group, locally,
+ * as polynomial products); the diagonal (BSGS) method is the standard way to
+ * run that product on packed slots (Halevi-Shoup 2014).
+ * Baby-step / giant-step ciphertext x plaintext matrix-vector product.
  *   d_x      [n_in][2][level+1][N] input ciphertexts
  *   d_diags  [n_out][n_in][n2][n1][level+1][N] plaintexts (NTT form); entry
  *            (o, c, g, b) is the diagonal for offset n1*g + b, already

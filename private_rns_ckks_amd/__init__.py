@@ -32,17 +32,14 @@ EXPORTED = [
     "ckks_ctx_create", "ckks_ctx_destroy", "ckks_ctx_psi",
     "ckks_ntt", "ckks_automorph", "ckks_keyswitch", "ckks_rotate", "ckks_rotate_noalloc", "ckks_rotate_hoisted",
     "ckks_rescale",
-    "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_ptmatvec", "ckks_ctmatvec", "ckks_trace_begin",
+    "ckks_mul_relin_rescale", "ckks_poly_eval", "ckks_poly_eval_tree", "ckks_ptmatvec", "ckks_ctmatvec", "ckks_trace_begin",
     "ckks_trace_end", "ckks_probe_list", "ckks_probe_rate",
 ]
 
 # Kernel whose launches take the largest share of a rotation batch (by
-# rocprofv3 time): the forward row pass fused with the key inner product.
-DOMINANT_KERNEL = "ntt_row_ip"
-# int32 VALU operations per 64-bit modmul-class operation: the 10 32x32-bit
-# partial products of a 64-bit Shoup (or Barrett) multiplication plus 6 int32
-# adds/subtracts to combine them and apply the quotient.
-OPS_PER_MODMUL = 16
+# rocprofv3 time): the ciphertext-prime inner product fused with the final
+# combination.
+DOMINANT_KERNEL = "comb_ip"
 
 
 class CKKSError(RuntimeError):
@@ -94,6 +91,8 @@ def _load():
         "ckks_mul_relin_rescale": (i, [vp, vp, vp, vp, vp, i, i, ctypes.c_uint, vp]),
         "ckks_poly_eval": (i, [vp, vp, i, i, ctypes.c_double, ctypes.POINTER(ctypes.c_double), i, vp, vp,
                                ctypes.POINTER(ctypes.c_double), vp]),
+        "ckks_poly_eval_tree": (i, [vp, vp, i, i, ctypes.c_double, ctypes.POINTER(ctypes.c_double), i, vp, vp,
+                                    ctypes.POINTER(ctypes.c_double), vp]),
         "ckks_ptmatvec": (i, [vp, vp, i, vp, i, i, i, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
         "ckks_ctmatvec": (i, [vp, vp, i, vp, i, i, i, vp, u32p, pp, u32p, pp, vp, i, ctypes.c_uint, vp]),
         "ckks_trace_begin": (i, [vp, ctypes.c_char_p]),
@@ -335,6 +334,28 @@ def ckks_poly_eval(ctx, d_ct_in, batch, level, scale, coeffs, d_rlk, d_ct_out, s
     return out_scale.value
 
 
+def tree_depth(degree):
+    """Levels ckks_poly_eval_tree consumes: ceil(log2(degree + 1))."""
+    return degree.bit_length()
+
+
+def ckks_poly_eval_tree(ctx, d_ct_in, batch, level, scale, coeffs, d_rlk, d_ct_out, stream=None):
+    """Depth-efficient evaluation of sum_k coeffs[k] x^k (depth
+    ceil(log2(d + 1))); returns the output scale (= scale)."""
+    c = (ctypes.c_double * len(coeffs))(*[float(v) for v in coeffs])
+    degree = len(coeffs) - 1
+    nl = _lvl(ctx, level)
+    n_out = None
+    if nl is not None and 1 <= degree <= 64 and nl > tree_depth(degree):
+        n_out = _w(batch, 2, nl - tree_depth(degree), ctx.N)
+    out_scale = ctypes.c_double(0.0)
+    _check(_lib.ckks_poly_eval_tree(ctx.handle, _dev(ctx, d_ct_in, _w(batch, 2, nl, ctx.N), "d_ct_in"), batch, level,
+                                    float(scale), c, degree, _dev(ctx, d_rlk, ctx.key_words, "d_rlk"),
+                                    _dev(ctx, d_ct_out, n_out, "d_ct_out"), ctypes.byref(out_scale),
+                                    _stream(stream)), "ckks_poly_eval_tree")
+    return out_scale.value
+
+
 def _matvec_args(ctx, d_x, n_in, n_out, n1, n2, baby_galois, d_evk_baby, giant_galois, d_evk_giant, d_y, level,
                  flags, diag_words):
     _count(baby_galois, max(n1 - 1, 0), "baby_galois")
@@ -389,8 +410,7 @@ class KernelTrace:
 
     def read(self):
         st = ckks_trace_end(self.ctx)
-        st.update(name=self.kernel, alg_units=st["work_units"], ops_per_unit=OPS_PER_MODMUL,
-                  unit_name="modmul-class ops")
+        st.update(name=self.kernel, alg_units=st["work_units"], unit_name="modmul-class ops")
         return st
 
     def close(self):

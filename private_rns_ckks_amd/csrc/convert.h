@@ -1,0 +1,56 @@
+// Basis-conversion helpers shared by the conversion kernels: constants read
+// through the constant address space (wave-uniform indices become scalar
+// loads into SGPRs) and the split multiply-accumulate of up to 16 sources
+// against one target's constants.
+#pragma once
+#include "arith.h"
+#include "internal.h"
+
+namespace ckks {
+
+// Read-only tables read with wave-uniform indices: through the constant
+// address space the compiler fetches them with scalar loads, and the
+// multiply-accumulates take them straight from SGPRs.
+typedef const __attribute__((address_space(4))) uint64_t* ConstU64;
+typedef const __attribute__((address_space(4))) PrimeConst* ConstPrime;
+
+// The constants a reduction mod prime i needs.
+struct RedConst {
+  uint64_t q, r64, r64p, inv1;
+};
+__device__ __forceinline__ RedConst red_const(ConstPrime p, int i) {
+  RedConst r;
+  r.q = p[i].q;
+  r.r64 = p[i].r64;
+  r.r64p = p[i].r64p;
+  r.inv1 = p[i].inv1;
+  return r;
+}
+
+// Split multiply-accumulate of NS sources against one target's constants
+// (rows of a zero-padded table, stride `stride`), reduced mod the target q:
+// in [0, 6q) for NS = 8, in [0, q) for NS = 16.  Both ranges are valid inputs
+// of the forward NTT that follows (lazy butterflies start from words below
+// 6q and stay below 70q < 2^64 for q < 2^57; the others accept words below
+// 8q).  NS is 8 or 16; sources past the real count have zero constants and
+// words.
+template <int NS>
+__device__ __forceinline__ uint64_t conv_dot(const uint32_t (&yl)[NS], const uint32_t (&yh)[NS], ConstU64 conv,
+                                             int stride, const RedConst& pc) {
+  uint64_t cw[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) cw[i] = conv[i * stride];
+  uint64_t r = 0;
+#pragma unroll
+  for (int g = 0; g < NS; g += 8) {
+    Acc3 A = {0, 0, 0};
+#pragma unroll
+    for (int i = g; i < g + 8; ++i) acc3_mac(A, yl[i], yh[i], (uint32_t)cw[i], (uint32_t)(cw[i] >> 32));
+    if (NS == 8) return acc3_reduce_6q(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    const uint64_t v = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    r = g ? add_mod(r, v, pc.q) : v;
+  }
+  return r;
+}
+
+}  // namespace ckks

@@ -231,6 +231,13 @@ static int build_tables(Ctx* c) {
     md.push_back(v);
     md.push_back(shoup(v, qi));
   }
+  c->md.pinv64 = md.size();
+  for (uint32_t i = 0; i < L; ++i) {
+    const uint64_t qi = c->mod[i];
+    const uint64_t v = mulmod((uint64_t)(((u128)1 << 64) % qi), md[c->md.pinv + 2 * i], qi);
+    md.push_back(v);
+    md.push_back(shoup(v, qi));
+  }
   if ((rc = upload((void**)&c->d_moddown, md.data(), md.size() * 8))) return rc;
   return CKKS_OK;
 }

@@ -40,8 +40,9 @@ struct ModUpEntry {
 //   [0, 2K)            : {[phat_k^-1 * N^-1]_{p_k}, Shoup}
 //   [2K, 2K + K*L)     : [phat_k * P^-1]_{q_i}, row k, column i
 //   [.., + 2L)         : {[P^-1]_{q_i}, Shoup}
+//   [.., + 2L)         : {[2^64 P^-1]_{q_i}, Shoup} (Montgomery sums times P^-1 in one product)
 struct ModDownLayout {
-  size_t phinv, conv, pinv;
+  size_t phinv, conv, pinv, pinv64;
 };
 
 // Kernel timing trace (see ckks_trace_begin): HIP event pairs recorded on the

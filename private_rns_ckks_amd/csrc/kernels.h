@@ -21,13 +21,14 @@ struct ModUpArgs {
 };
 
 struct ModDownArgs {
-  const uint64_t* acc;  // [2][next][N] per item; special limbs hold y_k (coefficient form)
+  const uint64_t* acc;  // per item; special limb k of component c (y_k, coefficient form) at limb
+                        // c*acc_comp_limbs + acc_k0 + k: [2][next][N] with (next, level+1), or [2][K][N] with (K, 0)
   uint64_t* w;          // [2][level+1][N] per item (coefficient form)
   uint64_t acc_bstride, w_bstride;
   const uint64_t* conv;   // [K][L]
   const PrimeConst* prime;
   uint32_t n;
-  int level, next, L, K;
+  int level, acc_comp_limbs, acc_k0, L, K;
 };
 
 struct TensorArgs {
@@ -110,11 +111,33 @@ int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch);
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
 int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out);
 // Rescale of `batch` items by limb `level`: v = iNTT of that limb per item
-// and component ([2][N], canonical), w scratch [2][level][N], out [2][level][N].
+// and component ([2][N], canonical), w scratch [2][level][N], out
+// [2][out_limbs][N] (out_limbs <= 0: level), the output limbs i < out_limbs
+// only; add0: per-limb constant added to component 0; acc: [2][out_limbs][N]
+// per item added to the output (may equal out).
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
                   uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
-                  const uint64_t* add0 = nullptr);
+                  const uint64_t* add0 = nullptr, int out_limbs = 0, const uint64_t* acc = nullptr,
+                  uint64_t acc_bstride = 0);
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
+
+// Sum of constant multiples of up to kMaxTerms ciphertexts that share one
+// layout: out = sum_t K_t * x_t (mod q_i, K_t signed, |K_t| < 2^62), both
+// components, limbs 0 .. nl-1, plus add0[i] on component 0 when has_add; x_t
+// item b at x[t] + b*x_bstride ([2][nl][N] with component stride x_comp), out
+// item b at out + b*out_bstride ([2][nl][N] contiguous).  With no terms out
+// is zero (plus the constant).
+constexpr int kMaxTerms = 32;
+struct TermMacArgs {
+  const uint64_t* x[kMaxTerms];
+  int64_t k[kMaxTerms];
+  uint64_t add0[64];
+  uint64_t* out;
+  uint64_t x_bstride, x_comp, out_bstride;
+  const PrimeConst* prime;
+  int nt, nl, log_n, has_add;
+};
+int launch_term_mac(Ctx* c, hipStream_t s, TermMacArgs& a, int batch);
 
 // Argument checks of a batched rotation (shared by the entry points that
 // rotate): CKKS_OK or the error code, with the detail set.

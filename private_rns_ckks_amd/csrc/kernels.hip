@@ -8,6 +8,7 @@
 // layout makes every load and store a contiguous 64-bit access per lane.
 #include "arith.h"
 #include "automorph.h"
+#include "convert.h"
 #include "kernels.h"
 #include "ntt_core.h"
 
@@ -36,51 +37,6 @@ __global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64
     const uint64_t v = in[base + u - n];
     out[base + r] = v ? q - v : 0;
   }
-}
-
-// Read-only tables read with wave-uniform indices: through the constant
-// address space the compiler fetches them with scalar loads, and the
-// multiply-accumulates take them straight from SGPRs.
-typedef const __attribute__((address_space(4))) uint64_t* ConstU64;
-typedef const __attribute__((address_space(4))) PrimeConst* ConstPrime;
-
-// The constants a reduction mod prime i needs.
-struct RedConst {
-  uint64_t q, r64, r64p, inv1;
-};
-__device__ __forceinline__ RedConst red_const(ConstPrime p, int i) {
-  RedConst r;
-  r.q = p[i].q;
-  r.r64 = p[i].r64;
-  r.r64p = p[i].r64p;
-  r.inv1 = p[i].inv1;
-  return r;
-}
-
-// Split multiply-accumulate of NS sources against one target's constants
-// (rows of a zero-padded table, stride `stride`), reduced mod the target q:
-// in [0, 6q) for NS = 8, in [0, q) for NS = 16.  Both ranges are valid inputs
-// of the forward NTT that follows (lazy butterflies start from words below
-// 6q and stay below 70q < 2^64 for q < 2^57; the others accept words below
-// 8q).  NS is 8 or 16; sources past the real count have zero constants and
-// words.
-template <int NS>
-__device__ __forceinline__ uint64_t conv_dot(const uint32_t (&yl)[NS], const uint32_t (&yh)[NS], ConstU64 conv,
-                                             int stride, const RedConst& pc) {
-  uint64_t cw[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) cw[i] = conv[i * stride];
-  uint64_t r = 0;
-#pragma unroll
-  for (int g = 0; g < NS; g += 8) {
-    Acc3 A = {0, 0, 0};
-#pragma unroll
-    for (int i = g; i < g + 8; ++i) acc3_mac(A, yl[i], yh[i], (uint32_t)cw[i], (uint32_t)(cw[i] >> 32));
-    if (NS == 8) return acc3_reduce_6q(A, pc.q, pc.r64, pc.r64p, pc.inv1);
-    const uint64_t v = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
-    r = g ? add_mod(r, v, pc.q) : v;
-  }
-  return r;
 }
 
 // ModUp for digit blockIdx.y of batch item blockIdx.z.
@@ -127,7 +83,7 @@ __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   const ConstPrime prime = (ConstPrime)a.prime;
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int comp = blockIdx.y;
-  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.next + nq) * a.n + c;
+  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.acc_comp_limbs + a.acc_k0) * a.n + c;
   uint32_t yl[NS], yh[NS];
   uint32_t neg = 0;
 #pragma unroll
@@ -434,6 +390,30 @@ __global__ void const_mul_kernel(ConstMulArgs a) {
   a.out[blockIdx.z * a.out_bstride + off] = reduce_4q(mul_shoup_lazy(v, a.k[i][0], a.k[i][1], q), q);
 }
 
+// out = sum_t K_t x_t mod q_i.  Products of reduced words (< q^2 < 2^124)
+// are summed in 128 bits, eight at a time (below 2^127, as reduce128 needs),
+// and the partial sums added mod q.
+__global__ void term_mac_kernel(TermMacArgs a) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int comp = blockIdx.y / a.nl, i = blockIdx.y % a.nl;
+  const PrimeConst pc = a.prime[i];
+  const uint64_t off = blockIdx.z * a.x_bstride + comp * a.x_comp + ((uint64_t)i << a.log_n) + c;
+  uint64_t r = 0;
+  for (int t0 = 0; t0 < a.nt; t0 += 8) {
+    U128 s = {0, 0};
+    const int t1 = min(a.nt, t0 + 8);
+    for (int t = t0; t < t1; ++t) {
+      const int64_t kt = a.k[t];
+      uint64_t k = reduce64(kt < 0 ? (uint64_t)(-kt) : (uint64_t)kt, pc.q, pc.inv1);
+      if (kt < 0 && k) k = pc.q - k;
+      mac(s, k, a.x[t][off]);
+    }
+    r = add_mod(r, reduce128(s, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+  }
+  if (a.has_add && comp == 0) r = add_mod(r, a.add0[i], pc.q);
+  a.out[blockIdx.z * a.out_bstride + ((uint64_t)blockIdx.y << a.log_n) + c] = r;
+}
+
 }  // namespace
 
 #define LAUNCH_CHECK() CKKS_HIP_CHECK(hipGetLastError())
@@ -520,6 +500,14 @@ int launch_add(Ctx* c, hipStream_t s, const uint64_t* x, const uint64_t* y, uint
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch) {
   TraceScope ts(c, s, "const_mul", (double)batch * 2 * a.nl * c->N);
   hipLaunchKernelGGL(const_mul_kernel, dim3(c->N / 256, 2 * a.nl, batch), dim3(256), 0, s, a);
+  LAUNCH_CHECK();
+  return CKKS_OK;
+}
+
+int launch_term_mac(Ctx* c, hipStream_t s, TermMacArgs& a, int batch) {
+  if (a.nt < 0 || a.nt > kMaxTerms || a.nl < 1 || a.nl > 64) return set_error(CKKS_EINTERNAL, "bad term count");
+  TraceScope ts(c, s, "term_mac", (double)batch * 2 * a.nl * (a.nt + (a.nt + 7) / 8) * c->N);
+  hipLaunchKernelGGL(term_mac_kernel, dim3(c->N / 256, 2 * a.nl, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -1,23 +1,29 @@
-// Hybrid key switching, with the automorphism fused into the first inverse
-// NTT pass and the final combination fused into the last forward NTT pass.
+// Hybrid key switching.
 //
 // Per batch item, at level l (nq = l+1 ciphertext limbs, K special limbs,
-// beta digits):
+// beta digits of alpha limbs), ks_chunk runs:
 //   A  inverse row pass of the input polynomial; when rotating, the load
 //      gathers tau_g(c1) (NTT form)
-//   B  inverse column pass; its final multiply uses [qhat_i^-1 N^-1]_{q_i},
-//      so it produces the ModUp inputs y_i directly
+//   B  inverse column pass times [qhat_i^-1 N^-1]_{q_i}: the ModUp inputs y_i
 //   C  ModUp conversion sum_i y_i [qhat_i]_{m_t} mod m_t to every target limb
 //      t of every digit, then the forward column pass of those limbs
-//   D  forward row pass of the converted limbs fused with the inner product
-//      against the key digits (limbs inside their own digit read the
-//      NTT-form input, through tau_g when rotating)
-//   F  inverse NTT of the special limbs of both accumulators, final multiply
-//      by [phat_k^-1 N^-1]_{p_k}: the ModDown inputs y_k
+//   D  special limbs: forward row pass of the converted limbs fused with the
+//      inner product against the key digits, then the inverse row pass of
+//      both accumulator components on the same tile
+//   G  inverse column pass of the special accumulators times
+//      [phat_k^-1 N^-1]_{p_k}: the ModDown inputs y_k
 //   H  ModDown conversion sum_k y_k [1/p_k]_{q_i} - #{k: y_k > (p_k-1)/2}
 //      (the centred lift, times P^-1), then the forward column pass
-//   I  forward row pass whose store forms acc*P^-1 - NTT(w) (+ tau_g(c0))
-//      (+ the input, when accumulating) straight into the output
+//   I  ciphertext limbs: forward row pass of the converted limbs fused with
+//      the inner product (limbs inside their own digit read the NTT-form
+//      input, through tau_g when rotating), then the forward row pass of the
+//      ModDown output on the same tile, storing acc*P^-1 - NTT(w)
+//      (+ tau_g(c0)) (+ the input, when accumulating) straight into the
+//      output: the ciphertext-limb accumulators never go to memory.
+// Hoisted rotations run A-C and the forward row pass once per input
+// (ks_decompose); per rotation, a gathered inner product over every limb
+// (ip_gather_kernel) and ks_back: the inverse NTT of the special limbs, H,
+// and a combining forward row pass.
 #include <string.h>
 
 #include "automorph.h"
@@ -93,6 +99,7 @@ struct RowIPArgs {
   uint32_t g[kMaxChunk];  // item b's input limbs are read through tau_g (0: as they are)
   int shared_key;  // every item uses the same key: order the grid items first
   int items_per_wg, n_items;  // a workgroup runs items z*items_per_wg .. (twiddles staged once)
+  int t0;          // target limb of grid job 0 (job j handles limb t0 + j)
 };
 
 // A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
@@ -194,25 +201,45 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
   }
 }
 
+// Forward row pass of one limb (src, lazy column-pass output) on the tile:
+// the thread ends with rows base..base+7 of its column in x[] (lazy).
+template <int LOGB, bool LAZY>
+__device__ __forceinline__ void ip_row_pass(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
+                                            uint32_t tile, int log_n, uint64_t q) {
+  typedef IPRounds<LOGB> G;
+  __syncthreads();  // every thread has read the tile's previous contents
+  if constexpr (G::R1 > 0) {
+    ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
+    __syncthreads();
+    ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, twl, tile, log_n, q);
+  } else {
+    ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
+  }
+  __syncthreads();
+  ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, twl, tile, log_n, q);
+}
+
+// Multiply-accumulate of target limb t (tile gp.tile, item gp.item) over the
+// digits: accb[i] / acca[i] receive sum_j x_j * evk_j.{b,a} for the thread's
+// 8 words (rows base..base+7 of column col), x_j the forward row pass of the
+// converted limb E[j][t] or, for t inside digit j, the NTT-form input limb
+// (through tau_g when rotating).  Sums of Montgomery products, below 8m
+// (reduced every 4 digits); the factor 2^-64 is left in them.
 template <int LOGB, int LOGN, bool LAZY>
-__device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, ulonglong2* twl, const PrimeConst& pc,
-                                            int keyl, const GridPos& gp, bool stage) {
+__device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds, const ulonglong2* twl,
+                                              const PrimeConst& pc, int keyl, const GridPos& gp, uint64_t (&accb)[8],
+                                              uint64_t (&acca)[8]) {
   typedef IPRounds<LOGB> G;
   const int log_n = LOGN ? LOGN : a.log_n;
-  const uint32_t s0 = (uint32_t)logb_col(log_n);
-  const int t = gp.job, item = gp.item;
+  const int t = gp.job + a.t0, item = gp.item;
   const uint32_t tile = gp.tile;
   const uint64_t q = pc.q, mp = pc.mprime;
-  const uint64_t* tw = a.tw + ((uint64_t)keyl << (log_n + 1));
   const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
-  // this thread's 8 output words: rows base..base+7 of column col
   int col, base;
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
-  if (stage) ip_stage_twiddles<LOGB>(twl, tw, tile, s0);  // read after the barrier that opens each digit's transform
   // Montgomery products are below 2m, so four of them sum below 8m < 2^63
-  uint64_t accb[8], acca[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) accb[i] = acca[i] = 0;
   for (int j = 0; j < a.beta; ++j) {
@@ -233,18 +260,9 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
           x[2 * i + 1] = v.y;
         }
       }
-    } else {  // forward row pass of the converted limb; outputs stay lazy (< 65q, or < 8q)
+    } else {  // forward row pass of the converted limb; outputs stay lazy (< 70q, or < 8q)
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
-      __syncthreads();  // the previous digit's last round has read the tile
-      if constexpr (G::R1 > 0) {
-        ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
-        __syncthreads();
-        ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, twl, tile, log_n, q);
-      } else {
-        ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
-      }
-      __syncthreads();
-      ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, twl, tile, log_n, q);
+      ip_row_pass<LOGB, LAZY>(x, src, lds, twl, tile, log_n, q);
     }
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
@@ -269,51 +287,242 @@ __device__ __forceinline__ void row_ip_body(const RowIPArgs& a, uint64_t* lds, u
       }
     }
   }
-  // remove the 2^-64 of the Montgomery products: times 2^64 mod m
-  ulonglong2* ob = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)t << log_n) + w0);
-  ulonglong2* oa = reinterpret_cast<ulonglong2*>(a.acc + item * a.acc_bstride + ((uint64_t)(a.next + t) << log_n) + w0);
+}
+
+// ---------------------------------------------------------------------------
+// Inner product of the special limbs only (targets t = l+1 .. l+K), followed
+// on the same tile by the first pass of their inverse NTT (the row pass), so
+// the accumulators leave in the form the fused ModDown conversion reads.
+//
+// The inverse row pass of one component: the thread's 8 words (rows
+// base..base+7 of its column, canonical) go through the Gentleman-Sande stages
+// of row bits 0-2 in registers, then of row bits 3.. and 6.. through the LDS
+// tile, and are stored in the lazy range of the inverse butterflies ([0, q)
+// after a final reduction for q < 2^54, [0, 4q) otherwise).
+template <int LOGB, bool LAZY>
+__device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t* lds, uint32_t tile, int log_n,
+                                                     const uint64_t* twi, uint64_t q, uint64_t inv1, uint64_t* dst) {
+  typedef IPRounds<LOGB> G;
+  constexpr int T = G::THREADS;
+  const uint32_t s0 = (uint32_t)logb_col(log_n);
+  int col, base;
+  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  {
+    const uint32_t blk = tile * G::KC + col;
+    round_regs<3, true, LAZY, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+  }
+  __syncthreads();  // every thread has read the tile's previous contents
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ulonglong2 vb, va;
-    vb.x = reduce_4q(mul_shoup_lazy(accb[2 * i], pc.r64, pc.r64p, q), q);
-    vb.y = reduce_4q(mul_shoup_lazy(accb[2 * i + 1], pc.r64, pc.r64p, q), q);
-    va.x = reduce_4q(mul_shoup_lazy(acca[2 * i], pc.r64, pc.r64p, q), q);
-    va.y = reduce_4q(mul_shoup_lazy(acca[2 * i + 1], pc.r64, pc.r64p, q), q);
-    ob[i] = vb;
-    oa[i] = va;
+  for (int i = 0; i < 8; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
+  __syncthreads();
+  // row bits [3, 3 + R2)
+  constexpr int N2 = 8 >> G::R2;
+#pragma unroll
+  for (int k = 0; k < N2; ++k) {
+    int c, b;
+    item_coords<false, G::R2, LOGB>(threadIdx.x + k * T, 3, c, b);
+    uint64_t y[1 << G::R2];
+#pragma unroll
+    for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
+    const uint32_t blk = tile * G::KC + c;
+    round_regs<G::R2, true, LAZY, false, false, 3>(y, b, 3, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+    if constexpr (G::R1 == 0) {
+#pragma unroll
+      for (int i = 0; i < (1 << G::R2); ++i) {
+        const uint64_t v = LAZY ? reduce64(y[i], q, inv1) : y[i];
+        dst[ip_word<LOGB>(tile, b + (i << 3), c)] = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < (1 << G::R2); ++i) lds[ip_lds<LOGB>(b + (i << 3), c)] = y[i];
+    }
+  }
+  if constexpr (G::R1 > 0) {
+    __syncthreads();
+    constexpr int N1 = 8 >> G::R1;
+    constexpr int P1 = 3 + G::R2;
+#pragma unroll
+    for (int k = 0; k < N1; ++k) {
+      int c, b;
+      item_coords<false, G::R1, LOGB>(threadIdx.x + k * T, P1, c, b);
+      uint64_t y[1 << G::R1];
+#pragma unroll
+      for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
+      const uint32_t blk = tile * G::KC + c;
+      round_regs<G::R1, true, LAZY, false, false, P1>(y, b, P1, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+#pragma unroll
+      for (int i = 0; i < (1 << G::R1); ++i) {
+        const uint64_t v = LAZY ? reduce64(y[i], q, inv1) : y[i];
+        dst[ip_word<LOGB>(tile, b + (i << P1), c)] = v;
+      }
+    }
   }
 }
 
-// at most 168 VGPRs: three waves per SIMD (three workgroups per CU at 2^8 rows)
+// acc: item b at acc + b*acc_bstride, [2][K][N] (special limbs only).
 template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void ntt_row_ip_kernel(
-    RowIPArgs a) {
+__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void ip_special_kernel(
+    RowIPArgs a, const uint64_t* twi) {
   __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
   __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
   const GridPos g0 = a.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
-  const int t = g0.job;
-  const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
+  const int t = g0.job + a.t0;  // a special limb
+  const int keyl = a.L + (t - a.level - 1);
   const PrimeConst& pc = a.prime[keyl];
+  const int log_n = LOGN ? LOGN : a.log_n;
+  const uint32_t s0 = (uint32_t)logb_col(log_n);
+  const uint64_t* tw_i = twi + ((uint64_t)keyl << (log_n + 1));
+  ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)keyl << (log_n + 1)), g0.tile, s0);
+  int col, base;
+  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   for (int k = 0; k < a.items_per_wg; ++k) {
     GridPos gp = g0;
     gp.item = g0.item * a.items_per_wg + k;
     if (gp.item >= a.n_items) break;
-    if (pc.q < (1ull << 57))
-      row_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp, k == 0);
+    uint64_t accb[8], acca[8];
+    const bool lazy_fwd = pc.q < (1ull << 57);
+    if (lazy_fwd)
+      ip_accumulate<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp, accb, acca);
     else
-      row_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp, k == 0);
+      ip_accumulate<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp, accb, acca);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // remove the 2^-64: canonical accumulators
+      accb[i] = reduce_4q(mul_shoup_lazy(accb[i], pc.r64, pc.r64p, pc.q), pc.q);
+      acca[i] = reduce_4q(mul_shoup_lazy(acca[i], pc.r64, pc.r64p, pc.q), pc.q);
+    }
+    uint64_t* ob = a.acc + gp.item * a.acc_bstride + ((uint64_t)(t - a.level - 1) << log_n);
+    uint64_t* oa = ob + ((uint64_t)a.K << log_n);
+    if (pc.q < (1ull << 54)) {
+      ip_inverse_row_store<LOGB, true>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, true>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+    } else {
+      ip_inverse_row_store<LOGB, false>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, false>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+    }
   }
 }
 
-typedef void (*RowIPFn)(RowIPArgs);
+typedef void (*IPSpecialFn)(RowIPArgs, const uint64_t*);
 
-RowIPFn pick_row_ip(int log_n, int logb) {
-  if (log_n == 16 && logb == 8) return ntt_row_ip_kernel<8, 16>;
+IPSpecialFn pick_ip_special(int log_n, int logb) {
+  if (log_n == 16 && logb == 8) return ip_special_kernel<8, 16>;
   switch (logb) {
-    case 5: return ntt_row_ip_kernel<5, 0>;
-    case 6: return ntt_row_ip_kernel<6, 0>;
-    case 7: return ntt_row_ip_kernel<7, 0>;
-    case 8: return ntt_row_ip_kernel<8, 0>;
+    case 5: return ip_special_kernel<5, 0>;
+    case 6: return ip_special_kernel<6, 0>;
+    case 7: return ip_special_kernel<7, 0>;
+    case 8: return ip_special_kernel<8, 0>;
+  }
+  return nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Inner product of the ciphertext limbs fused with the final combination:
+// per (tile, limb i <= l, item) the workgroup accumulates the key inner
+// product in registers (as ip_accumulate), then runs the forward row pass of
+// the ModDown output w of both components on the same tile, and stores
+//   out_c[i] = acc_c * P^-1 - NTT(w_c) (+ add_c) (+ accum_c)
+// directly: the ciphertext-limb accumulators never go to memory.  The
+// factors 2^64 (Montgomery) and P^-1 are one Shoup multiplication by
+// [2^64 P^-1]_{q_i}.
+struct CombIPArgs {
+  RowIPArgs ip;
+  const uint64_t* W;  // item b: W + b*W_bstride, [2][nq][N] (forward column pass done)
+  uint64_t W_bstride;
+  const uint64_t* add[2];  // component c's additive term, item b at + b*add_bstride, [nq][N]
+  uint64_t add_bstride;
+  uint32_t add_g[kMaxChunk];  // item b's add terms are read through tau_g (0: as they are)
+  const uint64_t* accum;      // [2][nq][N] per item, or NULL
+  uint64_t accum_bstride;
+  uint64_t* out;
+  uint64_t out_bstride;
+  int out_comp_limbs;
+  const uint64_t* pinv64;  // [L][2]: {[2^64 P^-1]_{q_i}, Shoup}
+};
+
+template <int LOGB, int LOGN, bool LAZY>
+__device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds, const ulonglong2* twl,
+                                             const PrimeConst& pc, int i, const GridPos& gp) {
+  const int log_n = LOGN ? LOGN : a.ip.log_n;
+  const int item = gp.item;
+  const uint64_t q = pc.q;
+  uint64_t acc[2][8];
+  ip_accumulate<LOGB, LOGN, LAZY>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
+  const uint64_t cw = a.pinv64[2 * i], cwp = a.pinv64[2 * i + 1];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[c][r] = reduce_4q(mul_shoup_lazy(acc[c][r], cw, cwp, q), q);
+  int col, base;
+  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  const uint32_t w0 = ip_word<LOGB>(gp.tile, base, col);
+  const uint32_t ag = a.add_g[item];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint64_t x[8];
+    ip_row_pass<LOGB, LAZY>(x, a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds, twl,
+                            gp.tile, log_n, q);
+    uint64_t add[8], accum[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) add[r] = accum[r] = 0;
+    if (a.add[c]) {
+      const uint64_t* ad = a.add[c] + item * a.add_bstride + ((uint64_t)i << log_n);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) add[r] = ad[ag ? automorph_src(w0 + r, ag, log_n) : w0 + r];
+    }
+    if (a.accum) {
+      const ulonglong2* ac =
+          reinterpret_cast<const ulonglong2*>(a.accum + item * a.accum_bstride + ((uint64_t)(c * (a.ip.level + 1) + i) << log_n) + w0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const ulonglong2 v = ac[r];
+        accum[2 * r] = v.x;
+        accum[2 * r + 1] = v.y;
+      }
+    }
+    ulonglong2* o = reinterpret_cast<ulonglong2*>(a.out + item * a.out_bstride +
+                                                  ((uint64_t)(c * a.out_comp_limbs + i) << log_n) + w0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ulonglong2 v;
+      uint64_t e0 = sub_mod(acc[c][2 * r], reduce64(x[2 * r], q, pc.inv1), q);
+      uint64_t e1 = sub_mod(acc[c][2 * r + 1], reduce64(x[2 * r + 1], q, pc.inv1), q);
+      v.x = add_mod(add_mod(e0, add[2 * r], q), accum[2 * r], q);
+      v.y = add_mod(add_mod(e1, add[2 * r + 1], q), accum[2 * r + 1], q);
+      o[r] = v;
+    }
+  }
+}
+
+template <int LOGB, int LOGN>
+__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void comb_ip_kernel(
+    CombIPArgs a) {
+  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
+  __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
+  const GridPos g0 = a.ip.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
+  const int i = g0.job;  // a ciphertext limb
+  const PrimeConst& pc = a.ip.prime[i];
+  const int log_n = LOGN ? LOGN : a.ip.log_n;
+  ip_stage_twiddles<LOGB>(twl, a.ip.tw + ((uint64_t)i << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  for (int k = 0; k < a.ip.items_per_wg; ++k) {
+    GridPos gp = g0;
+    gp.item = g0.item * a.ip.items_per_wg + k;
+    if (gp.item >= a.ip.n_items) break;
+    if (pc.q < (1ull << 57))
+      comb_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, i, gp);
+    else
+      comb_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, i, gp);
+  }
+}
+
+typedef void (*CombIPFn)(CombIPArgs);
+
+CombIPFn pick_comb_ip(int log_n, int logb) {
+  if (log_n == 16 && logb == 8) return comb_ip_kernel<8, 16>;
+  switch (logb) {
+    case 5: return comb_ip_kernel<5, 0>;
+    case 6: return comb_ip_kernel<6, 0>;
+    case 7: return comb_ip_kernel<7, 0>;
+    case 8: return comb_ip_kernel<8, 0>;
   }
   return nullptr;
 }
@@ -409,7 +618,7 @@ constexpr int kGatherWords = 4;  // consecutive output words per thread
 
 // acc_b[t][w] = sum_j D_j[t][pi_g(w)] * evk_j.b[t][w] (and acc_a), D_j the
 // raised digit j (c1 itself for limbs inside digit j), pi_g the NTT-form
-// automorphism.  Lazy Montgomery products as in ntt_row_ip_kernel.
+// automorphism.  Lazy Montgomery products as in ip_accumulate.
 __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
   const int t = blockIdx.y, item = blockIdx.z;
   const int keyl = t <= a.level ? t : a.L + (t - a.level - 1);
@@ -470,9 +679,94 @@ __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-size_t ws_words(const Ctx* c, int level) {
-  const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
-  return n * (nq /*Y*/ + beta * next /*E*/ + 2 * next /*A*/ + 2 * nq /*W*/);
+
+// ModUp of the inverse-row-passed input Y (item b at Y + b*ystride,
+// [nq][N]): the inverse column pass times [qhat_i^-1 N^-1] (canonical y_i), the
+// conversion to every target limb of every digit, and the forward column
+// pass of the converted limbs, into E (item b at E + b*estride,
+// [beta][next][N], lazy).  Y is overwritten.
+int modup_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* Y, uint64_t ystride, uint64_t* E,
+                uint64_t estride) {
+  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
+  int rc;
+  {
+    NttJobs jobs;
+    uint32_t off[kMaxJobs];
+    for (int j = 0; j < beta; ++j) {
+      const ModUpEntry& en = c->modup[level][j];
+      for (int i = en.lo; i < en.hi; ++i) {
+        off[jobs.n] = (uint32_t)(en.offset + 2 * (i - en.lo));
+        jobs.add(i, i, i);
+      }
+    }
+    if ((rc = ntt_pass_only(c, s, Y, Y, ystride, ystride, n_items, jobs, true, false, 2, c->d_modup, off))) return rc;
+  }
+  ModUpArgs mu;
+  memset(&mu, 0, sizeof(mu));
+  mu.x = Y;
+  mu.out = E;
+  mu.x_bstride = ystride;
+  mu.out_bstride = estride;
+  mu.tables = c->d_modup;
+  mu.prime = c->d_prime;
+  mu.n = c->N;
+  mu.level = level;
+  mu.next = next;
+  mu.L = (int)c->L;
+  for (int j = 0; j < beta; ++j) {
+    const ModUpEntry& en = c->modup[level][j];
+    mu.lo[j] = en.lo;
+    mu.hi[j] = en.hi;
+    mu.offset[j] = en.offset;
+  }
+  if ((rc = launch_modup(c, s, mu, beta, n_items))) return rc;
+  NttJobs jobs;
+  for (int j = 0; j < beta; ++j)
+    for (int t = 0; t < next; ++t) {
+      if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
+      jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
+    }
+  return ntt_pass_only(c, s, E, E, estride, estride, n_items, jobs, false, true, 0, nullptr, nullptr);
+}
+
+// ModDown of the special accumulators A (item b at A + b*astride, [2][K][N],
+// inverse row pass done): the inverse column pass times [phat_k^-1 N^-1]
+// (y_k, canonical), the centred conversion to the ciphertext limbs (times
+// P^-1), and their forward column pass, into W (item b at W + b*wstride,
+// [2][nq][N], lazy).  A is overwritten.
+int moddown_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* A, uint64_t astride, uint64_t* W,
+                  uint64_t wstride) {
+  const int nq = level + 1, K = (int)c->K;
+  int rc;
+  {
+    NttJobs jobs;
+    uint32_t off[kMaxJobs];
+    for (int comp = 0; comp < 2; ++comp)
+      for (int k = 0; k < K; ++k) {
+        off[jobs.n] = (uint32_t)(c->md.phinv + 2 * k);
+        jobs.add(comp * K + k, comp * K + k, (int)c->L + k);
+      }
+    if ((rc = ntt_pass_only(c, s, A, A, astride, astride, n_items, jobs, true, false, 2, c->d_moddown, off))) return rc;
+  }
+  ModDownArgs md;
+  memset(&md, 0, sizeof(md));
+  md.acc = A;
+  md.w = W;
+  md.acc_bstride = astride;
+  md.w_bstride = wstride;
+  md.conv = c->d_moddown + c->md.conv;
+  md.prime = c->d_prime;
+  md.n = c->N;
+  md.level = level;
+  md.acc_comp_limbs = K;
+  md.acc_k0 = 0;
+  md.L = (int)c->L;
+  md.K = K;
+  if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
+  NttJobs jobs;
+  for (int comp = 0; comp < 2; ++comp)
+    for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
+  return ntt_pass_only(c, s, W, W, wstride, wstride, n_items, jobs, false, true, 0, nullptr, nullptr);
 }
 
 // Steps F to I for n_items accumulators A (item i at A + i*per, [2][next][N]
@@ -508,7 +802,8 @@ int ks_back(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uin
     md.prime = c->d_prime;
     md.n = N;
     md.level = level;
-    md.next = next;
+    md.acc_comp_limbs = next;
+    md.acc_k0 = nq;
     md.L = (int)c->L;
     md.K = (int)c->K;
     if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
@@ -550,7 +845,16 @@ int ks_back(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uin
 
 }  // namespace
 
-size_t ks_ws_words(const Ctx* c, int level) { return ws_words(c, level); }
+// Workspace of the fused pipeline per item: Y [nq] (inverse row pass of the
+// input), E [beta][next] (raised digits after the forward column pass), A
+// [2][K] (special accumulators after the inverse row pass), W [2][nq]
+// (ModDown output after the forward column pass).
+size_t fused_ws_words(const Ctx* c, int level) {
+  const size_t n = c->N, nq = level + 1, next = nq + c->K, beta = c->beta(level);
+  return n * (nq + beta * next + 2 * (size_t)c->K + 2 * nq);
+}
+
+size_t ks_ws_words(const Ctx* c, int level) { return fused_ws_words(c, level); }
 
 size_t ks_dec_words(const Ctx* c, int level) {
   const size_t nq = level + 1, next = nq + c->K;
@@ -671,22 +975,32 @@ int ks_hoisted_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem
   return ks_back(c, s, level, n_items, it, A, W, per, 0, 0, out_stride, nq);
 }
 
-int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
-             uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
+// The fused pipeline (digits and special primes of at most 8 limbs):
+//   intt_row_gather   inverse row pass of tau_g(c1)                 -> Y
+//   modup pass        inverse column pass of each digit, ModUp,
+//                     forward column pass of every target limb      -> E
+//   ip_special        forward row pass + inner product of the K
+//                     special limbs, inverse row pass               -> A
+//   moddown pass      inverse column pass of A, centred ModDown,
+//                     forward column pass of every ciphertext limb  -> W
+//   comb_ip           forward row pass + inner product of the
+//                     ciphertext limbs, forward row pass of W,
+//                     acc*P^-1 - NTT(w) (+ add) (+ accum)           -> out
+int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
+                   uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
   const uint32_t N = c->N;
   const int log_n = (int)c->log_n;
-  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
-  const uint64_t per = ws_words(c, level);
+  const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level), K = (int)c->K;
+  const uint64_t per = fused_ws_words(c, level);
   uint64_t* Y = ws;
   uint64_t* E = Y + (uint64_t)nq * N;
   uint64_t* A = E + (uint64_t)beta * next * N;
-  uint64_t* W = A + (uint64_t)2 * next * N;
-  const int lr = logb_row(log_n), lc = logb_col(log_n);
+  uint64_t* W = A + (uint64_t)2 * K * N;
+  const int lr = logb_row(log_n);
   int rc;
-
-  // A: inverse row pass (gather tau_g(c1) when rotating)
   {
     GatherArgs ga;
+    memset(&ga, 0, sizeof(ga));
     ga.src = it[0].d;
     ga.src_bstride = d_stride;
     ga.dst = Y;
@@ -701,96 +1015,81 @@ int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, ui
     hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_items), dim3(kThreads), 0, s, ga);
     CKKS_HIP_CHECK(hipGetLastError());
   }
-  const uint64_t* Tsrc = it[0].d;
-  const uint64_t T_stride = d_stride;
-  // B: inverse column pass, times [qhat_i^-1 N^-1]: the ModUp inputs y_i
-  {
-    NttJobs jobs;
-    uint32_t off[kMaxJobs];
-    for (int j = 0; j < beta; ++j) {
-      const ModUpEntry& en = c->modup[level][j];
-      for (int i = en.lo; i < en.hi; ++i) {
-        off[jobs.n] = (uint32_t)(en.offset + 2 * (i - en.lo));
-        jobs.add(i, i, i);
-      }
-    }
-    // the row pass above already ran: run only the column pass, in place on Y
-    if ((rc = ntt_pass_only(c, s, Y, Y, per, per, n_items, jobs, true, false, 2, c->d_modup, off))) return rc;
+  if ((rc = modup_steps(c, s, level, n_items, Y, per, E, per))) return rc;
+  RowIPArgs ip;
+  memset(&ip, 0, sizeof(ip));
+  ip.E = E;
+  ip.E_bstride = per;
+  ip.T = it[0].d;
+  ip.T_bstride = d_stride;
+  for (int i = 0; i < n_items; ++i) ip.g[i] = it[i].g;
+  ip.shared_key = 1;
+  for (int i = 0; i < n_items; ++i) {
+    ip.evk[i] = it[i].evk;
+    if (it[i].evk != it[0].evk) ip.shared_key = 0;
   }
-  // C: ModUp conversion, then both forward passes of the converted limbs
+  ip.tw = c->d_tw_fwd;
+  ip.prime = c->d_prime;
+  ip.log_n = log_n;
+  ip.level = level;
+  ip.next = next;
+  ip.beta = beta;
+  ip.alpha = (int)c->alpha;
+  ip.L = (int)c->L;
+  ip.K = K;
+  ip.n_items = n_items;
+  const int logkc = ip_logkc(lr);
+  const dim3 block(1u << (lr - 3 + logkc));
   {
-    ModUpArgs mu;
-    memset(&mu, 0, sizeof(mu));
-    mu.x = Y;
-    mu.out = E;
-    mu.x_bstride = per;
-    mu.out_bstride = per;
-    mu.tables = c->d_modup;
-    mu.prime = c->d_prime;
-    mu.n = N;
-    mu.level = level;
-    mu.next = next;
-    mu.L = (int)c->L;
-    for (int j = 0; j < beta; ++j) {
-      const ModUpEntry& en = c->modup[level][j];
-      mu.lo[j] = en.lo;
-      mu.hi[j] = en.hi;
-      mu.offset[j] = en.offset;
-    }
-    if ((rc = launch_modup(c, s, mu, beta, n_items))) return rc;
-    NttJobs jobs;
-    for (int j = 0; j < beta; ++j)
-      for (int t = 0; t < next; ++t) {
-        if (t >= c->modup[level][j].lo && t < c->modup[level][j].hi) continue;
-        jobs.add(j * next + t, j * next + t, c->ext_prime(level, t));
-      }
-    if ((rc = ntt_pass_only(c, s, E, E, per, per, n_items, jobs, false, true, 0, nullptr, nullptr))) return rc;
+    RowIPArgs sp = ip;
+    sp.acc = A;
+    sp.acc_bstride = per;
+    sp.t0 = nq;
+    sp.items_per_wg = 2;
+    IPSpecialFn fn = pick_ip_special(log_n, lr);
+    if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
+    const double units = (double)K * ((double)beta * (N / 2) * lr + N * (2.0 * beta + 2) + 2.0 * (N / 2) * lr);
+    TraceScope ts(c, s, "ip_special", units * n_items);
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), K, (n_items + 1) / 2), block, 0, s, sp, c->d_tw_inv);
+    CKKS_HIP_CHECK(hipGetLastError());
   }
-  // D+E: forward row pass fused with the inner product
+  if ((rc = moddown_steps(c, s, level, n_items, A, per, W, per))) return rc;
   {
-    RowIPArgs ip;
-    memset(&ip, 0, sizeof(ip));
-    ip.E = E;
-    ip.E_bstride = per;
-    ip.T = Tsrc;
-    ip.T_bstride = T_stride;
-    for (int i = 0; i < n_items; ++i) ip.g[i] = it[i].g;
-    ip.acc = A;
-    ip.acc_bstride = per;
-    ip.shared_key = 1;
-    for (int i = 0; i < n_items; ++i) {
-      ip.evk[i] = it[i].evk;
-      if (it[i].evk != it[0].evk) ip.shared_key = 0;
-    }
-    ip.tw = c->d_tw_fwd;
-    ip.prime = c->d_prime;
-    ip.log_n = log_n;
-    ip.level = level;
-    ip.next = next;
-    ip.beta = beta;
-    ip.alpha = (int)c->alpha;
-    ip.L = (int)c->L;
-    ip.K = (int)c->K;
-    RowIPFn fn = pick_row_ip(log_n, lr);
+    CombIPArgs ca;
+    memset(&ca, 0, sizeof(ca));
+    ca.ip = ip;
+    ca.ip.t0 = 0;
+    ca.ip.items_per_wg = 2;
+    ca.W = W;
+    ca.W_bstride = per;
+    ca.add[0] = it[0].add[0];
+    ca.add[1] = it[0].add[1];
+    ca.add_bstride = add_stride;
+    for (int i = 0; i < n_items; ++i) ca.add_g[i] = it[i].add_g;
+    ca.accum = it[0].accum;
+    ca.accum_bstride = accum_stride;
+    ca.out = it[0].out;
+    ca.out_bstride = out_stride;
+    ca.out_comp_limbs = out_comp_limbs;
+    ca.pinv64 = c->d_moddown + c->md.pinv64;
+    CombIPFn fn = pick_comb_ip(log_n, lr);
     if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
     double units = 0;
     for (int j = 0; j < beta; ++j) {
       const int na = c->modup[level][j].hi - c->modup[level][j].lo;
-      units += (double)(next - na) * (N / 2) * lr;  // butterflies
+      units += (double)(nq - na) * (N / 2) * lr;  // row passes of the converted ciphertext limbs
     }
-    units += (double)next * N * (2.0 * beta + 2);  // products and final reductions
-    TraceScope ts(c, s, "ntt_row_ip", units * n_items);
-    const int logkc = ip_logkc(lr);
-    // two items per workgroup: the tile's twiddles are staged once for both
-    // (half the twiddle traffic); more items leave too few workgroups
-    const int ipw = 2;
-    ip.items_per_wg = ipw;
-    ip.n_items = n_items;
-    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), next, (n_items + ipw - 1) / ipw), dim3(1u << (lr - 3 + logkc)), 0,
-                       s, ip);
+    units += (double)nq * (N * (2.0 * beta + 2) + 2.0 * ((N / 2) * lr + N));
+    TraceScope ts(c, s, "comb_ip", units * n_items);
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), nq, (n_items + 1) / 2), block, 0, s, ca);
     CKKS_HIP_CHECK(hipGetLastError());
   }
-  return ks_back(c, s, level, n_items, it, A, W, per, add_stride, accum_stride, out_stride, out_comp_limbs);
+  return CKKS_OK;
+}
+
+int ks_chunk(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* it, uint64_t d_stride,
+             uint64_t add_stride, uint64_t accum_stride, uint64_t out_stride, int out_comp_limbs, uint64_t* ws) {
+  return ks_chunk_fused(c, s, level, n_items, it, d_stride, add_stride, accum_stride, out_stride, out_comp_limbs, ws);
 }
 
 }  // namespace ckks

@@ -52,9 +52,12 @@ int check_galois(const Ctx* c, uint32_t g) {
   return CKKS_OK;
 }
 
-// Rescale of `batch` items: in [2][level+1][N] at in + b*in_stride -> out [2][level][N].
+// Rescale of `batch` items: in [2][level+1][N] at in + b*in_stride -> out
+// [2][out_limbs][N] (out_limbs <= 0: level), plus acc (same layout as out,
+// may equal it) when given.
 int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride, uint64_t* out, uint64_t out_stride,
-                  int batch, int level, uint64_t* ws, uint64_t ws_words, const uint64_t* add0 = nullptr) {
+                  int batch, int level, uint64_t* ws, uint64_t ws_words, const uint64_t* add0 = nullptr,
+                  int out_limbs = 0, const uint64_t* acc = nullptr) {
   const uint32_t N = c->N;
   const uint64_t per = (uint64_t)N * (2 + 2 * level);
   const int chunk = (int)std::max<uint64_t>(1, std::min<uint64_t>(kMaxChunk, ws_words / per));
@@ -68,7 +71,7 @@ int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride,
     if (rc) return rc;
     // conversion and final combination fused into the forward NTT of w
     if ((rc = rescale_fused(c, s, in + b0 * in_stride, in_stride, V, per, W, per, out + b0 * out_stride, out_stride, n,
-                            level, add0)))
+                            level, add0, out_limbs, acc ? acc + b0 * out_stride : nullptr, out_stride)))
       return rc;
   }
   return CKKS_OK;
@@ -100,11 +103,13 @@ hipStream_t lane_stream(Ctx* c, hipStream_t s, int lanes, int k) { return lanes 
 // Multiply, relinearise and (when `rescale`) rescale a batch: a item b at
 // a + b*2(l+1)N; b item b at b + b*b_bstride with component stride b_comp (so
 // b may be a higher-level ciphertext read at its first l+1 limbs).  add0:
-// optional per-limb constant added to component 0 of the rescaled output.
+// optional per-limb constant added to component 0 of the rescaled output;
+// acc: optional ciphertexts (the output's layout, may be the output itself)
+// added to the rescaled output.
 static int mul_relin_rescale(Ctx* ctx, hipStream_t stream, const uint64_t* d_a, const uint64_t* d_b,
                              uint64_t b_bstride,
                              uint64_t b_comp, const uint64_t* d_rlk, uint64_t* d_out, int batch, int level,
-                             bool rescale, const uint64_t* add0) {
+                             bool rescale, const uint64_t* add0, const uint64_t* acc = nullptr) {
   if (batch == 0) return CKKS_OK;
   const uint32_t N = ctx->N;
   const int nq = level + 1;
@@ -152,7 +157,7 @@ static int mul_relin_rescale(Ctx* ctx, hipStream_t stream, const uint64_t* d_a, 
     if ((rc = ks_chunk(ctx, ls, level, n, items, tens, tens, 0, rel, nq, S))) break;
     if (rescale)
       rc = rescale_batch(ctx, ls, R, rel, d_out + b0 * 2ull * level * N, 2ull * level * N, n, level, S,
-                         chunk * std::max(ks, rs_per), add0);
+                         chunk * std::max(ks, rs_per), add0, 0, acc ? acc + b0 * 2ull * level * N : nullptr);
   }
   return join_lanes(ctx, stream, lanes, rc);
 }
@@ -609,6 +614,212 @@ int ckks_poly_eval(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level,
     --l;
   }
   return CKKS_OK;
+}
+
+static int ceil_log2(int k) {
+  int r = 0;
+  while ((1 << r) < k) ++r;
+  return r;
+}
+
+namespace {
+
+int trim_coeffs(const double* c, int n) {
+  while (n > 0 && c[n - 1] == 0.0) --n;
+  return n;
+}
+
+// Depth-efficient evaluation of a power-basis polynomial on a chunk of items
+// (see ckks_poly_eval_tree in include/ckks.h for the scheme).  Node results
+// and the high parts' intermediates live on a stack carved from `arena`.
+struct TreeEval {
+  Ctx* ctx;
+  hipStream_t s;
+  const uint64_t* rlk;
+  int level, n;                // input level, items in the chunk
+  const uint64_t* y[8];        // y_j = x^(2^j): item b at y[j] + b*y_stride[j], level - j
+  uint64_t y_stride[8];
+  double sc[8];
+  uint64_t* G;                 // constant-product scratch, [n][2][level+1][N]
+  uint64_t* stack;
+  uint64_t top, cap;           // words used / available on the stack
+  bool bad;
+
+  uint64_t ct_words(int t) const { return 2ull * (t + 1) * ctx->N; }
+  int64_t rnd(double v) {
+    int64_t r = 0;
+    if (!round_checked(v, &r)) bad = true;
+    return r;
+  }
+  void consts(int t, int64_t k, uint64_t* cv) const {
+    for (int i = 0; i <= t; ++i) cv[i] = signed_mod(k, ctx->mod[i]);
+  }
+
+  // Same recursion as eval(), constants only.
+  void check(const double* c, int nc, int t, double T) {
+    if (nc == 0) return;
+    if (nc <= 2) {
+      if (nc == 2) rnd(c[1] * T * (double)ctx->mod[t + 1] / sc[0]);
+      rnd(c[0] * T);
+      return;
+    }
+    const int j = ceil_log2(nc), g = 1 << (j - 1);
+    const int n_lo = trim_coeffs(c, g), n_hi = nc - g;
+    if (n_lo >= 2) check(c, n_lo, t, T);
+    else if (n_lo == 1) rnd(c[0] * T);
+    if (n_hi == 1) rnd(c[g] * T * (double)ctx->mod[t + 1] / sc[j - 1]);
+    else check(c + g, n_hi, t + 1, T * (double)ctx->mod[t + 1] / sc[j - 1]);
+  }
+
+  // out (= [n][2][t+1][N]) = K * y (limbs 0..t+1 of y, at level ly) rescaled
+  // by q_(t+1), plus acc, plus the constant k0 on component 0.
+  int scaled(const uint64_t* y, uint64_t ystride, int ly, int64_t K, int t, uint64_t* out, const uint64_t* acc,
+             bool has_k0, int64_t k0) {
+    const uint32_t N = ctx->N;
+    TermMacArgs ta;
+    memset(&ta, 0, sizeof(ta));
+    ta.x[0] = y;
+    ta.k[0] = K;
+    ta.nt = 1;
+    ta.out = G;
+    ta.x_bstride = ystride;
+    ta.x_comp = (uint64_t)(ly + 1) * N;
+    ta.out_bstride = ct_words(t + 1);
+    ta.prime = ctx->d_prime;
+    ta.nl = t + 2;
+    ta.log_n = (int)ctx->log_n;
+    int rc = launch_term_mac(ctx, s, ta, n);
+    if (rc) return rc;
+    const uint64_t rs_per = (uint64_t)N * (2 + 2 * (t + 1));
+    if ((rc = ensure_workspace(ctx, rs_per * std::min(n, kMaxChunk)))) return rc;
+    uint64_t cv[64];
+    if (has_k0) consts(t, k0, cv);
+    return rescale_batch(ctx, s, G, ct_words(t + 1), out, ct_words(t), n, t + 1, ctx->ws, ctx->ws_words,
+                         has_k0 ? cv : nullptr, 0, acc);
+  }
+
+  // out = (k0, 0): the trivial ciphertext of a constant
+  int constant(int t, int64_t k0, uint64_t* out) {
+    TermMacArgs ta;
+    memset(&ta, 0, sizeof(ta));
+    ta.nt = 0;
+    ta.out = out;
+    ta.out_bstride = ct_words(t);
+    ta.prime = ctx->d_prime;
+    ta.nl = t + 1;
+    ta.log_n = (int)ctx->log_n;
+    ta.has_add = 1;
+    consts(t, k0, ta.add0);
+    return launch_term_mac(ctx, s, ta, n);
+  }
+
+  // out = p(x) at level t and scale T (nc coefficients, the last nonzero)
+  int eval(const double* c, int nc, int t, double T, uint64_t* out) {
+    if (nc <= 1) return constant(t, nc ? rnd(c[0] * T) : 0, out);
+    if (nc == 2)
+      return scaled(y[0], y_stride[0], level, rnd(c[1] * T * (double)ctx->mod[t + 1] / sc[0]), t, out, nullptr,
+                    true, rnd(c[0] * T));
+    const int j = ceil_log2(nc), g = 1 << (j - 1);
+    const int n_lo = trim_coeffs(c, g), n_hi = nc - g;
+    int rc;
+    const uint64_t* acc = nullptr;
+    bool has_k0 = false;
+    int64_t k0 = 0;
+    if (n_lo >= 2) {
+      if ((rc = eval(c, n_lo, t, T, out))) return rc;
+      acc = out;
+    } else if (n_lo == 1) {
+      has_k0 = true;
+      k0 = rnd(c[0] * T);
+    }
+    const int ly = level - (j - 1);
+    if (n_hi == 1)
+      return scaled(y[j - 1], y_stride[j - 1], ly, rnd(c[g] * T * (double)ctx->mod[t + 1] / sc[j - 1]), t, out, acc,
+                    has_k0, k0);
+    // the high part at (t+1, T q_(t+1) / s_(j-1)), times y_(j-1) at level t+1
+    const int m = t + 1;
+    const uint64_t hw = (uint64_t)n * ct_words(m);
+    if (top + hw > cap) return set_error(CKKS_EINTERNAL, "polynomial evaluation stack exhausted");
+    uint64_t* H = stack + top;
+    top += hw;
+    rc = eval(c + g, n_hi, m, T * (double)ctx->mod[m] / sc[j - 1], H);
+    uint64_t cv[64];
+    if (has_k0) consts(t, k0, cv);
+    if (!rc)
+      rc = mul_relin_rescale(ctx, s, H, y[j - 1], y_stride[j - 1], (uint64_t)(ly + 1) * ctx->N, rlk, out, n, m, true,
+                             has_k0 ? cv : nullptr, acc);
+    top -= hw;
+    return rc;
+  }
+};
+
+}  // namespace
+
+int ckks_poly_eval_tree(ckks_ctx* ctx, const uint64_t* d_ct_in, int batch, int level, double scale,
+                        const double* coeffs, int degree, const uint64_t* d_rlk, uint64_t* d_ct_out, double* out_scale,
+                        ckks_stream_t stream) {
+  CTX_OR_FAIL(ctx);
+  if (!d_ct_in || !d_ct_out || !d_rlk || !coeffs || !out_scale || batch < 0)
+    return set_error(CKKS_EINVAL, "NULL pointer or bad batch");
+  if (misaligned(d_ct_in) || misaligned(d_ct_out) || misaligned(d_rlk))
+    return set_error(CKKS_EINVAL, "device buffers must be 16-byte aligned");
+  int rc = check_level(ctx, level);
+  if (rc) return rc;
+  if (degree < 1 || degree > 64) return set_error(CKKS_ERANGE, "degree must be 1..64");
+  const int depth = ceil_log2(degree + 1);
+  if (level < depth) return set_error(CKKS_ERANGE, "the level must be at least ceil(log2(degree + 1))");
+  if (ctx->K == 0) return set_error(CKKS_EPARAM, "relinearisation needs special primes");
+  const uint32_t N = ctx->N;
+  const int t = level - depth, nc = trim_coeffs(coeffs, degree + 1);
+  TreeEval E;
+  memset(&E, 0, sizeof(E));
+  E.ctx = ctx;
+  E.s = stream;
+  E.rlk = d_rlk;
+  E.level = level;
+  E.sc[0] = scale;
+  for (int j = 1; j < depth; ++j) E.sc[j] = E.sc[j - 1] * E.sc[j - 1] / (double)ctx->mod[level - j + 1];
+  E.check(coeffs, nc, t, scale);
+  if (E.bad) return set_error(CKKS_EINVAL, "a rounded polynomial constant reaches 2^62");
+  *out_scale = scale;
+  if (batch == 0) return CKKS_OK;
+  const uint64_t in_ct = 2ull * (level + 1) * N, out_ct = 2ull * (t + 1) * N;
+  REJECT_OVERLAP(d_ct_out, out_ct * batch, d_ct_in, in_ct * batch, "the input");
+  REJECT_OVERLAP(d_ct_out, out_ct * batch, d_rlk, (uint64_t)ctx->dnum * 2 * (ctx->L + ctx->K) * N, "the key");
+  // per item: the powers y_1 .. y_(depth-1), the constant-product scratch and
+  // one high-part buffer per recursion depth
+  uint64_t pw_off[8], per_item = 0;
+  for (int j = 1; j < depth; ++j) {
+    pw_off[j] = per_item;
+    per_item += 2ull * (level - j + 1) * N;
+  }
+  const uint64_t g_off = per_item;
+  per_item += in_ct;
+  const uint64_t st_off = per_item;
+  per_item += (uint64_t)depth * in_ct;
+  const int chunk = (int)std::max<uint64_t>(1, std::min<uint64_t>({(uint64_t)batch, 16, (1ull << 30) / per_item}));
+  if ((rc = ensure_aux(ctx, chunk * per_item))) return rc;
+  uint64_t* aux = ctx->aux;
+  for (int b0 = 0; b0 < batch && rc == CKKS_OK; b0 += chunk) {
+    const int n = std::min(chunk, batch - b0);
+    E.n = n;
+    E.y[0] = d_ct_in + b0 * in_ct;
+    E.y_stride[0] = in_ct;
+    for (int j = 1; j < depth && rc == CKKS_OK; ++j) {
+      E.y[j] = aux + chunk * pw_off[j];
+      E.y_stride[j] = 2ull * (level - j + 1) * N;
+      rc = mul_relin_rescale(ctx, stream, E.y[j - 1], E.y[j - 1], E.y_stride[j - 1],
+                             (uint64_t)(level - j + 2) * N, d_rlk, aux + chunk * pw_off[j], n, level - j + 1, true,
+                             nullptr);
+    }
+    if (rc) break;
+    E.G = aux + chunk * g_off;
+    E.stack = aux + chunk * st_off;
+    E.top = 0;
+    E.cap = (uint64_t)chunk * depth * in_ct;
+    rc = E.eval(coeffs, nc, t, scale, d_ct_out + b0 * out_ct);
+  }
+  return rc;
 }
 
 int ckks_ptmatvec(ckks_ctx* ctx, const uint64_t* d_x, int n_in, const uint64_t* d_diags, int n_out, int n1, int n2,

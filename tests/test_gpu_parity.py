@@ -354,6 +354,7 @@ def test_overlap_rejected(lib, orc, c3small):
         lambda: lib.ckks_mul_relin_rescale(ctx, x, x, k, x, 1, 23, lib.CKKS_NO_RESCALE),
         lambda: lib.ckks_mul_relin_rescale(ctx, x[:1], x[1:], k, ks[0][:1], 1, 23, lib.CKKS_NO_RESCALE),
         lambda: lib.ckks_poly_eval(ctx, x, 1, 23, 2.0 ** 54, [0.5, 1.0], k, x),
+        lambda: lib.ckks_poly_eval_tree(ctx, x, 1, 23, 2.0 ** 54, [0.5, 1.0, 0.25], k, x),
         lambda: lib.ckks_ptmatvec(ctx, x[:1], 1, empty_dev((1, 1, 2, 2, 24, P.N)), 1, 2, 2, [5], [k], [25], [k],
                                   x[:1], 23, lib.CKKS_NO_RESCALE),
         lambda: lib.ckks_ctmatvec(ctx, x[:1], 1, empty_dev((1, 1, 2, 2, 2, 24, P.N)), 1, 2, 2, k, [5], [k], [25],
@@ -407,6 +408,117 @@ def test_poly_eval_errors(lib, orc, c3small):
                                 (2, [0.0, 2.0 ** 40], lib.CKKS_EINVAL)]:
         with pytest.raises(lib.CKKSError) as e:
             lib.ckks_poly_eval(ctx, x, 1, level, 2.0 ** 54, coeffs, k, y)
+        assert e.value.code == code
+
+
+def _cheb_fit(f, degree, lo, hi):
+    from numpy.polynomial import chebyshev as C, polynomial as Pm
+    p = C.Chebyshev.interpolate(f, degree, domain=[lo, hi]).convert(kind=Pm.Polynomial, domain=[-1, 1],
+                                                                   window=[-1, 1])
+    return [float(v) for v in p.coef]
+
+
+def _gelu_fit():
+    import math
+
+    c = _cheb_fit(lambda u: 2.0 * u * (1.0 + np.vectorize(math.erf)(4.0 * u / math.sqrt(2.0))), 15, -1.0, 1.0)
+    for k in range(3, 16, 2):  # GELU(x) - x/2 is even
+        c[k] = 0.0
+    return c
+
+
+TREE_CASES = [
+    ("exp7_l23", [1.0, 1.0, 0.5, 1 / 6, 1 / 24, 1 / 120, 1 / 720, 1 / 5040], 23, 3, None),
+    ("exp11_m4_0_l23", None, 23, 3, "exp"),                   # x in [-4, 0] directly: powers up to 4^8
+    ("exp11_u_l23", None, 23, 3, "exp_u"),                    # u = x/4 in [-1, 0], fit of exp(4u)
+    ("gelu15_l23", None, 23, 3, "gelu"),
+    ("deg16_l8", [0.1 * (-1) ** k / (k + 1) for k in range(17)], 8, 3, None),
+    ("cubic_l5_b18", [-1.75, 0.3, 1.9, -0.6], 5, 18, None),   # two chunks of items
+    ("affine_l1", [0.25, -1.5], 1, 3, None),
+    ("quad_no_x_l2", [0.1, 0.0, 2.5], 2, 3, None),            # output at level 0
+    ("quad_no_x_l4", [0.1, 0.0, 2.5], 4, 3, None),
+    ("const_only_l1", [0.3, 0.0], 1, 3, None),                # every term zero: a trivial ciphertext
+    ("x_only_l3", [0.0, 1.0], 3, 3, None),
+    ("x8_l6", [0.3, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, -0.7], 6, 3, None),   # one-coefficient high part
+    ("deg31_l12", [0.2 * (k % 3 - 1) for k in range(32)], 12, 2, None),      # zero runs, depth 5
+]
+
+
+@pytest.mark.parametrize("name,coeffs,level,B,fn", TREE_CASES, ids=[c[0] for c in TREE_CASES])
+def test_poly_eval_tree_parity(lib, orc, c3small, name, coeffs, level, B, fn):
+    """Depth-efficient evaluation on B ciphertexts, word for word against the
+    oracle; item 0 a real encryption at scale 2^54 that decrypts to the
+    polynomial (exp: inputs in [-4, 0]; GELU: u = x/4 in [-1, 1])."""
+    from helpers import encrypt_slots, relin_key, secret
+
+    ctx, P = c3small
+    if fn == "exp":
+        coeffs = _cheb_fit(np.exp, 11, -4.0, 0.0)
+    elif fn == "exp_u":
+        coeffs = _cheb_fit(lambda u: np.exp(4.0 * u), 11, -1.0, 0.0)
+    elif fn == "gelu":
+        coeffs = _gelu_fit()
+    d = len(coeffs) - 1
+    depth = lib.tree_depth(d)
+    announce("poly_eval_tree %s degree=%d level=%d batch=%d" % (name, d, level, B))
+    s, s_ntt = secret(orc, P, 12, 192)
+    rlk = relin_key(orc, P, s_ntt, 12, tag="gpu/pt/rlk")
+    scale = 2.0 ** 54
+    cts = S.uniform_limbs(S.stream(level, "gpu/pt/ct"), P.q[: level + 1], P.N, lead=(B, 2))
+    rng = S.stream(level, "gpu/pt/z")
+    if fn == "exp":
+        z = -4.0 * rng.random(P.N // 2)
+    elif fn == "exp_u":
+        z = -rng.random(P.N // 2)
+    else:
+        z = S.uniform_slots(rng, P.N // 2, complex_values=False).real
+    cts[0] = encrypt_slots(orc, P, s_ntt, z.astype(np.complex128), scale, level, 12, "gpu/pt/enc")
+    out = empty_dev((B, 2, level - depth + 1, P.N))
+    s_out = lib.ckks_poly_eval_tree(ctx, to_dev(cts), B, level, scale, coeffs, to_dev(rlk), out)
+    got = to_host(out)
+    ref, ref_scale = orc.poly_eval_tree(P, level, cts, scale, coeffs, rlk)
+    assert s_out == ref_scale == scale
+    assert np.array_equal(got, ref)
+    fit = np.polynomial.polynomial.polyval(z, coeffs)
+    if level - depth == 0 and np.max(np.abs(fit)) >= 0.45:
+        return  # one 54-bit limb at scale 2^54 holds values below 1/2 only
+    dec = orc.decrypt(P, level - depth, got[0], s_ntt, s_out).real
+    # inputs in [-4, 0] taken directly: the high part's absolute noise (about
+    # 1e-12 after relinearisations at N = 2^12, h = 192) is multiplied by x^8,
+    # up to 65536; with |x| <= 1 every intermediate stays below 1
+    tol = 2e-7 if fn == "exp" else 2 ** -28
+    assert np.max(np.abs(dec - fit)) < tol
+    if fn == "exp":
+        assert np.max(np.abs(dec - np.exp(z))) < tol
+    if fn == "exp_u":
+        assert np.max(np.abs(dec - np.exp(4.0 * z))) < 1e-8
+
+
+def test_poly_eval_tree_full_size(lib, orc):
+    """N = 2^16 with the C3 primes: degree 5 (depth 3) on one ciphertext at
+    level 23, every word against the oracle."""
+    ctx, P = config_pair(lib, orc, "C3")
+    announce("poly_eval_tree N=2^16 degree 5")
+    coeffs = [0.5, -1.0, 0.25, 0.125, -0.5, 0.0625]
+    rlk = S.uniform_limbs(S.stream(3, "gpu/ptf/k"), P.mods, P.N, lead=(P.dnum, 2))
+    cts = S.uniform_limbs(S.stream(3, "gpu/ptf/ct"), P.q, P.N, lead=(1, 2))
+    out = empty_dev((1, 2, 24 - lib.tree_depth(5), P.N))
+    lib.ckks_poly_eval_tree(ctx, to_dev(cts), 1, 23, 2.0 ** 54, coeffs, to_dev(rlk), out)
+    ref, _ = orc.poly_eval_tree(P, 23, cts, 2.0 ** 54, coeffs, rlk)
+    assert np.array_equal(to_host(out), ref)
+
+
+def test_poly_eval_tree_errors(lib, orc, c3small):
+    ctx, P = c3small
+    x = empty_dev((1, 2, 4, P.N))
+    k = empty_dev((3, 2, 32, P.N))
+    y = empty_dev((1, 2, 4, P.N))
+    for level, coeffs, code in [(3, [1.0] * 10, lib.CKKS_ERANGE),    # degree 9: depth 4 > level 3
+                                (3, [1.0], lib.CKKS_ERANGE),         # degree 0
+                                (3, [0.5] * 66, lib.CKKS_ERANGE),    # degree 65
+                                (3, [0.0, 2.0 ** 40], lib.CKKS_EINVAL)]:
+        with pytest.raises(lib.CKKSError) as e:
+            lib.ckks_poly_eval_tree(ctx, x, 1, level, 2.0 ** 54, coeffs, k, y)
         assert e.value.code == code
 
 
@@ -601,6 +713,7 @@ def test_empty_batches(lib, orc, c3small):
     lib.ckks_rescale(ctx, x, y, 0, 23)
     lib.ckks_mul_relin_rescale(ctx, x, x, k, y, 0, 23)
     lib.ckks_poly_eval(ctx, x, 0, 23, 2.0 ** 54, [0.5, 1.0], k, y)
+    lib.ckks_poly_eval_tree(ctx, x, 0, 23, 2.0 ** 54, [0.5, 1.0, 0.25], k, y)
     torch.cuda.synchronize()
     assert bool((y == 7).all())
 

@@ -90,23 +90,24 @@ def test_noalloc_small_params_against_oracle(lib, orc):
 
 def test_noalloc_limits_and_checks(lib, orc):
     torch = torch_cuda()
-    # 32 + 16 primes, dnum 2 at N = 2^16: one ciphertext at level 31 needs
-    # 144 MiB of workspace (more than the 128 MiB scratch); at level 20, 105 MiB
-    q = lib.ckks_find_primes(16, 54, 32)
+    # 48 + 16 primes, dnum 3 at N = 2^16: one ciphertext at level 47 needs
+    # N x (48 + 3 x 64 + 2 x 16 + 2 x 48) words = 184 MiB of workspace (more
+    # than the 128 MiB scratch); at level 20 (two digits), 84.5 MiB
+    q = lib.ckks_find_primes(16, 54, 48)
     p = lib.ckks_find_primes(16, 60, 16)
-    ctx = lib.Context(16, q, p, 2)
+    ctx = lib.Context(16, q, p, 3)
     N = 1 << 16
-    key = torch.zeros((2, 2, 48, N), dtype=torch.int64, device="cuda")
-    x = torch.zeros((1, 2, 32, N), dtype=torch.int64, device="cuda")
+    key = torch.zeros((3, 2, 64, N), dtype=torch.int64, device="cuda")
+    x = torch.zeros((1, 2, 48, N), dtype=torch.int64, device="cuda")
     y = torch.empty_like(x)
     with pytest.raises(lib.CKKSError) as e:
-        lib.ckks_rotate_noalloc(ctx, x, y, 1, 31, [5], [key])
+        lib.ckks_rotate_noalloc(ctx, x, y, 1, 47, [5], [key])
     assert e.value.code == lib.CKKS_ERANGE
     assert "scratch" in lib.ckks_last_error()
     lib.ckks_rotate_noalloc(ctx, x[:, :, :21].contiguous(), y[:, :, :21].contiguous(), 1, 20, [5], [key])
     torch.cuda.synchronize()
     # the same argument checks as ckks_rotate
-    for args, code in [((1, 32, [5], [key]), lib.CKKS_ERANGE), ((1, 20, [6], [key]), lib.CKKS_EINVAL)]:
+    for args, code in [((1, 48, [5], [key]), lib.CKKS_ERANGE), ((1, 20, [6], [key]), lib.CKKS_EINVAL)]:
         with pytest.raises(lib.CKKSError) as e:
             lib.ckks_rotate_noalloc(ctx, x, y, *args)
         assert e.value.code == code
