@@ -31,15 +31,20 @@ if ROOT not in sys.path:
 
 METRIC = "HRot (hybrid key-switch) ops/s at N=2^16,L=24,dnum=3; NTT GB/s vs HBM peak"
 HBM_PEAK_GBPS = 8000.0
-# int32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 BYTES_PER_HROT = 150_994_944  # ciphertext in (24 MiB) + key (96 MiB) + ciphertext out (24 MiB)
 # modmul-class operations per HRot at level 23: 83.9M butterflies (160 limb
 # transforms), 44.0M ModUp, 16.8M inner product, 32.5M ModDown
 OPS_PER_HROT = 177_200_000
-# limbs the dominant kernel reads or writes per ciphertext at level 23: 192 key
-# limbs (3 digits x 2 x 32), 72 converted limbs, 24 input limbs, 64 accumulator limbs
-IP_LIMBS_PER_ITEM = 192 + 72 + 24 + 64
+# limbs of 2^16 words each kernel family reads or writes per ciphertext at
+# level 23 (its own I/O, intermediates included)
+# ciphertexts per launch of the dominant kernel (the key switch's chunk)
+DOMINANT_ITEMS_PER_LAUNCH = 4
+KERNEL_IO_LIMBS = {
+    # per ciphertext limb: 2 converted limbs (the other digits) + 1 input limb
+    # (its own digit) + 3 x 2 key limbs + 2 ModDown limbs + 1 limb of tau_g(c0)
+    # read, 2 output limbs written: 24 x (2 + 1 + 6 + 2 + 1 + 2)
+    "comb_ip": 48 + 24 + 144 + 48 + 24 + 48,
+}
 
 
 def log(msg):
@@ -49,7 +54,7 @@ def log(msg):
 # Sources the dominant kernel is compiled from: HBM traffic taken with
 # rocprofv3 counters is reported only while these are unchanged.
 KERNEL_SOURCES = ["keyswitch.hip", "ntt_core.h", "arith.h", "internal.h", "kernels.h", "automorph.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ntt_row_ip_c3_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "comb_ip_c3_traffic.txt")
 
 
 def kernel_sources_sha256():
@@ -81,43 +86,26 @@ def measured_traffic():
         return None
 
 
-def copy_probe(torch):
-    """A plain device copy of 1 GiB, three times: the reference reading for
-    the FETCH_SIZE / WRITE_SIZE counters (each copy reads and writes 2^30 B)."""
-    a = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    del a, b
+def copy_probe(lib):
+    """The library's plain device copy of 1 GiB (include/ckks_probe.h, probe
+    "copy"; 16 launches): the reference reading for the FETCH_SIZE /
+    WRITE_SIZE counters, each launch reading and writing 2^30 B."""
+    lib.ckks_probe_rate("copy", copy_bytes=1 << 30)
 
 
-def copy_bandwidth(torch, reps=10):
-    """Measured device-copy rate (bytes read + written per second) of 1 GiB."""
-    a = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    gbps = 2 * (1 << 30) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del a, b
-    torch.cuda.empty_cache()
-    return gbps
+def cpu_baseline(cfg, q, p, cts, gs, keys, target_s, got):
+    """The CPU oracle on a bounded sample of the batch (same words), and the
+    parity of the GPU's output words for the items the sample computed."""
+    import numpy as np
 
-
-def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
-    """The CPU oracle on a bounded sample of the batch (same words)."""
     import oracle
 
     P = oracle.Params(cfg["log_n"], q, p, cfg["dnum"])
     level = cfg["L"] - 1
     t0 = time.perf_counter()
-    oracle.rotate_batch(P, level, cts[:1], gs[:1], keys[:1])
+    ref0 = oracle.rotate_batch(P, level, cts[:1], gs[:1], keys[:1])
     t1 = time.perf_counter() - t0
+    checked = {0: int(np.count_nonzero(ref0[0] != got[0]))}
     # items 1..B-1 of the batch, cycled until about target_s of work
     k = max(1, int(round(target_s / max(t1, 1e-3))))
     B = len(gs)
@@ -126,8 +114,10 @@ def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
         lo = 1 + done % (B - 1)
         hi = min(B, lo + (k - done))
         t0 = time.perf_counter()
-        oracle.rotate_batch(P, level, cts[lo:hi], gs[lo:hi], keys[lo:hi])
+        ref = oracle.rotate_batch(P, level, cts[lo:hi], gs[lo:hi], keys[lo:hi])
         dt += time.perf_counter() - t0
+        for i in range(lo, hi):
+            checked[i] = int(np.count_nonzero(ref[i - lo] != got[i]))
         done += hi - lo
     cores = oracle.num_threads()
     # one-thread figure on one rotation of the sample
@@ -136,6 +126,13 @@ def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
     oracle.rotate_batch(P, level, cts[1:2], gs[1:2], keys[1:2])
     t_one = time.perf_counter() - t0
     oracle.set_num_threads(cores)
+    parity = {
+        "status": "bit-exact" if not any(checked.values()) else "MISMATCH",
+        "items_checked": sorted(checked),
+        "words_checked": len(checked) * int(got[0].size),
+        "mismatched_words": int(sum(checked.values())),
+        "against": "CPU oracle (oracle/ckks_oracle.c), same input words, every word of each checked item",
+    }
     return {
         "value": k / dt,
         "unit": "HRot/s",
@@ -145,7 +142,7 @@ def cpu_baseline(cfg, q, p, cts, gs, keys, target_s):
                   "plain __int128 %% oracle with OpenMP over limbs/coefficients; %.1f s" % (k, B - 1, dt),
         "value_1thread": round(1.0 / t_one, 4),
         "cpu_model": cpu_model(),
-    }
+    }, parity
 
 
 def cpu_model():
@@ -170,13 +167,31 @@ def main():
     ap.add_argument("--no-ntt", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the C4 / C5 timings")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="first copy 1 GiB three times (reference for HBM byte counters)")
+                    help="first copy 1 GiB with the library's probe copy kernel (reference for HBM byte counters)")
     ap.add_argument("--ntt-only", action="store_true",
                     help="time only the C2 batched NTT and print its figures (for profiling the transform)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the batch's chunks one after another on one stream (CKKS_LANES=1): kernels do not "
+                         "overlap, for per-kernel counters")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the calibration probes (the ALU ceiling and copy rate are then not reported)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print a per-kernel markdown table from the rocprofv3 CSV output under DIR (kernel trace "
+                         "and counter collection runs) and exit")
+    ap.add_argument("--traffic-out", metavar="FILE",
+                    help="with --summarize-counters: also write the dominant kernel's scaled FETCH_SIZE / "
+                         "WRITE_SIZE bytes per launch to FILE (read back by later runs while its sources match)")
+    ap.add_argument("--traffic-command", default="",
+                    help="the counter command recorded in the --traffic-out file")
     ap.add_argument("--probe", action="store_true",
                     help="measure the device calibration probes (instruction and modular-primitive rates, copy "
                          "rate by size) and print them as one JSON line")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.traffic_out, args.traffic_command))
+        return 0
+    if args.serial:
+        os.environ["CKKS_LANES"] = "1"  # read by the library at its first batched call
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(rotation batches shard by ciphertext with no exchange; see the design notes). "
@@ -194,7 +209,7 @@ def main():
     level, B = L - 1, cfg["batch"]
     torch.cuda.set_device(0)
     if args.copy_probe:
-        copy_probe(torch)
+        copy_probe(lib)
     if args.probe:
         print(json.dumps({"probe": calibration(lib, copy_sizes_mib=PROBE_COPY_MIB)}), flush=True)
         return 0
@@ -221,71 +236,83 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # headline: K steps, each bracketed by HIP events on the call's stream, no
+    # tracing; the reported step time is the median, the total is kept too
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms_median = step_ms[len(step_ms) // 2]
+    ms_mean = sum(step_ms) / len(step_ms)
+    value = B / (ms_median / 1e3)
+    log("HRot/s %.1f  (median %.3f ms, mean %.3f ms per batch of %d)" % (value, ms_median, ms_mean, B))
+
+    # device ceilings measured on this GPU: the library's lazy forward
+    # butterfly rate is the modmul-class operation rate R_mm
+    cal = None if args.no_calibration else calibration(lib, copy_sizes_mib=(128, 1024))
+    r_mm = cal["butterfly_ct"] * 1e12 if cal else None
+    copy_gbps = cal["copy_GBps"]["1024"] if cal else None
+
+    # dominant kernel: a second pass of K steps with HIP events around each of
+    # its launches (recorded by the library on the stream it launches on)
     trace = lib.KernelTrace(ctx, lib.DOMINANT_KERNEL)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
     for _ in range(args.steps):
         step()
-    e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
     kstat = trace.read()
     trace.close()
-    ms_step = ms / args.steps
-    value = B * args.steps / (ms / 1e3)
-    log("HRot/s %.1f  (%.3f ms per batch of %d)" % (value, ms_step, B))
-
-    # dominant kernel roofline, from the events recorded around each of its
-    # launches: the bound is whichever of its algorithmic ALU work (at the
-    # int32 VALU peak) and algorithmic bytes (at the HBM peak) takes longer
     roof = None
     if kstat["launches"]:
         avg_s = kstat["total_ms"] / kstat["launches"] / 1e3
-        per_launch = kstat["alg_units"] / kstat["launches"]
-        ops = per_launch * kstat["ops_per_unit"]
-        alg_bytes = B * args.steps / kstat["launches"] * IP_LIMBS_PER_ITEM * N * 8
-        alu_tops = ops / avg_s / 1e12
+        items_per_launch = B * args.steps / kstat["launches"]
+        alg_bytes = items_per_launch * BYTES_PER_HROT      # the survey's per-HRot bytes x HRots per launch
+        ops = kstat["alg_units"] / kstat["launches"]       # modmul-class operations per launch
         hbm_gbps = alg_bytes / avg_s / 1e9
-        hbm_bound = alg_bytes / (HBM_PEAK_GBPS * 1e9) > ops / (VALU_PEAK_TOPS * 1e12)
+        alu_frac = ops / avg_s / r_mm if r_mm else None
+        hbm_bound = r_mm is None or alg_bytes / (HBM_PEAK_GBPS * 1e9) >= ops / r_mm
         roof = {
             "kernel": kstat["name"],
             "bound": "hbm" if hbm_bound else "alu",
-            "achieved": round(hbm_gbps if hbm_bound else alu_tops, 3),
-            "peak": HBM_PEAK_GBPS if hbm_bound else round(VALU_PEAK_TOPS, 2),
-            "unit": "GB/s" if hbm_bound else "Tops/s",
-            "frac": round(hbm_gbps / HBM_PEAK_GBPS if hbm_bound else alu_tops / VALU_PEAK_TOPS, 4),
+            "achieved": round(hbm_gbps, 2) if hbm_bound else round(ops / avg_s / 1e12, 4),
+            "peak": HBM_PEAK_GBPS if hbm_bound else round(r_mm / 1e12, 4),
+            "unit": "GB/s" if hbm_bound else "T modmul-class ops/s",
+            "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4) if hbm_bound else round(alu_frac, 4),
             "traffic": measured_traffic(),
+            "items_per_launch": items_per_launch,
             "alg_bytes_per_launch": int(alg_bytes),
-            "alg_ops_per_launch": "%d %s x %d int32 VALU ops" % (per_launch, kstat["unit_name"],
-                                                               kstat["ops_per_unit"]),
-            "alu_frac": round(alu_tops / VALU_PEAK_TOPS, 4),
-            "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+            "kernel_io_bytes_per_launch": int(items_per_launch * KERNEL_IO_LIMBS[kstat["name"]] * N * 8),
+            "alg_ops_per_launch": int(ops),
+            "alu_frac": round(alu_frac, 4) if alu_frac is not None else None,
             "avg_launch_us": round(avg_s * 1e6, 2),
             "launches": kstat["launches"],
-            "note": "chunks of the batch run on two streams at once, so a launch's duration includes "
-                    "co-running kernels of the other stream; alu_roofline_frac and hbm_roofline_frac "
-                    "cover the whole step",
+            "note": "achieved = %d B per HRot x %g HRots per launch / average launch time, from a second pass of "
+                    "%d steps with HIP events around each launch (the headline pass runs untraced); chunks run "
+                    "on two streams at once, so a launch's time includes co-running kernels of the other stream"
+                    % (BYTES_PER_HROT, items_per_launch, args.steps),
         }
 
     ntt = None
     if not args.no_ntt:
         ntt = ntt_bench(lib, S, torch, np, args)
+        for d in ("fwd", "inv"):
+            ntt[d + "_copy_frac"] = round(ntt[d + "_GBps"] / copy_gbps, 4) if copy_gbps else None
 
     workloads = None
     if not args.no_workloads:
         workloads = workload_bench(lib, S, torch, ctx, q, p, stream)
         workloads.update(c1_bench(lib, S, torch, np, stream))
-    copy_gbps = copy_bandwidth(torch)
-    if ntt:
-        for d in ("fwd", "inv"):
-            ntt[d + "_copy_frac"] = round(ntt[d + "_GBps"] / copy_gbps, 4)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(cfg, q, p, cts, gs, keys_h, args.cpu_seconds)
+        got = d_out.cpu().numpy().view(np.uint64)
+        cpu, parity = cpu_baseline(cfg, q, p, cts, gs, keys_h, args.cpu_seconds, got)
 
     out = {
         "metric": METRIC,
@@ -294,7 +321,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_median, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
+        "timed_wall_s": round(wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -307,9 +336,12 @@ def main():
         },
         "roofline": roof,
         "hbm_roofline_frac": round(value * BYTES_PER_HROT / 1e9 / HBM_PEAK_GBPS, 4),
-        "alu_roofline_frac": round(value * OPS_PER_HROT * lib.OPS_PER_MODMUL / 1e12 / VALU_PEAK_TOPS, 4),
-        "copy_GBps": round(copy_gbps, 1),
-        "hbm_frac_vs_copy": round(value * BYTES_PER_HROT / 1e9 / copy_gbps, 4),
+        "alu_roofline_frac": round(value * OPS_PER_HROT / r_mm, 4) if r_mm else None,
+        "r_mm_Tops": round(r_mm / 1e12, 4) if r_mm else None,
+        "copy_GBps": copy_gbps,
+        "hbm_frac_vs_copy": round(value * BYTES_PER_HROT / 1e9 / copy_gbps, 4) if copy_gbps else None,
+        "calibration": cal,
+        "parity": parity,
         "ntt": ntt,
         "workloads": workloads,
         "cpu_baseline": cpu,
@@ -317,6 +349,75 @@ def main():
     print(json.dumps(out), flush=True)
     ctx.close()
     return 0
+
+
+def summarize_counters(root, traffic_out=None, command=""):
+    """Markdown table per kernel from the rocprofv3 CSVs under root: every
+    *_kernel_stats.csv (durations) and *_counter_collection.csv (counters,
+    summed per dispatch and averaged over the kernel's dispatches).  FETCH_SIZE
+    and WRITE_SIZE are scaled by the factors that make the library's probe
+    copy kernel (bench.py --copy-probe: 1 GiB read and written) read and write
+    its own size, and reported in MB per dispatch.  With traffic_out, the
+    dominant kernel's scaled bytes per dispatch are also written there, in the
+    form measured_traffic() reads, tagged with the hash of its sources."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    dur = {}
+    for f in glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            dur[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    per = defaultdict(lambda: defaultdict(float))  # (kernel, counter) -> dispatch -> value
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            per[(r["Kernel_Name"], r["Counter_Name"])][(f, r["Dispatch_Id"])] += float(r["Counter_Value"])
+    avg = {k: sum(v.values()) / len(v) for k, v in per.items()}
+    kernels = sorted({k for k, _ in avg} | set(dur), key=lambda k: -dur.get(k, (0, 0))[0] * dur.get(k, (0, 0))[1])
+    copy = next((k for k, _ in avg if "copy_kernel" in k), "copy_kernel")
+    fscale = wscale = 1.0
+    # the copy probe copies 1 GiB: 1048576 KiB read and written
+    if (copy, "FETCH_SIZE") in avg:
+        fscale = 1048576.0 / avg[(copy, "FETCH_SIZE")]
+    if (copy, "WRITE_SIZE") in avg:
+        wscale = 1048576.0 / avg[(copy, "WRITE_SIZE")]
+    names = sorted({c for _, c in avg})
+    head = ("| Kernel | Calls | Average (us) | " + " | ".join(names) +
+            " | HBM read per dispatch (MB) | HBM written per dispatch (MB) |")
+    lines = [head, "|" + "---|" * (head.count("|") - 1)]
+    for k in kernels:
+        calls, us = dur.get(k, (0, float("nan")))
+        vals = ["%.4g" % avg[(k, c)] if (k, c) in avg else "" for c in names]
+        rd = "%.1f" % (avg[(k, "FETCH_SIZE")] * fscale * 1024 / 1e6) if (k, "FETCH_SIZE") in avg else ""
+        wr = "%.1f" % (avg[(k, "WRITE_SIZE")] * wscale * 1024 / 1e6) if (k, "WRITE_SIZE") in avg else ""
+        lines.append("| `%s` | %d | %.1f | %s | %s | %s |" % (k[:90], calls, us, " | ".join(vals), rd, wr))
+    lines.append("")
+    lines.append("FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f (from %s)" % (fscale, wscale, copy))
+    if traffic_out:
+        import private_rns_ckks_amd as lib
+
+        dom = next(k for k in kernels if lib.DOMINANT_KERNEL + "_kernel" in k)
+        f_b = avg[(dom, "FETCH_SIZE")] * fscale * 1024
+        w_b = avg[(dom, "WRITE_SIZE")] * wscale * 1024
+        n_f = len(per[(dom, "FETCH_SIZE")])
+        items = DOMINANT_ITEMS_PER_LAUNCH
+        alg = items * KERNEL_IO_LIMBS[lib.DOMINANT_KERNEL] * (1 << 16) * 8
+        with open(traffic_out, "w") as f:
+            f.write("# HBM traffic per launch of %s on the HRot batch (N=2^16, L=24 + K=8, dnum=3,\n" % dom[:60])
+            f.write("# level 23, 32 ciphertexts; launches of %d ciphertexts), %d dispatches averaged.\n" % (items, n_f))
+            f.write("# Command (MI355X, repository root; FETCH_SIZE and WRITE_SIZE each in its own run):\n")
+            f.write("#   %s\n" % command)
+            f.write("# Scale: the probe copy of 1 GiB reads FETCH_SIZE x %.4f and writes WRITE_SIZE x %.4f\n"
+                    % (fscale, wscale))
+            f.write("# of its size, so the counters are multiplied by those factors.  Algorithmic bytes\n")
+            f.write("# per launch: %d items x %d limbs x 2^16 words x 8 B (the kernel's own reads and\n"
+                    % (items, KERNEL_IO_LIMBS[lib.DOMINANT_KERNEL]))
+            f.write("# writes).  bench.py reports traffic while the sources hash to sources_sha256.\n")
+            f.write("sources_sha256: %s\n" % kernel_sources_sha256())
+            f.write("fetch_bytes_per_launch: %d\n" % round(f_b))
+            f.write("write_bytes_per_launch: %d\n" % round(w_b))
+            f.write("algorithmic_bytes_per_launch: %d\n" % alg)
+    return "\n".join(lines)
 
 
 PROBE_COPY_MIB = (16, 32, 64, 128, 192, 256, 384, 512, 1024, 2048)
