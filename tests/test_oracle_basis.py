@@ -37,9 +37,15 @@ def small_c3(orc, log_n=8):
     return orc.Params.generate(log_n, c["L"], c["q_bits"], c["K"], c["p_bits"], c["dnum"])
 
 
-@pytest.mark.parametrize("level", [23, 12, 7, 20])
-def test_modup_is_plain_fast_basis_conversion(orc, level):
-    P = small_c3(orc)
+def wide_params(orc, log_n=8):
+    """Primes at the top of the supported range: 6 x 62-bit ciphertext primes,
+    2 x 61-bit special primes, dnum 3."""
+    return orc.Params.generate(log_n, 6, 62, 2, 61, 3)
+
+
+@pytest.mark.parametrize("level,wide", [(23, False), (12, False), (7, False), (20, False), (5, True), (2, True)])
+def test_modup_is_plain_fast_basis_conversion(orc, level, wide):
+    P = wide_params(orc) if wide else small_c3(orc)
     x = S.uniform_limbs(S.stream(level, "modup/x"), P.q[: level + 1], P.N)
     ext = P.ext_mods(level)
     for j in range(P.beta(level)):
@@ -82,9 +88,9 @@ def test_moddown_single_special_prime_is_exact_rounding(orc):
         assert int(got[c]) == r
 
 
-@pytest.mark.parametrize("level", [23, 9])
-def test_moddown_centered_identity(orc, level):
-    P = small_c3(orc)
+@pytest.mark.parametrize("level,wide", [(23, False), (9, False), (5, True)])
+def test_moddown_centered_identity(orc, level, wide):
+    P = wide_params(orc) if wide else small_c3(orc)
     ext = P.ext_mods(level)
     psis = P.psi[: level + 1] + P.psi[P.L:]
     acc_coeff = S.uniform_limbs(S.stream(level, "md/acc8"), ext, P.N)
@@ -107,9 +113,9 @@ def test_moddown_centered_identity(orc, level):
         assert (int(O[c]) * Pp - (Xc - eps)) % Ql == 0
 
 
-@pytest.mark.parametrize("level", [23, 1])
-def test_rescale_is_exact_rounding(orc, level):
-    P = small_c3(orc)
+@pytest.mark.parametrize("level,wide", [(23, False), (1, False), (5, True)])
+def test_rescale_is_exact_rounding(orc, level, wide):
+    P = wide_params(orc) if wide else small_c3(orc)
     ct_coeff = S.uniform_limbs(S.stream(level, "rs/ct"), P.q[: level + 1], P.N, lead=(2,))
     ct = orc.ntt_params(P, ct_coeff)
     out = orc.rescale(P, level, ct)

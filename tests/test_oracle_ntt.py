@@ -46,7 +46,7 @@ def negacyclic(a, b, m):
 
 
 @pytest.mark.parametrize("log_n", [1, 2, 3, 5, 7, 9])
-@pytest.mark.parametrize("bits", [30, 54, 60])
+@pytest.mark.parametrize("bits", [30, 54, 60, 61, 62])
 def test_forward_matches_direct_evaluation(orc, log_n, bits):
     m = orc.gen_primes(16, bits, 1)[0]  # 1 mod 2^17, hence 1 mod 2N for every N here
     psi = orc.min_psi(m, log_n)

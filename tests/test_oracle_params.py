@@ -29,7 +29,7 @@ def composite_witness(c):
     return any(pow(b, c - 1, c) != 1 for b in (2, 3, 5, 7, 11, 13))
 
 
-CASES = [(12, 30, 4), (12, 60, 1), (16, 54, 24), (16, 60, 8), (10, 54, 3)]
+CASES = [(12, 30, 4), (12, 60, 1), (16, 54, 24), (16, 60, 8), (10, 54, 3), (12, 62, 3), (16, 61, 2)]
 
 
 @pytest.mark.parametrize("log_n,bits,count", CASES)

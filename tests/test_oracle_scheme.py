@@ -56,6 +56,26 @@ def test_keyswitch_noise_free_bound(orc, level):
     assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h)
 
 
+@pytest.mark.parametrize("level", [5, 2])
+def test_keyswitch_noise_free_bound_wide_primes(orc, level):
+    """The same bound with primes at the top of the supported range (62-bit
+    ciphertext and 61-bit special primes)."""
+    P = orc.Params.generate(9, 6, 62, 2, 61, 3)
+    h = 64
+    s, s_ntt = secret(orc, P, 6, h)
+    g = P.galois(5)
+    evk = galois_key(orc, P, s_ntt, g, 6, "ksw", zero_error=True)
+    d = S.uniform_limbs(S.stream(level, "ksw/d"), P.q[: level + 1], P.N)
+    k = orc.keyswitch(P, level, d, evk)
+    mods = P.q[: level + 1]
+    s_from = orc.automorph_ntt(s_ntt, P.log_n, g)[: level + 1]
+    t1 = np.array([[int(a) * int(b) % m for a, b in zip(k[1, i], s_ntt[i])] for i, m in enumerate(mods)], dtype=np.uint64)
+    t2 = np.array([[int(a) * int(b) % m for a, b in zip(d[i], s_from[i])] for i, m in enumerate(mods)], dtype=np.uint64)
+    e = np.array([[(int(a) + int(b) - int(c)) % m for a, b, c in zip(k[0, i], t1[i], t2[i])]
+                  for i, m in enumerate(mods)], dtype=np.uint64)
+    assert centered_max(orc, P, e, level) <= (P.K / 2) * (1 + h)
+
+
 def test_hoisted_rotation_noise_free_bound(orc):
     """Hoisted rotations are key switches of tau_g(c1): with error-free keys
     k0 + k1*s = tau_g(c0) + tau_g(c1)*tau_g(s) up to the ModDown rounding."""
