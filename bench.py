@@ -499,7 +499,21 @@ def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
         lib.ckks_poly_eval(ctx, a_top, B, level, 2.0 ** 54, coeffs, rlk, pe_out, stream)
 
     res["poly_eval_deg7_ms"] = round(timed(torch, stream, run_pe, reps), 3)
-    del a, b, a_top, keys, bufs, pe_out
+    # the same polynomial, and a degree-15 one, by the depth-efficient split
+    # (depth 3 and 4; 5 and 10 ciphertext products per item, against 6 and 14 for Horner)
+    c15 = [(-1) ** k / (k + 1) for k in range(16)]
+    tree_out = {d: torch.empty((B, 2, level + 1 - lib.tree_depth(d), N), dtype=torch.int64, device="cuda")
+                for d in (7, 15)}
+
+    def run_tree7():
+        lib.ckks_poly_eval_tree(ctx, a_top, B, level, 2.0 ** 54, coeffs, rlk, tree_out[7], stream)
+
+    def run_tree15():
+        lib.ckks_poly_eval_tree(ctx, a_top, B, level, 2.0 ** 54, c15, rlk, tree_out[15], stream)
+
+    res["poly_eval_tree_deg7_ms"] = round(timed(torch, stream, run_tree7, reps), 3)
+    res["poly_eval_tree_deg15_ms"] = round(timed(torch, stream, run_tree15, reps), 3)
+    del a, b, a_top, keys, bufs, pe_out, tree_out
     torch.cuda.empty_cache()
     # attention output A x V with encrypted weights (ckks_ctmatvec)
     av = S.CONFIGS["AV"]
@@ -521,7 +535,8 @@ def workload_bench(lib, S, torch, ctx, q, p, stream, reps=3):
     torch.cuda.empty_cache()
     res["note"] = "C4: one ckks_ptmatvec call; C5: ckks_mul_relin_rescale on 48 pairs + 15 accumulate rotations " \
                   "of the 48 products (768 key switches); poly_eval: degree-7 Horner evaluation on 48 ciphertexts " \
-                  "at level 23 (6 products each); av: one ckks_ctmatvec call (A x V, 3 inputs, 3 outputs, 576 " \
+                  "at level 23 (6 products each, depth 7); poly_eval_tree: the same degree-7 polynomial and a " \
+                  "degree-15 one by the depth-efficient split (depth 3 and 4); av: one ckks_ctmatvec call (A x V, 3 inputs, 3 outputs, 576 " \
                   "ciphertext diagonals at level 12, 24 relinearisations); c1: one ckks_rotate of a C1 " \
                   "ciphertext (N=2^12) by 1 and by 7, time per rotation over 20 reps; device-generated uniform " \
                   "words, %d timed reps" % reps

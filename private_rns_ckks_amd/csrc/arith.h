@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ckks {
 
 struct U128 {
@@ -141,6 +143,13 @@ __device__ __forceinline__ uint64_t mont_mul_lazy(uint64_t a, uint64_t b, uint64
   return hi + mulhi64(u, m) + (lo != 0 ? 1 : 0);
 }
 
+// Lazy Montgomery products are below 2m; a running sum reduced to [0, m)
+// after every k products stays below (2k + 1) m < 2^64 for k = 4 when
+// m < 2^60, 3 when m < 2^61 and 1 when m < 2^62.
+__host__ __device__ inline int mont_fold(uint64_t m) {
+  return m < (1ull << 60) ? 4 : m < (1ull << 61) ? 3 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // Exact dot products of residues below 2^60 without carry chains.
 // Each operand is split into 30-bit halves (v = vh*2^30 + vl); a product then
@@ -190,13 +199,6 @@ __device__ __forceinline__ uint64_t reduce128_lazy(U128 x, uint64_t q, uint64_t 
   return s >= q ? s - q : s;
 }
 
-// Running sum of products folded every 8 terms (the Acc3 capacity).
-struct DotMod {
-  Acc3 A;
-  int n;
-  uint64_t r;
-  __device__ __forceinline__ DotMod() : A{0, 0, 0}, n(0), r(0) {}
-};
 
 __device__ __forceinline__ uint64_t acc3_reduce(const Acc3& A, const uint64_t q, uint64_t r64, uint64_t r64p,
                                                 uint64_t inv1) {
@@ -218,6 +220,53 @@ __device__ __forceinline__ uint64_t sub_mod(uint64_t a, uint64_t b, uint64_t q) 
 __device__ __forceinline__ uint64_t mul_mod(uint64_t a, uint64_t b, uint64_t q, uint64_t r64, uint64_t r64p,
                                             uint64_t inv1) {
   return reduce128(mul_wide(a, b), q, r64, r64p, inv1);
+}
+
+// Exact dot products in two operand forms, chosen per parameter set: NARROW
+// (every operand below 2^60: 30-bit halves and Acc3 column sums) and WIDE
+// (operands below 2^62: full 64x64 -> 128-bit products; 8 of them sum below
+// 2^127, within reduce128's range).  Either form takes 8 products between
+// reductions.  Tables of constants store them as lo30 | hi30 << 32 (hi30 up
+// to 32 bits for constants below 2^62).
+struct SplitN {
+  uint32_t l, h;
+};
+struct SplitWd {
+  uint64_t v;
+};
+template <bool WIDE>
+using Split = typename std::conditional<WIDE, SplitWd, SplitN>::type;
+template <bool WIDE>
+using AccT = typename std::conditional<WIDE, U128, Acc3>::type;
+
+template <bool WIDE>
+__device__ __forceinline__ Split<WIDE> split_word(uint64_t v) {
+  if constexpr (WIDE) return SplitWd{v};
+  else return SplitN{lo30(v), hi30(v)};
+}
+template <bool WIDE>
+__device__ __forceinline__ Split<WIDE> split_table(uint64_t cw) {
+  if constexpr (WIDE) return SplitWd{(cw & 0x3fffffffull) | ((cw >> 32) << 30)};
+  else return SplitN{(uint32_t)cw, (uint32_t)(cw >> 32)};
+}
+template <bool WIDE>
+__device__ __forceinline__ void acc_mac(AccT<WIDE>& A, const Split<WIDE>& x, const Split<WIDE>& c) {
+  if constexpr (WIDE) mac(A, x.v, c.v);
+  else acc3_mac(A, x.l, x.h, c.l, c.h);
+}
+// the sum mod q, in [0, q)
+template <bool WIDE>
+__device__ __forceinline__ uint64_t acc_reduce(const AccT<WIDE>& A, uint64_t q, uint64_t r64, uint64_t r64p,
+                                               uint64_t inv1) {
+  if constexpr (WIDE) return reduce128(A, q, r64, r64p, inv1);
+  else return acc3_reduce(A, q, r64, r64p, inv1);
+}
+// the sum mod q, in [0, 6q) (NARROW) or [0, q) (WIDE)
+template <bool WIDE>
+__device__ __forceinline__ uint64_t acc_reduce_6q(const AccT<WIDE>& A, uint64_t q, uint64_t r64, uint64_t r64p,
+                                                  uint64_t inv1) {
+  if constexpr (WIDE) return reduce128(A, q, r64, r64p, inv1);
+  else return acc3_reduce_6q(A, q, r64, r64p, inv1);
 }
 
 }  // namespace ckks

@@ -27,27 +27,27 @@ __device__ __forceinline__ RedConst red_const(ConstPrime p, int i) {
   return r;
 }
 
-// Split multiply-accumulate of NS sources against one target's constants
-// (rows of a zero-padded table, stride `stride`), reduced mod the target q:
-// in [0, 6q) for NS = 8, in [0, q) for NS = 16.  Both ranges are valid inputs
-// of the forward NTT that follows (lazy butterflies start from words below
-// 6q and stay below 70q < 2^64 for q < 2^57; the others accept words below
-// 8q).  NS is 8 or 16; sources past the real count have zero constants and
-// words.
-template <int NS>
-__device__ __forceinline__ uint64_t conv_dot(const uint32_t (&yl)[NS], const uint32_t (&yh)[NS], ConstU64 conv,
-                                             int stride, const RedConst& pc) {
+// Multiply-accumulate of NS sources against one target's constants (rows of
+// a zero-padded table of split constants, stride `stride`), reduced mod the
+// target q: NARROW, in [0, 6q) for NS = 8 and [0, q) for NS = 16; WIDE, in
+// [0, q).  Both ranges are valid inputs of the forward NTT that follows (lazy
+// butterflies start from words below 6q and stay below 70q < 2^64 for
+// q < 2^57; Harvey butterflies accept words below 8q, strict ones below 4q).
+// NS is 8 or 16; sources past the real count have zero constants and words.
+template <int NS, bool WIDE>
+__device__ __forceinline__ uint64_t conv_dot(const Split<WIDE> (&y)[NS], ConstU64 conv, int stride,
+                                             const RedConst& pc) {
   uint64_t cw[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) cw[i] = conv[i * stride];
   uint64_t r = 0;
 #pragma unroll
   for (int g = 0; g < NS; g += 8) {
-    Acc3 A = {0, 0, 0};
+    AccT<WIDE> A{};
 #pragma unroll
-    for (int i = g; i < g + 8; ++i) acc3_mac(A, yl[i], yh[i], (uint32_t)cw[i], (uint32_t)(cw[i] >> 32));
-    if (NS == 8) return acc3_reduce_6q(A, pc.q, pc.r64, pc.r64p, pc.inv1);
-    const uint64_t v = acc3_reduce(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    for (int i = g; i < g + 8; ++i) acc_mac<WIDE>(A, y[i], split_table<WIDE>(cw[i]));
+    if (NS == 8) return acc_reduce_6q<WIDE>(A, pc.q, pc.r64, pc.r64p, pc.inv1);
+    const uint64_t v = acc_reduce<WIDE>(A, pc.q, pc.r64, pc.r64p, pc.inv1);
     r = g ? add_mod(r, v, pc.q) : v;
   }
   return r;

@@ -76,7 +76,7 @@ static int validate(const ckks_params* p) {
   if (p->n_p) all.insert(all.end(), p->p, p->p + p->n_p);
   for (size_t i = 0; i < all.size(); ++i) {
     uint64_t m = all[i];
-    if (m >= (1ull << 60)) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not below 2^60");
+    if (m >= (1ull << 62)) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not below 2^62");
     if (m % two_n != 1) return set_error(CKKS_EPARAM, "prime " + std::to_string(m) + " is not 1 mod 2N");
     if (!is_prime(m)) return set_error(CKKS_EPARAM, std::to_string(m) + " is not prime");
     for (size_t j = 0; j < i; ++j)
@@ -167,8 +167,9 @@ static int build_tables(Ctx* c) {
   if ((rc = upload((void**)&c->d_tw_inv, iv.data(), iv.size() * 8))) return rc;
   if (c->K == 0) return CKKS_OK;
 
-  // Basis-conversion constants (below 2^60) are stored split in 30-bit halves,
-  // lo | hi << 32, the operand form of the split multiply-accumulate.
+  // Basis-conversion constants are stored split, lo30 | (v >> 30) << 32: the
+  // operand form of the 30-bit split multiply-accumulate (constants below
+  // 2^60); the full-width kernels reassemble the value (below 2^62).
   auto split30 = [](uint64_t v) { return (v & 0x3fffffffull) | ((v >> 30) << 32); };
   // ModUp constants per (level, digit)
   std::vector<uint64_t> mu;
@@ -317,6 +318,7 @@ int ckks_ctx_create(const ckks_params* params, int hip_device, ckks_ctx** out) {
   c->alpha = (c->L + c->dnum - 1) / c->dnum;
   c->mod.assign(params->q, params->q + c->L);
   if (c->K) c->mod.insert(c->mod.end(), params->p, params->p + c->K);
+  for (uint64_t m : c->mod) c->wide = c->wide || m >= (1ull << 60);
   for (uint32_t i = 0; i < c->L + c->K; ++i)
     c->psi.push_back(params->psi ? params->psi[i] : host::smallest_primitive_root_2n(c->mod[i], (int)c->log_n));
   if ((rc = build_tables(c)) || (rc = build_rescale(c)) || (rc = noalloc_init_device(hip_device))) {

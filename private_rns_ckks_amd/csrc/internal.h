@@ -58,6 +58,9 @@ struct Ctx {
   int device = 0;
   uint32_t log_n = 0, N = 0, L = 0, K = 0, dnum = 0, alpha = 0;
   std::vector<uint64_t> mod, psi;  // host copies, L+K entries
+  // Some prime is at least 2^60: the dot-product kernels use full-width
+  // 64x64-bit products instead of 30-bit halves.
+  bool wide = false;
   PrimeConst* d_prime = nullptr;   // [L+K]
   uint64_t* d_tw_fwd = nullptr;    // [L+K][N][2] {psi^brv(k), Shoup}
   uint64_t* d_tw_inv = nullptr;    // [L+K][N][2] {psi^-brv(k), Shoup}

@@ -45,8 +45,9 @@ __global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64
 // t outside the digit, out_t = sum_i y_i [qhat_i]_{m_t} mod m_t (exact,
 // left in the range conv_dot gives).
 // Constants [qhat_i]_{m_t}: [NS][next], split into 30-bit halves, zero rows
-// past the digit's size.
-template <int NS>
+// past the digit's size.  WIDE: some prime is at least 2^60 (full-width
+// products).
+template <int NS, bool WIDE>
 __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
   const int j = blockIdx.y;
   const int lo = a.lo[j], hi = a.hi[j], na = hi - lo;
@@ -55,17 +56,13 @@ __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t* x = a.x + blockIdx.z * a.x_bstride + (uint64_t)lo * a.n + c;
   uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
-  uint32_t yl[NS], yh[NS];
+  Split<WIDE> y[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const uint64_t y = i < na ? x[(uint64_t)i * a.n] : 0;
-    yl[i] = lo30(y);
-    yh[i] = hi30(y);
-  }
+  for (int i = 0; i < NS; ++i) y[i] = split_word<WIDE>(i < na ? x[(uint64_t)i * a.n] : 0);
   for (int t = 0; t < a.next; ++t) {
     if (t >= lo && t < hi) continue;
     const RedConst pc = red_const(prime, t <= a.level ? t : a.L + (t - a.level - 1));
-    out[(uint64_t)t * a.n] = conv_dot<NS>(yl, yh, conv + t, a.next, pc);
+    out[(uint64_t)t * a.n] = conv_dot<NS, WIDE>(y, conv + t, a.next, pc);
   }
 }
 
@@ -76,7 +73,7 @@ __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
 // sum_k y_k [1/p_k]_{q_i} - #negative  (mod q_i).  w: [2][level+1][N] per item,
 // in the range conv_dot gives.
 // Constants [1/p_k]_{q_i}: [NS][L], split into 30-bit halves, zero rows past K.
-template <int NS>
+template <int NS, bool WIDE>
 __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   const int nq = a.level + 1;
   const ConstU64 conv = (ConstU64)a.conv;
@@ -84,7 +81,7 @@ __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int comp = blockIdx.y;
   const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.acc_comp_limbs + a.acc_k0) * a.n + c;
-  uint32_t yl[NS], yh[NS];
+  Split<WIDE> y[NS];
   uint32_t neg = 0;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
@@ -93,17 +90,17 @@ __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
       v = acc[(uint64_t)k * a.n];
       neg += v > (prime[a.L + k].q >> 1) ? 1u : 0u;
     }
-    yl[k] = lo30(v);
-    yh[k] = hi30(v);
+    y[k] = split_word<WIDE>(v);
   }
   uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * nq * a.n + c;
   for (int i = 0; i < nq; ++i) {
     const RedConst pc = red_const(prime, i);
-    w[(uint64_t)i * a.n] = sub_mod(conv_dot<NS>(yl, yh, conv + i, a.L, pc), neg, pc.q);
+    w[(uint64_t)i * a.n] = sub_mod(conv_dot<NS, WIDE>(y, conv + i, a.L, pc), neg, pc.q);
   }
 }
 
 // d0 = a0 b0, d1 = a0 b1 + a1 b0, d2 = a1 b1 on limb blockIdx.y.
+template <bool WIDE>
 __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
   const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
   const int i = blockIdx.y;
@@ -114,16 +111,16 @@ __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
   const uint64_t* y = a.b + blockIdx.z * a.b_bstride;
   uint64_t* d = a.out + blockIdx.z * a.out_bstride;
   const uint64_t a0 = x[off], a1 = x[lim + off], b0 = y[off], b1 = y[a.b_comp + off];
-  const uint32_t a0l = lo30(a0), a0h = hi30(a0), a1l = lo30(a1), a1h = hi30(a1);
-  const uint32_t b0l = lo30(b0), b0h = hi30(b0), b1l = lo30(b1), b1h = hi30(b1);
-  Acc3 m0 = {0, 0, 0}, m1 = {0, 0, 0}, m2 = {0, 0, 0};
-  acc3_mac(m0, a0l, a0h, b0l, b0h);
-  acc3_mac(m1, a0l, a0h, b1l, b1h);
-  acc3_mac(m1, a1l, a1h, b0l, b0h);
-  acc3_mac(m2, a1l, a1h, b1l, b1h);
-  d[off] = acc3_reduce(m0, pc.q, pc.r64, pc.r64p, pc.inv1);
-  d[lim + off] = acc3_reduce(m1, pc.q, pc.r64, pc.r64p, pc.inv1);
-  d[2 * lim + off] = acc3_reduce(m2, pc.q, pc.r64, pc.r64p, pc.inv1);
+  const Split<WIDE> sa0 = split_word<WIDE>(a0), sa1 = split_word<WIDE>(a1);
+  const Split<WIDE> sb0 = split_word<WIDE>(b0), sb1 = split_word<WIDE>(b1);
+  AccT<WIDE> m0{}, m1{}, m2{};
+  acc_mac<WIDE>(m0, sa0, sb0);
+  acc_mac<WIDE>(m1, sa0, sb1);
+  acc_mac<WIDE>(m1, sa1, sb0);
+  acc_mac<WIDE>(m2, sa1, sb1);
+  d[off] = acc_reduce<WIDE>(m0, pc.q, pc.r64, pc.r64p, pc.inv1);
+  d[lim + off] = acc_reduce<WIDE>(m1, pc.q, pc.r64, pc.r64p, pc.inv1);
+  d[2 * lim + off] = acc_reduce<WIDE>(m2, pc.q, pc.r64, pc.r64p, pc.inv1);
 }
 
 // BSGS inner sums: inner[o][g][comp][i] = sum_c sum_b diag[o][c][g][b][i] * baby[b][c][comp][i].
@@ -134,6 +131,7 @@ __global__ __launch_bounds__(256) void tensor_kernel(TensorArgs a) {
 // same for every g and every o, and the workgroup order below keeps the
 // workgroups of one coefficient tile (all o) together on one XCD, so they are
 // served by that XCD's L2.
+template <bool WIDE>
 __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
   const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
   const int o = (int)gp.tile, i = gp.job;
@@ -159,15 +157,15 @@ __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
           c1[k] = ct[ln];
         }
       }
-      Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
+      AccT<WIDE> s0{}, s1{};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t pl = lo30(pt[k]), ph = hi30(pt[k]);
-        acc3_mac(s0, pl, ph, lo30(c0[k]), hi30(c0[k]));
-        acc3_mac(s1, pl, ph, lo30(c1[k]), hi30(c1[k]));
+        const Split<WIDE> p = split_word<WIDE>(pt[k]);
+        acc_mac<WIDE>(s0, p, split_word<WIDE>(c0[k]));
+        acc_mac<WIDE>(s1, p, split_word<WIDE>(c1[k]));
       }
-      r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r0 = add_mod(r0, acc_reduce<WIDE>(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc_reduce<WIDE>(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
     }
     uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 2 * ln;
     out[off] = r0;
@@ -181,6 +179,7 @@ __global__ __launch_bounds__(256) void ptmac_kernel(PtMacArgs a) {
 // workgroup order as ptmac_kernel; four split accumulators per group of 8
 // terms (the middle part keeps its two products apart, so no accumulator
 // takes more than 8 products).
+template <bool WIDE>
 __global__ __launch_bounds__(256) void ctmac_kernel(CtMacArgs a) {
   const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
   const int o = (int)gp.tile, i = gp.job;
@@ -208,20 +207,20 @@ __global__ __launch_bounds__(256) void ctmac_kernel(CtMacArgs a) {
           x1[k] = x[ln];
         }
       }
-      Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0}, s1b = {0, 0, 0}, s2 = {0, 0, 0};
+      AccT<WIDE> s0{}, s1{}, s1b{}, s2{};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t al = lo30(d0[k]), ah = hi30(d0[k]), bl = lo30(d1[k]), bh = hi30(d1[k]);
-        const uint32_t ul = lo30(x0[k]), uh = hi30(x0[k]), vl = lo30(x1[k]), vh = hi30(x1[k]);
-        acc3_mac(s0, al, ah, ul, uh);
-        acc3_mac(s1, al, ah, vl, vh);
-        acc3_mac(s1b, bl, bh, ul, uh);
-        acc3_mac(s2, bl, bh, vl, vh);
+        const Split<WIDE> da = split_word<WIDE>(d0[k]), db = split_word<WIDE>(d1[k]);
+        const Split<WIDE> xu = split_word<WIDE>(x0[k]), xv = split_word<WIDE>(x1[k]);
+        acc_mac<WIDE>(s0, da, xu);
+        acc_mac<WIDE>(s1, da, xv);
+        acc_mac<WIDE>(s1b, db, xu);
+        acc_mac<WIDE>(s2, db, xv);
       }
-      r0 = add_mod(r0, acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      r1 = add_mod(r1, acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      r1 = add_mod(r1, acc3_reduce(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-      r2 = add_mod(r2, acc3_reduce(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r0 = add_mod(r0, acc_reduce<WIDE>(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc_reduce<WIDE>(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r1 = add_mod(r1, acc_reduce<WIDE>(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+      r2 = add_mod(r2, acc_reduce<WIDE>(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
     }
     uint64_t* out = a.out + ((uint64_t)o * a.n2 + g) * 3 * ln;
     out[off] = r0;
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(256) void ctmac_kernel(CtMacArgs a) {
 // The same sums with the loops swapped, for n2 <= MAXG: the baby-step words
 // of a group of 8 (c, b) terms are loaded once and used for every giant step,
 // whose running sums stay in registers; only the diagonals stream.
-template <int MAXG>
+template <int MAXG, bool WIDE>
 __global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
   const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
   const int o = (int)gp.tile, i = gp.job;
@@ -247,7 +246,7 @@ __global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
 #pragma unroll
   for (int g = 0; g < MAXG; ++g) r0[g] = r1[g] = 0;
   for (int t0 = 0; t0 < terms; t0 += 8) {
-    uint32_t c0l[8], c0h[8], c1l[8], c1h[8];
+    Split<WIDE> sc0[8], sc1[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int t = t0 + k;
@@ -258,10 +257,8 @@ __global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
         x0 = ct[0];
         x1 = ct[ln];
       }
-      c0l[k] = lo30(x0);
-      c0h[k] = hi30(x0);
-      c1l[k] = lo30(x1);
-      c1h[k] = hi30(x1);
+      sc0[k] = split_word<WIDE>(x0);
+      sc1[k] = split_word<WIDE>(x1);
     }
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
@@ -276,15 +273,15 @@ __global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
             pt[k] = a.diags[((((uint64_t)o * a.n_in + ci) * a.n2 + g) * a.n1 + b) * ln + off];
           }
         }
-        Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0};
+        AccT<WIDE> s0{}, s1{};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t pl = lo30(pt[k]), ph = hi30(pt[k]);
-          acc3_mac(s0, pl, ph, c0l[k], c0h[k]);
-          acc3_mac(s1, pl, ph, c1l[k], c1h[k]);
+          const Split<WIDE> p = split_word<WIDE>(pt[k]);
+          acc_mac<WIDE>(s0, p, sc0[k]);
+          acc_mac<WIDE>(s1, p, sc1[k]);
         }
-        r0[g] = add_mod(r0[g], acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        r1[g] = add_mod(r1[g], acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r0[g] = add_mod(r0[g], acc_reduce<WIDE>(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc_reduce<WIDE>(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
       }
     }
   }
@@ -299,7 +296,7 @@ __global__ __launch_bounds__(256) void ptmac_regs_kernel(PtMacArgs a) {
 }
 
 // ctmac_kernel with the loops swapped as in ptmac_regs_kernel (n2 <= MAXG).
-template <int MAXG>
+template <int MAXG, bool WIDE>
 __global__ __launch_bounds__(256) void ctmac_regs_kernel(CtMacArgs a) {
   const nttc::GridPos gp = nttc::row_grid_pos();  // grid (n_out, limbs, N/256): o fastest
   const int o = (int)gp.tile, i = gp.job;
@@ -313,7 +310,7 @@ __global__ __launch_bounds__(256) void ctmac_regs_kernel(CtMacArgs a) {
 #pragma unroll
   for (int g = 0; g < MAXG; ++g) r0[g] = r1[g] = r2[g] = 0;
   for (int t0 = 0; t0 < terms; t0 += 8) {
-    uint32_t ul[8], uh[8], vl[8], vh[8];
+    Split<WIDE> xu[8], xv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int t = t0 + k;
@@ -324,10 +321,8 @@ __global__ __launch_bounds__(256) void ctmac_regs_kernel(CtMacArgs a) {
         x0 = x[0];
         x1 = x[ln];
       }
-      ul[k] = lo30(x0);
-      uh[k] = hi30(x0);
-      vl[k] = lo30(x1);
-      vh[k] = hi30(x1);
+      xu[k] = split_word<WIDE>(x0);
+      xv[k] = split_word<WIDE>(x1);
     }
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
@@ -344,19 +339,19 @@ __global__ __launch_bounds__(256) void ctmac_regs_kernel(CtMacArgs a) {
             d1[k] = d[ln];
           }
         }
-        Acc3 s0 = {0, 0, 0}, s1 = {0, 0, 0}, s1b = {0, 0, 0}, s2 = {0, 0, 0};
+        AccT<WIDE> s0{}, s1{}, s1b{}, s2{};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t al = lo30(d0[k]), ah = hi30(d0[k]), bl = lo30(d1[k]), bh = hi30(d1[k]);
-          acc3_mac(s0, al, ah, ul[k], uh[k]);
-          acc3_mac(s1, al, ah, vl[k], vh[k]);
-          acc3_mac(s1b, bl, bh, ul[k], uh[k]);
-          acc3_mac(s2, bl, bh, vl[k], vh[k]);
+          const Split<WIDE> da = split_word<WIDE>(d0[k]), db = split_word<WIDE>(d1[k]);
+          acc_mac<WIDE>(s0, da, xu[k]);
+          acc_mac<WIDE>(s1, da, xv[k]);
+          acc_mac<WIDE>(s1b, db, xu[k]);
+          acc_mac<WIDE>(s2, db, xv[k]);
         }
-        r0[g] = add_mod(r0[g], acc3_reduce(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        r1[g] = add_mod(r1[g], acc3_reduce(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        r1[g] = add_mod(r1[g], acc3_reduce(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
-        r2[g] = add_mod(r2[g], acc3_reduce(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r0[g] = add_mod(r0[g], acc_reduce<WIDE>(s0, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc_reduce<WIDE>(s1, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r1[g] = add_mod(r1[g], acc_reduce<WIDE>(s1b, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
+        r2[g] = add_mod(r2[g], acc_reduce<WIDE>(s2, pc.q, pc.r64, pc.r64p, pc.inv1), pc.q);
       }
     }
   }
@@ -443,47 +438,44 @@ int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch) {
     units += na + (double)(a.next - na) * (na + 1);
   }
   TraceScope ts(c, s, "modup", units * batch * c->N);
-  if (conv_rows(c->alpha) == 8)
-    hipLaunchKernelGGL(modup_kernel<8>, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(modup_kernel<16>, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
+  auto fn = conv_rows(c->alpha) == 8 ? (c->wide ? modup_kernel<8, true> : modup_kernel<8, false>)
+                                     : (c->wide ? modup_kernel<16, true> : modup_kernel<16, false>);
+  hipLaunchKernelGGL(fn, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
   TraceScope ts(c, s, "moddown_conv", (double)batch * 2 * (a.K + (double)(a.level + 1) * (a.K + 1)) * c->N);
-  if (conv_rows(c->K) == 8)
-    hipLaunchKernelGGL(moddown_conv_kernel<8>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(moddown_conv_kernel<16>, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
+  auto fn = conv_rows(c->K) == 8 ? (c->wide ? moddown_conv_kernel<8, true> : moddown_conv_kernel<8, false>)
+                                 : (c->wide ? moddown_conv_kernel<16, true> : moddown_conv_kernel<16, false>);
+  hipLaunchKernelGGL(fn, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_tensor(Ctx* c, hipStream_t s, TensorArgs& a, int batch) {
   TraceScope ts(c, s, "tensor", (double)batch * (a.level + 1) * 7 * c->N);
-  hipLaunchKernelGGL(tensor_kernel, dim3(c->N / 256, a.level + 1, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(c->wide ? tensor_kernel<true> : tensor_kernel<false>, dim3(c->N / 256, a.level + 1, batch),
+                     dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ptmac", (double)n_out * a.n2 * (a.level + 1) * 2 * (a.n_in * a.n1 + 1) * c->N);
-  if (a.n2 <= 8)
-    hipLaunchKernelGGL(ptmac_regs_kernel<8>, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(ptmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  auto fn = a.n2 <= 8 ? (c->wide ? ptmac_regs_kernel<8, true> : ptmac_regs_kernel<8, false>)
+                      : (c->wide ? ptmac_kernel<true> : ptmac_kernel<false>);
+  hipLaunchKernelGGL(fn, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }
 
 int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out) {
   TraceScope ts(c, s, "ctmac", (double)n_out * a.n2 * (a.level + 1) * (4 * a.n_in * a.n1 + 3) * c->N);
-  if (a.n2 <= 8)
-    hipLaunchKernelGGL(ctmac_regs_kernel<8>, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(ctmac_kernel, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
+  auto fn = a.n2 <= 8 ? (c->wide ? ctmac_regs_kernel<8, true> : ctmac_regs_kernel<8, false>)
+                      : (c->wide ? ctmac_kernel<true> : ctmac_kernel<false>);
+  hipLaunchKernelGGL(fn, dim3(n_out, a.level + 1, c->N / 256), dim3(256), 0, s, a);
   LAUNCH_CHECK();
   return CKKS_OK;
 }

@@ -29,6 +29,7 @@
 #include "automorph.h"
 #include "kernels.h"
 #include "ntt_core.h"
+#include "rowpass.h"
 
 namespace ckks {
 
@@ -102,130 +103,13 @@ struct RowIPArgs {
   int t0;          // target limb of grid job 0 (job j handles limb t0 + j)
 };
 
-// A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
-// on, so several workgroups share a CU).  The row pass's LOGB stages run as
-// register rounds of at most 3 stages, the last of exactly 3, so every thread
-// holds 8 words in every round and ends with 8 consecutive words of one
-// column: the layout the multiply phase reads the key digits in.
-__host__ __device__ constexpr int ip_logkc(int logb) { return logb >= 7 ? 3 : 4; }
-
-template <int LOGB>
-struct IPRounds {
-  static constexpr int R3 = 3;
-  static constexpr int R2 = LOGB >= 6 ? 3 : LOGB - 3;
-  static constexpr int R1 = LOGB - R2 - R3;  // 0 when two rounds suffice
-  static constexpr int LOGKC = ip_logkc(LOGB);
-  static constexpr int KC = 1 << LOGKC;
-  static constexpr int THREADS = KC << (LOGB - 3);
-};
-
-// global word index (within the limb) of tile element (row, col)
-template <int LOGB>
-__device__ __forceinline__ uint32_t ip_word(uint32_t tile, int row, int col) {
-  return ((tile * IPRounds<LOGB>::KC + col) << LOGB) + row;
-}
-
-// LDS position of row-pass tile element (row, col): column-major, with row
-// bits 0-4 XOR-ed by (row bits 5-7) and (row bits 6-7) << 3.  For the rounds
-// of 2, 3, 3 stages at row bits 6, 3, 0 every 64-bit access of a wave then
-// shares its bank pair with at most one other lane.
-template <int LOGB>
-__device__ __forceinline__ int ip_lds(int row, int col) {
-  return col * (1 << LOGB) + (row ^ (((row >> 6) & 3) << 3) ^ ((row >> 5) & 7));
-}
-
-// The row pass's twiddles for one tile, staged in LDS once per workgroup and
-// used by every digit: relative stage d (global stage s0 + d) of column col
-// needs entries col * 2^d .. col * 2^d + 2^d - 1 of a run of KC * 2^d
-// consecutive table entries, stored from LDS entry KC * (2^d - 1) on.
-template <int LOGB>
-__device__ __forceinline__ void ip_stage_twiddles(ulonglong2* twl, const uint64_t* tw, uint32_t tile, uint32_t s0) {
-  typedef IPRounds<LOGB> G;
-  constexpr int ENTRIES = G::KC * ((1 << LOGB) - 1);
-  for (int e = threadIdx.x; e < ENTRIES; e += G::THREADS) {
-    const int d = 31 - __clz((e >> G::LOGKC) + 1);
-    const uint32_t g = (1u << (s0 + d)) + (tile << (G::LOGKC + d)) + (uint32_t)(e - G::KC * ((1 << d) - 1));
-    twl[e] = *reinterpret_cast<const ulonglong2*>(tw + 2 * (uint64_t)g);
-  }
-}
-
-// R forward stages on the 2^R words of one item (rows base + (i << pos) of
-// column col), twiddles from the LDS copy.
-template <int R, int LOGB, bool LAZY>
-__device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, int pos, int col, const ulonglong2* twl,
-                                               uint64_t q) {
-  constexpr int E = 1 << R;
-#pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int half = E >> (s + 1);
-    const int d = LOGB - pos - R + s;
-#pragma unroll
-    for (int g = 0; g < (1 << s); ++g) {
-      const int i0 = g * 2 * half;
-      const int row = base + (i0 << pos);
-      const ulonglong2 w = twl[IPRounds<LOGB>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
-#pragma unroll
-      for (int m = 0; m < half; ++m) ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w.x, w.y, q);
-    }
-  }
-}
-
-// One register round of R forward stages on row bits [POS, POS+R): item k of
-// the thread (k < 8 >> R) is tid + k * THREADS; its words are rows
-// base + (i << POS) of column col, read from global memory (src) or LDS and
-// left in LDS or in x[].
-template <int R, int POS, int LOGB, bool LAZY, bool FROM_GLOBAL, bool TO_LDS>
-__device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
-                                         uint32_t tile, int log_n, uint64_t q) {
-  constexpr int T = IPRounds<LOGB>::THREADS;
-  constexpr int NI = 8 >> R;
-  uint64_t y[NI][1 << R];
-  int col[NI], base[NI];
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    item_coords<false, R, LOGB>(threadIdx.x + k * T, POS, col[k], base[k]);
-#pragma unroll
-    for (int i = 0; i < (1 << R); ++i) {
-      const int row = base[k] + (i << POS);
-      y[k][i] = FROM_GLOBAL ? src[ip_word<LOGB>(tile, row, col[k])] : lds[ip_lds<LOGB>(row, col[k])];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    ip_butterflies<R, LOGB, LAZY>(y[k], base[k], POS, col[k], twl, q);
-#pragma unroll
-    for (int i = 0; i < (1 << R); ++i) {
-      if (TO_LDS) lds[ip_lds<LOGB>(base[k] + (i << POS), col[k])] = y[k][i];
-      else x[(k << R) + i] = y[k][i];
-    }
-  }
-}
-
-// Forward row pass of one limb (src, lazy column-pass output) on the tile:
-// the thread ends with rows base..base+7 of its column in x[] (lazy).
-template <int LOGB, bool LAZY>
-__device__ __forceinline__ void ip_row_pass(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
-                                            uint32_t tile, int log_n, uint64_t q) {
-  typedef IPRounds<LOGB> G;
-  __syncthreads();  // every thread has read the tile's previous contents
-  if constexpr (G::R1 > 0) {
-    ip_round<G::R1, LOGB - G::R1, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
-    __syncthreads();
-    ip_round<G::R2, G::R3, LOGB, LAZY, false, true>(x, src, lds, twl, tile, log_n, q);
-  } else {
-    ip_round<G::R2, G::R3, LOGB, LAZY, true, true>(x, src, lds, twl, tile, log_n, q);
-  }
-  __syncthreads();
-  ip_round<G::R3, 0, LOGB, LAZY, false, false>(x, src, lds, twl, tile, log_n, q);
-}
-
 // Multiply-accumulate of target limb t (tile gp.tile, item gp.item) over the
 // digits: accb[i] / acca[i] receive sum_j x_j * evk_j.{b,a} for the thread's
 // 8 words (rows base..base+7 of column col), x_j the forward row pass of the
 // converted limb E[j][t] or, for t inside digit j, the NTT-form input limb
-// (through tau_g when rotating).  Sums of Montgomery products, below 8m
-// (reduced every 4 digits); the factor 2^-64 is left in them.
-template <int LOGB, int LOGN, bool LAZY>
+// (through tau_g when rotating).  Sums of Montgomery products, reduced every
+// mont_fold(m) digits (below 9m); the factor 2^-64 is left in them.
+template <int LOGB, int LOGN, int AR>
 __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds, const ulonglong2* twl,
                                               const PrimeConst& pc, int keyl, const GridPos& gp, uint64_t (&accb)[8],
                                               uint64_t (&acca)[8]) {
@@ -239,9 +123,10 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
-  // Montgomery products are below 2m, so four of them sum below 8m < 2^63
 #pragma unroll
   for (int i = 0; i < 8; ++i) accb[i] = acca[i] = 0;
+  const int fold = mont_fold(q);
+  int since = 0;
   for (int j = 0; j < a.beta; ++j) {
     const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
     uint64_t x[8];
@@ -262,7 +147,7 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
       }
     } else {  // forward row pass of the converted limb; outputs stay lazy (< 70q, or < 8q)
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
-      ip_row_pass<LOGB, LAZY>(x, src, lds, twl, tile, log_n, q);
+      ip_row_pass<LOGB, AR>(x, src, lds, twl, tile, log_n, q);
     }
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
@@ -279,7 +164,8 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
       acca[2 * i] += mont_mul_lazy(x[2 * i], va[i].x, q, mp);
       acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], va[i].y, q, mp);
     }
-    if ((j & 3) == 3) {
+    if (++since == fold) {
+      since = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         accb[i] = reduce64(accb[i], q, pc.inv1);
@@ -297,9 +183,9 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
 // The inverse row pass of one component: the thread's 8 words (rows
 // base..base+7 of its column, canonical) go through the Gentleman-Sande stages
 // of row bits 0-2 in registers, then of row bits 3.. and 6.. through the LDS
-// tile, and are stored in the lazy range of the inverse butterflies ([0, q)
-// after a final reduction for q < 2^54, [0, 4q) otherwise).
-template <int LOGB, bool LAZY>
+// tile, and are stored in the range of the inverse butterflies of AR ([0, q)
+// after a final reduction for AR_LAZY).
+template <int LOGB, int AR>
 __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t* lds, uint32_t tile, int log_n,
                                                      const uint64_t* twi, uint64_t q, uint64_t inv1, uint64_t* dst) {
   typedef IPRounds<LOGB> G;
@@ -309,7 +195,7 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   {
     const uint32_t blk = tile * G::KC + col;
-    round_regs<3, true, LAZY, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+    round_regs<3, true, AR, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
   }
   __syncthreads();  // every thread has read the tile's previous contents
 #pragma unroll
@@ -325,11 +211,11 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
 #pragma unroll
     for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
     const uint32_t blk = tile * G::KC + c;
-    round_regs<G::R2, true, LAZY, false, false, 3>(y, b, 3, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+    round_regs<G::R2, true, AR, false, false, 3>(y, b, 3, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
     if constexpr (G::R1 == 0) {
 #pragma unroll
       for (int i = 0; i < (1 << G::R2); ++i) {
-        const uint64_t v = LAZY ? reduce64(y[i], q, inv1) : y[i];
+        const uint64_t v = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
         dst[ip_word<LOGB>(tile, b + (i << 3), c)] = v;
       }
     } else {
@@ -349,10 +235,10 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
       const uint32_t blk = tile * G::KC + c;
-      round_regs<G::R1, true, LAZY, false, false, P1>(y, b, P1, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+      round_regs<G::R1, true, AR, false, false, P1>(y, b, P1, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i) {
-        const uint64_t v = LAZY ? reduce64(y[i], q, inv1) : y[i];
+        const uint64_t v = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
         dst[ip_word<LOGB>(tile, b + (i << P1), c)] = v;
       }
     }
@@ -380,11 +266,13 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     gp.item = g0.item * a.items_per_wg + k;
     if (gp.item >= a.n_items) break;
     uint64_t accb[8], acca[8];
-    const bool lazy_fwd = pc.q < (1ull << 57);
-    if (lazy_fwd)
-      ip_accumulate<LOGB, LOGN, true>(a, lds, twl, pc, keyl, gp, accb, acca);
+    const int far = fwd_ar(pc.q);
+    if (far == AR_LAZY)
+      ip_accumulate<LOGB, LOGN, AR_LAZY>(a, lds, twl, pc, keyl, gp, accb, acca);
+    else if (far == AR_HARVEY)
+      ip_accumulate<LOGB, LOGN, AR_HARVEY>(a, lds, twl, pc, keyl, gp, accb, acca);
     else
-      ip_accumulate<LOGB, LOGN, false>(a, lds, twl, pc, keyl, gp, accb, acca);
+      ip_accumulate<LOGB, LOGN, AR_STRICT>(a, lds, twl, pc, keyl, gp, accb, acca);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {  // remove the 2^-64: canonical accumulators
       accb[i] = reduce_4q(mul_shoup_lazy(accb[i], pc.r64, pc.r64p, pc.q), pc.q);
@@ -392,12 +280,16 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     }
     uint64_t* ob = a.acc + gp.item * a.acc_bstride + ((uint64_t)(t - a.level - 1) << log_n);
     uint64_t* oa = ob + ((uint64_t)a.K << log_n);
-    if (pc.q < (1ull << 54)) {
-      ip_inverse_row_store<LOGB, true>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
-      ip_inverse_row_store<LOGB, true>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+    const int iar = inv_ar(pc.q);
+    if (iar == AR_LAZY) {
+      ip_inverse_row_store<LOGB, AR_LAZY>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_LAZY>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+    } else if (iar == AR_HARVEY) {
+      ip_inverse_row_store<LOGB, AR_HARVEY>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_HARVEY>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
     } else {
-      ip_inverse_row_store<LOGB, false>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
-      ip_inverse_row_store<LOGB, false>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+      ip_inverse_row_store<LOGB, AR_STRICT>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_STRICT>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
     }
   }
 }
@@ -439,14 +331,14 @@ struct CombIPArgs {
   const uint64_t* pinv64;  // [L][2]: {[2^64 P^-1]_{q_i}, Shoup}
 };
 
-template <int LOGB, int LOGN, bool LAZY>
+template <int LOGB, int LOGN, int AR>
 __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds, const ulonglong2* twl,
                                              const PrimeConst& pc, int i, const GridPos& gp) {
   const int log_n = LOGN ? LOGN : a.ip.log_n;
   const int item = gp.item;
   const uint64_t q = pc.q;
   uint64_t acc[2][8];
-  ip_accumulate<LOGB, LOGN, LAZY>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
+  ip_accumulate<LOGB, LOGN, AR>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
   const uint64_t cw = a.pinv64[2 * i], cwp = a.pinv64[2 * i + 1];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -459,7 +351,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     uint64_t x[8];
-    ip_row_pass<LOGB, LAZY>(x, a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds, twl,
+    ip_row_pass<LOGB, AR>(x, a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds, twl,
                             gp.tile, log_n, q);
     uint64_t add[8], accum[8];
 #pragma unroll
@@ -507,10 +399,13 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     GridPos gp = g0;
     gp.item = g0.item * a.ip.items_per_wg + k;
     if (gp.item >= a.ip.n_items) break;
-    if (pc.q < (1ull << 57))
-      comb_ip_body<LOGB, LOGN, true>(a, lds, twl, pc, i, gp);
+    const int far = fwd_ar(pc.q);
+    if (far == AR_LAZY)
+      comb_ip_body<LOGB, LOGN, AR_LAZY>(a, lds, twl, pc, i, gp);
+    else if (far == AR_HARVEY)
+      comb_ip_body<LOGB, LOGN, AR_HARVEY>(a, lds, twl, pc, i, gp);
     else
-      comb_ip_body<LOGB, LOGN, false>(a, lds, twl, pc, i, gp);
+      comb_ip_body<LOGB, LOGN, AR_STRICT>(a, lds, twl, pc, i, gp);
   }
 }
 
@@ -635,6 +530,8 @@ __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
   uint64_t accb[kGatherWords], acca[kGatherWords];
 #pragma unroll
   for (int i = 0; i < kGatherWords; ++i) accb[i] = acca[i] = 0;
+  const int fold = mont_fold(q);
+  int since = 0;
   for (int j = 0; j < a.beta; ++j) {
     const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
     const uint64_t* d = in_digit ? a.T + ((uint64_t)t << log_n) : a.E + ((uint64_t)(j * a.next + t) << log_n);
@@ -656,7 +553,8 @@ __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
       acca[2 * i] += mont_mul_lazy(x[2 * i], va[i].x, q, mp);
       acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], va[i].y, q, mp);
     }
-    if ((j & 3) == 3) {  // sums of up to 4 products below 2m stay below 8m < 2^63
+    if (++since == fold) {  // mont_fold(m) products since the last reduction
+      since = 0;
 #pragma unroll
       for (int i = 0; i < kGatherWords; ++i) {
         accb[i] = reduce64(accb[i], q, pc.inv1);

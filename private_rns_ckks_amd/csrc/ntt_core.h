@@ -27,11 +27,18 @@
 // with other data (key-switch epilogue) without a separate trip through
 // memory.
 //
-// Arithmetic: Shoup multiplication by the twiddle with an approximate
-// quotient (result in [0, 4q)).  Forward butterflies are fully lazy for
-// q < 2^57 (values grow by at most 4q per stage: 16 stages from [0, q) stay
-// below 65q < 2^64) and keep [0, 8q) otherwise; inverse butterflies keep
-// [0, 4q).  The last pass reduces to [0, q).
+// Arithmetic ranges (template parameter AR, chosen per prime by fwd_ar /
+// inv_ar):
+//   AR_LAZY    forward q < 2^57: Shoup products with an approximate quotient
+//              ([0, 4q)) and no reduction (values grow by at most 4q per
+//              stage: 16 stages from [0, q) stay below 65q < 2^64); inverse
+//              q < 2^54: the sum is not reduced (the bound doubles per stage
+//              from 4q, 8 stages end below 2^10 q, each pass reduces once);
+//   AR_HARVEY  q < 2^61: forward words in [0, 8q), inverse in [0, 4q), with
+//              one conditional subtraction per butterfly;
+//   AR_STRICT  q < 2^62: forward words in [0, 4q) and inverse in [0, 2q),
+//              with exact-quotient Shoup products ([0, 2q)).
+// The last pass reduces to [0, q).
 #pragma once
 #include "arith.h"
 #include "internal.h"
@@ -72,11 +79,27 @@ __device__ __forceinline__ void load_tw(const uint64_t* tw, uint32_t ti, uint64_
   wp = v.y;
 }
 
-template <bool LAZY>
+enum : int { AR_STRICT = 0, AR_HARVEY = 1, AR_LAZY = 2 };
+__host__ __device__ inline int fwd_ar(uint64_t q) {
+  return q < (1ull << 57) ? AR_LAZY : q < (1ull << 61) ? AR_HARVEY : AR_STRICT;
+}
+__host__ __device__ inline int inv_ar(uint64_t q) {
+  return q < (1ull << 54) ? AR_LAZY : q < (1ull << 61) ? AR_HARVEY : AR_STRICT;
+}
+
+template <int AR>
 __device__ __forceinline__ void ct_butterfly(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q) {
+  if (AR == AR_STRICT) {  // words below 4q
+    const uint64_t two_q = 2 * q;
+    const uint64_t u = x >= two_q ? x - two_q : x;
+    const uint64_t t = mul_shoup(y, w, wp, q);  // [0, 2q)
+    x = u + t;
+    y = u + two_q - t;
+    return;
+  }
   const uint64_t four_q = 4 * q;
   uint64_t u = x;
-  if (!LAZY) u = u >= four_q ? u - four_q : u;
+  if (AR == AR_HARVEY) u = u >= four_q ? u - four_q : u;
   const uint64_t t = mul_shoup_lazy(y, w, wp, q);  // [0, 4q)
   x = u + t;
   y = u + four_q - t;
@@ -90,6 +113,20 @@ __device__ __forceinline__ void gs_butterfly(uint64_t& x, uint64_t& y, uint64_t 
   y = mul_shoup_lazy_split(d, w, wp, q);
 }
 
+// Gentleman-Sande on words below 2q, for q < 2^62: sums below 4q.
+__device__ __forceinline__ void gs_butterfly_strict(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q) {
+  const uint64_t two_q = 2 * q;
+  const uint64_t s = x + y;
+  const uint64_t d = x + two_q - y;
+  x = s >= two_q ? s - two_q : s;
+  y = mul_shoup(d, w, wp, q);  // [0, 2q)
+}
+
+// Inverse butterfly of range AR; m: the lazy bound of the stage (AR_LAZY).
+template <int AR>
+__device__ __forceinline__ void gs_butterfly_ar(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q,
+                                                uint64_t m);
+
 // Gentleman-Sande without reducing the sum, for q < 2^54: with every word of
 // the pass below m before the stage, the sum stays below 2m, x + m - y lies in
 // (0, 2m) and the product below 4q, so m doubles per stage.  From words below
@@ -102,6 +139,14 @@ __device__ __forceinline__ void gs_butterfly_lazy(uint64_t& x, uint64_t& y, uint
   y = mul_shoup_lazy_split(d, w, wp, q);
 }
 
+template <int AR>
+__device__ __forceinline__ void gs_butterfly_ar(uint64_t& x, uint64_t& y, uint64_t w, uint64_t wp, uint64_t q,
+                                                uint64_t m) {
+  if (AR == AR_LAZY) gs_butterfly_lazy(x, y, w, wp, q, m);
+  else if (AR == AR_HARVEY) gs_butterfly(x, y, w, wp, q);
+  else gs_butterfly_strict(x, y, w, wp, q);
+}
+
 // R stages in registers on the 2^R words x[] of one thread; the words are
 // rows base + (i << pos) of column col.  Global stage of sub-stage s is
 // s0 + logb - pos - R + s.
@@ -112,7 +157,7 @@ __device__ __forceinline__ void gs_butterfly_lazy(uint64_t& x, uint64_t& y, uint
 typedef const __attribute__((address_space(4))) uint64_t* ConstTw;
 
 // KDONE: stages of this pass already done (bound of the lazy inverse).
-template <int R, bool INV, bool LAZY, bool COLFAST, bool UTW = false, int KDONE = 0>
+template <int R, bool INV, int AR, bool COLFAST, bool UTW = false, int KDONE = 0>
 __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int pos, int col, int logb, uint32_t tile,
                                            uint32_t s0, int log_n, const uint64_t* tw, uint64_t q) {
   constexpr int E = 1 << R;
@@ -136,9 +181,8 @@ __device__ __forceinline__ void round_regs(uint64_t (&x)[1 << R], int base, int 
       }
 #pragma unroll
       for (int m = 0; m < half; ++m) {
-        if (INV && LAZY) gs_butterfly_lazy(x[i0 + m], x[i0 + m + half], w, wp, q, (4 * q) << (KDONE + ss));
-        else if (INV) gs_butterfly(x[i0 + m], x[i0 + m + half], w, wp, q);
-        else ct_butterfly<LAZY>(x[i0 + m], x[i0 + m + half], w, wp, q);
+        if (INV) gs_butterfly_ar<AR>(x[i0 + m], x[i0 + m + half], w, wp, q, (4 * q) << (KDONE + ss));
+        else ct_butterfly<AR>(x[i0 + m], x[i0 + m + half], w, wp, q);
       }
     }
   }
@@ -175,7 +219,7 @@ __host__ __device__ constexpr int logb_row(int log_n) { return log_n - logb_col(
 
 // LOGN > 0 fixes log N at compile time (index arithmetic folds to constants);
 // LOGN = 0 takes it from log_n_rt.
-template <int RA, int RB, bool INV, bool COLFAST, bool LAZY, int LOGN, class IO>
+template <int RA, int RB, bool INV, bool COLFAST, int AR, int LOGN, class IO>
 __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t tile, int log_n_rt,
                                           const uint64_t* tw, uint64_t q, const Finish& fin) {
   const int log_n = LOGN ? LOGN : log_n_rt;
@@ -218,7 +262,7 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
       x[i] = stage_in ? lds[lds_index<COLFAST, RB, ROWS>(row, col)]
                       : io.load(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
     }
-    round_regs<R1, INV, LAZY, COLFAST, COLFAST && !INV>(x, base, pos1, col, LOGB, tile, s0, log_n, tw, q);
+    round_regs<R1, INV, AR, COLFAST, COLFAST && !INV>(x, base, pos1, col, LOGB, tile, s0, log_n, tw, q);
     // each thread writes back exactly the words it read: no hazard with other threads
 #pragma unroll
     for (int i = 0; i < (1 << R1); ++i) lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos1), col)] = x[i];
@@ -230,8 +274,8 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
     uint64_t x[1 << R2];
 #pragma unroll
     for (int i = 0; i < (1 << R2); ++i) x[i] = lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)];
-    round_regs<R2, INV, LAZY, COLFAST, COLFAST && INV, R1>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
-    if (INV && LAZY && fin.mode != 2) {
+    round_regs<R2, INV, AR, COLFAST, COLFAST && INV, R1>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
+    if (INV && AR == AR_LAZY && fin.mode != 2) {
       // lazy inverse: words below 2^10 q, reduced once (the next pass, or the caller, takes them below q)
 #pragma unroll
       for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);
@@ -276,14 +320,17 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
   }
 }
 
-// Dispatch on the butterfly form (lazy forward for small primes).
+// Dispatch on the butterfly range of the prime.
 template <int RA, int RB, bool INV, bool COLFAST, int LOGN, class IO>
 __device__ __forceinline__ void run_pass(const IO& io, uint64_t* lds, uint32_t tile, int log_n,
                                          const uint64_t* tw, uint64_t q, const Finish& fin) {
-  if (INV ? q < (1ull << 54) : q < (1ull << 57))
-    pass_body<RA, RB, INV, COLFAST, true, LOGN>(io, lds, tile, log_n, tw, q, fin);
+  const int ar = INV ? inv_ar(q) : fwd_ar(q);
+  if (ar == AR_LAZY)
+    pass_body<RA, RB, INV, COLFAST, AR_LAZY, LOGN>(io, lds, tile, log_n, tw, q, fin);
+  else if (ar == AR_HARVEY)
+    pass_body<RA, RB, INV, COLFAST, AR_HARVEY, LOGN>(io, lds, tile, log_n, tw, q, fin);
   else
-    pass_body<RA, RB, INV, COLFAST, false, LOGN>(io, lds, tile, log_n, tw, q, fin);
+    pass_body<RA, RB, INV, COLFAST, AR_STRICT, LOGN>(io, lds, tile, log_n, tw, q, fin);
 }
 
 inline uint32_t pass_tiles(uint32_t n, int logb) { return n / ((1u << logb) * kCols); }

@@ -44,7 +44,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_find_primes_matches_oracle(lib, orc):
-    for log_n, bits, count in [(12, 30, 4), (12, 60, 1), (16, 54, 24), (16, 60, 8), (10, 40, 5)]:
+    for log_n, bits, count in [(12, 30, 4), (12, 60, 1), (16, 54, 24), (16, 60, 8), (10, 40, 5), (12, 62, 3),
+                               (16, 61, 2)]:
         assert lib.ckks_find_primes(log_n, bits, count) == orc.gen_primes(log_n, bits, count)
 
 
@@ -80,6 +81,12 @@ def test_params_validate_rejects(lib):
     assert lib.ckks_params_validate(log_n, q, p, dnum, [2] * 32) == E         # bad psi
     assert lib.ckks_params_validate(log_n, [], p, dnum) == E
     assert "n_p" in lib.ckks_last_error() or lib.ckks_last_error() != ""
+    # primes up to 2^62 are accepted, 2^62 and above rejected
+    wq, wp = lib.ckks_find_primes(12, 62, 6), lib.ckks_find_primes(12, 61, 2)
+    assert lib.ckks_params_validate(12, wq, wp, 3) == lib.CKKS_OK
+    big = next(m for m in range(2 ** 62 + 1, 2 ** 62 + (2 << 12) * 4000, 2 << 12) if pow(3, m - 1, m) == 1)
+    assert lib.ckks_params_validate(12, [big] + wq[1:], wp, 3) == E
+    assert "2^62" in lib.ckks_last_error()
 
 
 def test_strerror(lib):
