@@ -35,6 +35,11 @@ BYTES_PER_HROT = 150_994_944  # ciphertext in (24 MiB) + key (96 MiB) + cipherte
 # modmul-class operations per HRot at level 23: 83.9M butterflies (160 limb
 # transforms), 44.0M ModUp, 16.8M inner product, 32.5M ModDown
 OPS_PER_HROT = 177_200_000
+# Derived ALU peak in modmul-class operations per second: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz = 39.32 T 32-bit lane-operations/s, at 16 lane-operations
+# per 64-bit modmul-class operation (the measured lazy butterfly is 2.3 T/s).
+# It decides a kernel's bound; the measured R_mm gives the ALU fractions.
+ALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9 / 16
 # limbs of 2^16 words each kernel family reads or writes per ciphertext at
 # level 23 (its own I/O, intermediates included)
 # ciphertexts per launch of the dominant kernel (the key switch's chunk)
@@ -53,7 +58,7 @@ def log(msg):
 
 # Sources the dominant kernel is compiled from: HBM traffic taken with
 # rocprofv3 counters is reported only while these are unchanged.
-KERNEL_SOURCES = ["keyswitch.hip", "ntt_core.h", "arith.h", "internal.h", "kernels.h", "automorph.h"]
+KERNEL_SOURCES = ["keyswitch.hip", "rowpass.h", "ntt_core.h", "arith.h", "internal.h", "kernels.h", "automorph.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "comb_ip_c3_traffic.txt")
 
 
@@ -275,14 +280,14 @@ def main():
         ops = kstat["alg_units"] / kstat["launches"]       # modmul-class operations per launch
         hbm_gbps = alg_bytes / avg_s / 1e9
         alu_frac = ops / avg_s / r_mm if r_mm else None
-        hbm_bound = r_mm is None or alg_bytes / (HBM_PEAK_GBPS * 1e9) >= ops / r_mm
+        hbm_bound = alg_bytes / (HBM_PEAK_GBPS * 1e9) >= ops / ALU_PEAK_OPS
         roof = {
             "kernel": kstat["name"],
             "bound": "hbm" if hbm_bound else "alu",
             "achieved": round(hbm_gbps, 2) if hbm_bound else round(ops / avg_s / 1e12, 4),
-            "peak": HBM_PEAK_GBPS if hbm_bound else round(r_mm / 1e12, 4),
+            "peak": HBM_PEAK_GBPS if hbm_bound else round(ALU_PEAK_OPS / 1e12, 4),
             "unit": "GB/s" if hbm_bound else "T modmul-class ops/s",
-            "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4) if hbm_bound else round(alu_frac, 4),
+            "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4) if hbm_bound else round(ops / avg_s / ALU_PEAK_OPS, 4),
             "traffic": measured_traffic(),
             "items_per_launch": items_per_launch,
             "alg_bytes_per_launch": int(alg_bytes),

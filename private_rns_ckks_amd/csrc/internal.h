@@ -77,6 +77,9 @@ struct Ctx {
   // Set while an allocation-free call runs: tracing records no events then
   // (creating them could allocate).
   bool no_alloc = false;
+  // Sequence number of the key-switch chunk being dumped (CKKS_DEBUG_DUMP),
+  // or -1 when dumping is off.
+  int dump_seq = -1;
   // Internal streams (default priority) on which consecutive chunks of a
   // batch run concurrently, forked from and joined back to the caller's
   // stream with events; created on first use.

@@ -24,7 +24,13 @@
 // (ks_decompose); per rotation, a gathered inner product over every limb
 // (ip_gather_kernel) and ks_back: the inverse NTT of the special limbs, H,
 // and a combining forward row pass.
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
+#include <string>
+#include <vector>
 
 #include "automorph.h"
 #include "kernels.h"
@@ -583,6 +589,43 @@ __global__ __launch_bounds__(256) void ip_gather_kernel(IPGatherArgs a) {
 // conversion to every target limb of every digit, and the forward column
 // pass of the converted limbs, into E (item b at E + b*estride,
 // [beta][next][N], lazy).  Y is overwritten.
+// Debug dumps of the key switch's intermediates, for localising a mismatch
+// against the oracle to one stage.  When the environment variable
+// CKKS_DEBUG_DUMP names a directory, each chunk of a key switch gets the next
+// sequence number and, after the step that produces it, every item's buffer
+// is copied to the host and written as raw little-endian 64-bit words to
+// <dir>/ks<seq>_<stage>_item<k>.u64:
+//   modup_in     [l+1][N]     y_i = [x_i qhat_i^-1]_{q_i}, coefficient form
+//   modup_out    [beta][next][N]  the ModUp conversion, coefficient form,
+//                congruent to the exact value (below 6q); the slots of a
+//                digit's own limbs are not written
+//   moddown_in   [2][K][N]    y_k = [acc_k phat_k^-1]_{p_k}, coefficient form
+//   moddown_out  [2][l+1][N]  the ModDown conversion times P^-1, coefficient
+//                form, congruent (below 6q)
+// The stream is synchronised for every dump.  Allocation-free calls dump
+// nothing.
+static std::atomic<int> g_dump_seq{0};
+
+int debug_dump(Ctx* c, hipStream_t s, const char* stage, int n_items, const uint64_t* base, uint64_t stride,
+               uint64_t words) {
+  const char* dir = getenv("CKKS_DEBUG_DUMP");
+  if (!dir || !*dir || c->no_alloc || c->dump_seq < 0) return CKKS_OK;
+  CKKS_HIP_CHECK(hipStreamSynchronize(s));
+  std::vector<uint64_t> h(words);
+  for (int k = 0; k < n_items; ++k) {
+    CKKS_HIP_CHECK(hipMemcpy(h.data(), base + k * stride, words * 8, hipMemcpyDeviceToHost));
+    char name[64];
+    snprintf(name, sizeof(name), "/ks%06d_%s_item%d.u64", c->dump_seq, stage, k);
+    const std::string path = std::string(dir) + name;
+    FILE* f = fopen(path.c_str(), "wb");
+    if (!f) return set_error(CKKS_EINVAL, "CKKS_DEBUG_DUMP: cannot write " + path);
+    const size_t wrote = fwrite(h.data(), 8, words, f);
+    fclose(f);
+    if (wrote != words) return set_error(CKKS_EINVAL, "CKKS_DEBUG_DUMP: short write to " + path);
+  }
+  return CKKS_OK;
+}
+
 int modup_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* Y, uint64_t ystride, uint64_t* E,
                 uint64_t estride) {
   const int nq = level + 1, next = nq + (int)c->K, beta = c->beta(level);
@@ -599,6 +642,7 @@ int modup_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* Y, uint
     }
     if ((rc = ntt_pass_only(c, s, Y, Y, ystride, ystride, n_items, jobs, true, false, 2, c->d_modup, off))) return rc;
   }
+  if ((rc = debug_dump(c, s, "modup_in", n_items, Y, ystride, (uint64_t)nq * c->N))) return rc;
   ModUpArgs mu;
   memset(&mu, 0, sizeof(mu));
   mu.x = Y;
@@ -618,6 +662,7 @@ int modup_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* Y, uint
     mu.offset[j] = en.offset;
   }
   if ((rc = launch_modup(c, s, mu, beta, n_items))) return rc;
+  if ((rc = debug_dump(c, s, "modup_out", n_items, E, estride, (uint64_t)beta * next * c->N))) return rc;
   NttJobs jobs;
   for (int j = 0; j < beta; ++j)
     for (int t = 0; t < next; ++t) {
@@ -646,6 +691,7 @@ int moddown_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* A, ui
       }
     if ((rc = ntt_pass_only(c, s, A, A, astride, astride, n_items, jobs, true, false, 2, c->d_moddown, off))) return rc;
   }
+  if ((rc = debug_dump(c, s, "moddown_in", n_items, A, astride, 2ull * K * c->N))) return rc;
   ModDownArgs md;
   memset(&md, 0, sizeof(md));
   md.acc = A;
@@ -661,6 +707,7 @@ int moddown_steps(Ctx* c, hipStream_t s, int level, int n_items, uint64_t* A, ui
   md.L = (int)c->L;
   md.K = K;
   if ((rc = launch_moddown_conv(c, s, md, n_items))) return rc;
+  if ((rc = debug_dump(c, s, "moddown_out", n_items, W, wstride, 2ull * nq * c->N))) return rc;
   NttJobs jobs;
   for (int comp = 0; comp < 2; ++comp)
     for (int i = 0; i < nq; ++i) jobs.add(comp * nq + i, comp * nq + i, i);
@@ -896,6 +943,10 @@ int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* 
   uint64_t* W = A + (uint64_t)2 * K * N;
   const int lr = logb_row(log_n);
   int rc;
+  {
+    const char* dump = getenv("CKKS_DEBUG_DUMP");
+    c->dump_seq = (dump && *dump) ? g_dump_seq++ : -1;
+  }
   {
     GatherArgs ga;
     memset(&ga, 0, sizeof(ga));

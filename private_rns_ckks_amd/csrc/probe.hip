@@ -124,7 +124,7 @@ __device__ __forceinline__ void step(uint64_t& x, uint64_t& z, uint64_t y, uint6
     x = a.a0 + a.a1;
     z = a.a2;
   } else if constexpr (OP == OP_BFLY_CT) {
-    nttc::ct_butterfly<true>(z, x, w, wp, q);  // words wrap past 2^64: the instructions are the same
+    nttc::ct_butterfly<nttc::AR_LAZY>(z, x, w, wp, q);  // words wrap past 2^64: the instructions are the same
   } else if constexpr (OP == OP_BFLY_GS) {
     nttc::gs_butterfly_lazy(z, x, w, wp, q, 4 * q);
   }

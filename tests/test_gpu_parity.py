@@ -367,6 +367,86 @@ def test_overlap_rejected(lib, orc, c3small):
         assert "overlap" in lib.ckks_last_error(), i
 
 
+def test_keyswitch_debug_dump_localises_stages(lib, orc, c3small, tmp_path, monkeypatch):
+    """CKKS_DEBUG_DUMP writes the key switch's intermediates; each is checked
+    against its definition, computed here from the oracle's transforms and
+    conversions, so a mismatch names its stage: the ModUp inputs
+    y_i = x_i [qhat_i^-1], the ModUp conversion, the special accumulators'
+    y_k = iNTT(sum_j NTT(modup_j) evk_j) [phat_k^-1] and the ModDown
+    conversion sum_k y_k [1/p_k]_{q_i} - #{y_k > (p_k-1)/2}."""
+    import glob
+    import os
+
+    ctx, P = c3small
+    level = 13  # two digits, the second partial
+    nq, N = level + 1, P.N
+    announce("keyswitch debug dump level=%d" % level)
+    d = S.uniform_limbs(S.stream(3, "gpu/dump/d"), P.q[:nq], N)
+    evk = S.uniform_limbs(S.stream(3, "gpu/dump/k"), P.mods, N, lead=(P.dnum, 2))
+    monkeypatch.setenv("CKKS_DEBUG_DUMP", str(tmp_path))
+    out = empty_dev((2, nq, N))
+    lib.ckks_keyswitch(ctx, to_dev(d), to_dev(evk), out, level)
+    monkeypatch.delenv("CKKS_DEBUG_DUMP")
+    assert np.array_equal(to_host(out), orc.keyswitch(P, level, d, evk))
+    seq = max(os.path.basename(f)[2:8] for f in glob.glob(str(tmp_path / "ks*_modup_in_item0.u64")))
+
+    def dump(stage, shape):
+        return np.fromfile(str(tmp_path / ("ks%s_%s_item0.u64" % (seq, stage))), dtype=np.uint64).reshape(shape)
+
+    x = orc.ntt_params(P, d, inverse=True)  # coefficient form
+    beta, alpha, K = P.beta(level), P.alpha, P.K
+    next_ = nq + K
+    ext = P.ext_mods(level)
+    # modup_in
+    y = dump("modup_in", (nq, N))
+    for j in range(beta):
+        lo, hi = j * alpha, min((j + 1) * alpha, nq)
+        for i in range(lo, hi):
+            qi = P.q[i]
+            qhat = 1
+            for t in range(lo, hi):
+                if t != i:
+                    qhat *= P.q[t]
+            c = pow(qhat % qi, -1, qi)
+            assert [int(v) for v in y[i]] == [int(v) * c % qi for v in x[i]], ("modup_in", i)
+    # modup_out
+    e = dump("modup_out", (beta, next_, N))
+    mu = [orc.modup(P, level, j, x) for j in range(beta)]
+    for j in range(beta):
+        lo, hi = j * alpha, min((j + 1) * alpha, nq)
+        for t in range(next_):
+            if lo <= t < hi:
+                continue
+            m = ext[t]
+            assert np.array_equal(e[j, t] % np.uint64(m), mu[j][t]), ("modup_out", j, t)
+    # moddown_in
+    a = dump("moddown_in", (2, K, N))
+    psi_p = P.psi[P.L:]
+    Pprod = 1
+    for pk in P.p:
+        Pprod *= pk
+    ys = np.zeros((2, K, N), dtype=object)
+    for k, pk in enumerate(P.p):
+        acc = [np.zeros(N, dtype=object), np.zeros(N, dtype=object)]
+        for j in range(beta):
+            f = orc.ntt(mu[j][nq + k][None], [pk], [psi_p[k]], P.log_n)[0].astype(object)
+            for comp in range(2):
+                acc[comp] = (acc[comp] + f * evk[j, comp, P.L + k].astype(object)) % pk
+        phinv = pow((Pprod // pk) % pk, -1, pk)
+        for comp in range(2):
+            coeff = orc.ntt(np.array(acc[comp], dtype=np.uint64)[None], [pk], [psi_p[k]], P.log_n, inverse=True)[0]
+            ys[comp, k] = coeff.astype(object) * phinv % pk
+            assert [int(v) for v in a[comp, k]] == list(ys[comp, k]), ("moddown_in", comp, k)
+    # moddown_out
+    w = dump("moddown_out", (2, nq, N))
+    for comp in range(2):
+        neg = sum((ys[comp, k] > (pk - 1) // 2).astype(object) for k, pk in enumerate(P.p))
+        for i in range(nq):
+            qi = P.q[i]
+            ref = sum(ys[comp, k] * pow(pk % qi, -1, qi) for k, pk in enumerate(P.p)) - neg
+            assert [int(v) % qi for v in w[comp, i]] == [int(v) % qi for v in ref], ("moddown_out", comp, i)
+
+
 # ---------------------------------------------------------------- polynomial evaluation
 
 @pytest.mark.parametrize("coeffs,level", [
