@@ -134,8 +134,8 @@ typedef struct {
  * "ntt_row_combine" (forward row pass + final combination, hoisted
  * rotations), "automorph", "modup",
  * "moddown_conv", "rescale", "tensor", "ptmac", "ctmac", "add",
- * "const_mul", "ip_gather".  NULL or "" stops
- * tracing.
+ * "const_mul", "term_mac" (polynomial evaluation's constant multiples),
+ * "ip_gather".  NULL or "" stops tracing.
  * Tracing adds two event records per traced launch and nothing else. */
 int ckks_trace_begin(ckks_ctx* ctx, const char* kernel);
 /* Waits for the recorded events, returns the totals and stops tracing. */

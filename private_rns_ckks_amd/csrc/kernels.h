@@ -112,13 +112,11 @@ int launch_ptmac(Ctx* c, hipStream_t s, PtMacArgs& a, int n_out);
 int launch_ctmac(Ctx* c, hipStream_t s, CtMacArgs& a, int n_out);
 // Rescale of `batch` items by limb `level`: v = iNTT of that limb per item
 // and component ([2][N], canonical), w scratch [2][level][N], out
-// [2][out_limbs][N] (out_limbs <= 0: level), the output limbs i < out_limbs
-// only; add0: per-limb constant added to component 0; acc: [2][out_limbs][N]
-// per item added to the output (may equal out).
+// [2][level][N]; add0: per-limb constant added to component 0; acc:
+// [2][level][N] per item added to the output (may equal out).
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
                   uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
-                  const uint64_t* add0 = nullptr, int out_limbs = 0, const uint64_t* acc = nullptr,
-                  uint64_t acc_bstride = 0);
+                  const uint64_t* add0 = nullptr, const uint64_t* acc = nullptr, uint64_t acc_bstride = 0);
 int launch_const_mul(Ctx* c, hipStream_t s, ConstMulArgs& a, int batch);
 
 // Sum of constant multiples of up to kMaxTerms ciphertexts that share one

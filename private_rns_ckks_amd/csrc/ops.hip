@@ -53,11 +53,10 @@ int check_galois(const Ctx* c, uint32_t g) {
 }
 
 // Rescale of `batch` items: in [2][level+1][N] at in + b*in_stride -> out
-// [2][out_limbs][N] (out_limbs <= 0: level), plus acc (same layout as out,
-// may equal it) when given.
+// [2][level][N], plus acc (same layout as out, may equal it) when given.
 int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride, uint64_t* out, uint64_t out_stride,
                   int batch, int level, uint64_t* ws, uint64_t ws_words, const uint64_t* add0 = nullptr,
-                  int out_limbs = 0, const uint64_t* acc = nullptr) {
+                  const uint64_t* acc = nullptr) {
   const uint32_t N = c->N;
   const uint64_t per = (uint64_t)N * (2 + 2 * level);
   const int chunk = (int)std::max<uint64_t>(1, std::min<uint64_t>(kMaxChunk, ws_words / per));
@@ -71,7 +70,7 @@ int rescale_batch(Ctx* c, hipStream_t s, const uint64_t* in, uint64_t in_stride,
     if (rc) return rc;
     // conversion and final combination fused into the forward NTT of w
     if ((rc = rescale_fused(c, s, in + b0 * in_stride, in_stride, V, per, W, per, out + b0 * out_stride, out_stride, n,
-                            level, add0, out_limbs, acc ? acc + b0 * out_stride : nullptr, out_stride)))
+                            level, add0, acc ? acc + b0 * out_stride : nullptr, out_stride)))
       return rc;
   }
   return CKKS_OK;
@@ -157,7 +156,7 @@ static int mul_relin_rescale(Ctx* ctx, hipStream_t stream, const uint64_t* d_a, 
     if ((rc = ks_chunk(ctx, ls, level, n, items, tens, tens, 0, rel, nq, S))) break;
     if (rescale)
       rc = rescale_batch(ctx, ls, R, rel, d_out + b0 * 2ull * level * N, 2ull * level * N, n, level, S,
-                         chunk * std::max(ks, rs_per), add0, 0, acc ? acc + b0 * 2ull * level * N : nullptr);
+                         chunk * std::max(ks, rs_per), add0, acc ? acc + b0 * 2ull * level * N : nullptr);
   }
   return join_lanes(ctx, stream, lanes, rc);
 }
@@ -695,7 +694,7 @@ struct TreeEval {
     uint64_t cv[64];
     if (has_k0) consts(t, k0, cv);
     return rescale_batch(ctx, s, G, ct_words(t + 1), out, ct_words(t), n, t + 1, ctx->ws, ctx->ws_words,
-                         has_k0 ? cv : nullptr, 0, acc);
+                         has_k0 ? cv : nullptr, acc);
   }
 
   // out = (k0, 0): the trivial ciphertext of a constant

@@ -3,7 +3,7 @@
 // pass (the converted limbs make one round trip through memory instead of
 // three).  Optionally a per-limb constant (a constant polynomial in NTT form)
 // is added to component 0, and another ciphertext to the output, by the same
-// final store, and only the lowest output limbs are produced.  Per item,
+// final store.  Per item,
 // component and limb i < l, with v = iNTT(c_l) canonical and vbar its centred
 // lift:
 //   w_i   = (vbar mod q_i) * [q_l^-1]_{q_i}
@@ -23,14 +23,13 @@ struct RescalePassArgs {
   const uint64_t* v;   // item b: v + b*v_bstride, [2][N] iNTT of limb l
   uint64_t* w;         // item b: w + b*w_bstride, [2][l][N]
   const uint64_t* ct;  // item b: ct + b*ct_bstride, [2][l+1][N]
-  uint64_t* out;       // item b: out + b*out_bstride, [2][out_limbs][N]
-  const uint64_t* acc; // optional, added to the output: item b at acc + b*acc_bstride, [2][out_limbs][N]
+  uint64_t* out;       // item b: out + b*out_bstride, [2][l][N]
+  const uint64_t* acc; // optional, added to the output: item b at acc + b*acc_bstride, [2][l][N]
   uint64_t v_bstride, w_bstride, ct_bstride, out_bstride, acc_bstride;
   const uint64_t* tab;  // [L][L][4]: for level l, limb i: {q_l^-1, Shoup, q_l mod q_i, 0}
   const PrimeConst* prime;
   const uint64_t* tw;  // forward twiddles
   int log_n, level, L;
-  int out_limbs;       // output limbs 0 .. out_limbs-1 (<= level)
   int has_add;
   uint64_t add0[64];  // has_add: added to component 0 of limb i (a constant in NTT form)
 };
@@ -56,8 +55,8 @@ template <int RA, int RB, int LOGN>
 __global__ __launch_bounds__(kThreads) void rescale_col_kernel(RescalePassArgs a) {
   constexpr int ROWS = 1 << (RA + RB);
   __shared__ uint64_t lds[lds_words<true, RB, ROWS>()];
-  const int job = blockIdx.y, item = blockIdx.z;  // job = comp * out_limbs + i
-  const int comp = job / a.out_limbs, i = job % a.out_limbs;
+  const int job = blockIdx.y, item = blockIdx.z;  // job = comp * l + i
+  const int comp = job / a.level, i = job % a.level;
   const PrimeConst& pc = a.prime[i];
   const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
   PrepIO io;
@@ -100,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void rescale_row_kernel(RescalePassArgs a
   __shared__ uint64_t lds[lds_words<false, RB, ROWS>()];
   const GridPos gp = row_grid_pos();
   const int job = gp.job, item = gp.item;
-  const int comp = job / a.out_limbs, i = job % a.out_limbs;
+  const int comp = job / a.level, i = job % a.level;
   const PrimeConst& pc = a.prime[i];
   const uint64_t* rs = a.tab + ((uint64_t)a.level * a.L + i) * 4;
   RescaleCombineIO io;
@@ -120,9 +119,7 @@ __global__ __launch_bounds__(kThreads) void rescale_row_kernel(RescalePassArgs a
 
 int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride, const uint64_t* v, uint64_t v_bstride,
                   uint64_t* w, uint64_t w_bstride, uint64_t* out, uint64_t out_bstride, int batch, int level,
-                  const uint64_t* add0, int out_limbs, const uint64_t* acc, uint64_t acc_bstride) {
-  if (out_limbs <= 0) out_limbs = level;
-  if (out_limbs > level) return set_error(CKKS_EINTERNAL, "rescale output limbs above the level");
+                  const uint64_t* add0, const uint64_t* acc, uint64_t acc_bstride) {
   const uint32_t N = c->N;
   const int log_n = (int)c->log_n;
   const int lr = logb_row(log_n), lc = logb_col(log_n);
@@ -142,25 +139,24 @@ int rescale_fused(Ctx* c, hipStream_t s, const uint64_t* ct, uint64_t ct_bstride
   a.log_n = log_n;
   a.level = level;
   a.L = (int)c->L;
-  a.out_limbs = out_limbs;
   a.acc = acc;
   a.acc_bstride = acc_bstride;
   if (add0) {
     if (level > 64) return set_error(CKKS_EINTERNAL, "too many limbs for a fused constant");
     a.has_add = 1;
-    for (int i = 0; i < out_limbs; ++i) a.add0[i] = add0[i];
+    for (int i = 0; i < level; ++i) a.add0[i] = add0[i];
   }
   auto fc = CKKS_PICK_PASS(rescale_col_kernel, log_n, lc);
   auto fr = CKKS_PICK_PASS(rescale_row_kernel, log_n, lr);
   if (!fc || !fr) return set_error(CKKS_EINTERNAL, "unsupported N");
   {
-    TraceScope ts(c, s, "rescale", (double)batch * 2 * out_limbs * ((double)(N / 2) * lc + N));
-    hipLaunchKernelGGL(fc, dim3(pass_tiles(N, lc), 2 * out_limbs, batch), dim3(kThreads), 0, s, a);
+    TraceScope ts(c, s, "rescale", (double)batch * 2 * level * ((double)(N / 2) * lc + N));
+    hipLaunchKernelGGL(fc, dim3(pass_tiles(N, lc), 2 * level, batch), dim3(kThreads), 0, s, a);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   {
-    TraceScope ts(c, s, "rescale", (double)batch * 2 * out_limbs * ((double)(N / 2) * lr + N));
-    hipLaunchKernelGGL(fr, dim3(pass_tiles(N, lr), 2 * out_limbs, batch), dim3(kThreads), 0, s, a);
+    TraceScope ts(c, s, "rescale", (double)batch * 2 * level * ((double)(N / 2) * lr + N));
+    hipLaunchKernelGGL(fr, dim3(pass_tiles(N, lr), 2 * level, batch), dim3(kThreads), 0, s, a);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   return CKKS_OK;
