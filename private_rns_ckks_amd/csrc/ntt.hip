@@ -125,8 +125,8 @@ typedef void (*PassFn)(PassArgs);
 
 int launch_pass(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs, int logb, bool inv, bool colfast) {
   const int log_n = (int)c->log_n;
-  PassFn fn = inv ? (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, true)
-                             : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, false))
+  // the inverse row pass runs in ntt_row_inv_kernel (launch_row_inv)
+  PassFn fn = inv ? (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, true) : nullptr)
                   : (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, true)
                              : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, false));
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
@@ -204,6 +204,7 @@ int ntt_pass_only(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, siz
   a.dst_bstride = dst_bstride;
   a.final_pass = first ? 0 : 1;
   const bool colpass = (inverse != first);  // forward first / inverse second
+  if (inverse && first) return launch_row_inv(c, s, a, batch, jobs.n);
   return launch_pass(c, s, a, batch, jobs.n, colpass ? logb_col(log_n) : logb_row(log_n), inverse, colpass);
 }
 
