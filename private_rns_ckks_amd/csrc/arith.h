@@ -13,6 +13,8 @@
 //                  correction, so callers stay lazy.
 //   reduce_2q      [0, 2q) -> [0, q)
 //   reduce64       any 64-bit value -> [0, q), using floor(2^64/q).
+//   reduce_hi      partial reduction with a quotient from the high word
+//                  (one 32-bit multiply-high), for q > 2^33.
 //   U128 / mac     exact 128-bit accumulation of 64x64 products and one
 //                  Barrett-style reduction per output.
 #pragma once
@@ -104,6 +106,16 @@ __device__ __forceinline__ uint64_t reduce64(uint64_t a, uint64_t q, uint64_t in
   uint64_t r = a - mulhi64(a, inv1) * q;  // Shoup with w = 1: r in [0, 2q)
   return reduce_2q(r, q);
 }
+
+// For 2^33 < q (so m = floor(2^64/q) < 2^31): with h = floor(a / 2^32), the
+// estimate e = floor(h m / 2^32) never exceeds a/q and falls short of it by
+// less than 2^32/q + h/2^32 + 1, so a - e q lies in [0, 2.5q) for any 64-bit
+// a and in [0, 2q) for a < 2^63.
+__device__ __forceinline__ uint64_t reduce_hi(uint64_t a, uint64_t q, uint32_t m) {
+  const uint32_t e = __umulhi((uint32_t)(a >> 32), m);
+  return a - (uint64_t)e * q;
+}
+constexpr uint64_t kReduceHiMin = 1ull << 33;  // reduce_hi needs q above this
 
 __device__ __forceinline__ U128 mul_wide(uint64_t a, uint64_t b) {
   U128 r;

@@ -183,14 +183,13 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
 
 // ---------------------------------------------------------------------------
 // Inner product of the special limbs only (targets t = l+1 .. l+K), followed
-// on the same tile by the first pass of their inverse NTT (the row pass), so
-// the accumulators leave in the form the fused ModDown conversion reads.
+// on the same tile by the first pass of their inverse NTT (the row pass); the
+// inverse column pass (scaled for ModDown) completes it.
 //
 // The inverse row pass of one component: the thread's 8 words (rows
 // base..base+7 of its column, canonical) go through the Gentleman-Sande stages
 // of row bits 0-2 in registers, then of row bits 3.. and 6.. through the LDS
-// tile, and are stored in the range of the inverse butterflies of AR ([0, q)
-// after a final reduction for AR_LAZY).
+// tile, and are stored below 4q for the column pass (inv_row_out).
 template <int LOGB, int AR>
 __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t* lds, uint32_t tile, int log_n,
                                                      const uint64_t* twi, uint64_t q, uint64_t inv1, uint64_t* dst) {
@@ -221,7 +220,7 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
     if constexpr (G::R1 == 0) {
 #pragma unroll
       for (int i = 0; i < (1 << G::R2); ++i) {
-        const uint64_t v = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
+        const uint64_t v = inv_row_out<AR>(y[i], q, inv1);
         dst[ip_word<LOGB>(tile, b + (i << 3), c)] = v;
       }
     } else {
@@ -244,7 +243,7 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
       round_regs<G::R1, true, AR, false, false, P1>(y, b, P1, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i) {
-        const uint64_t v = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
+        const uint64_t v = inv_row_out<AR>(y[i], q, inv1);
         dst[ip_word<LOGB>(tile, b + (i << P1), c)] = v;
       }
     }

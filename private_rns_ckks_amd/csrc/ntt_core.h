@@ -276,13 +276,23 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
     for (int i = 0; i < (1 << R2); ++i) x[i] = lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos2), col)];
     round_regs<R2, INV, AR, COLFAST, COLFAST && INV, R1>(x, base, pos2, col, LOGB, tile, s0, log_n, tw, q);
     if (INV && AR == AR_LAZY && fin.mode != 2) {
-      // lazy inverse: words below 2^10 q, reduced once (the next pass, or the caller, takes them below q)
+      // lazy inverse: words below 2^10 q, reduced once.  After the first
+      // pass [0, 2.5q) is enough (the next pass takes words below 4q).
+      if (fin.mode == 0 && q > kReduceHiMin) {
 #pragma unroll
-      for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);
+        for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_hi(x[i], q, (uint32_t)fin.inv1);
+      } else {
+#pragma unroll
+        for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);
+      }
     } else if (fin.mode == 1) {
       if (INV) {
 #pragma unroll
         for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_4q(x[i], q);
+      } else if (AR == AR_LAZY && q > kReduceHiMin && q < (1ull << 56)) {
+        // lazy forward words lie below 65q < 2^63: reduce_hi leaves [0, 2q)
+#pragma unroll
+        for (int i = 0; i < (1 << R2); ++i) x[i] = reduce_2q(reduce_hi(x[i], q, (uint32_t)fin.inv1), q);
       } else {
 #pragma unroll
         for (int i = 0; i < (1 << R2); ++i) x[i] = reduce64(x[i], q, fin.inv1);

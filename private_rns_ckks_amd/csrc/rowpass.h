@@ -152,9 +152,19 @@ __device__ __forceinline__ void ip_inv_butterflies(uint64_t (&x)[1 << R], int ba
   }
 }
 
+// Output word of an inverse row pass, for the inverse column pass that
+// follows (it takes words below 4q): the lazy butterflies end below 2^10 q and
+// are reduced once, to [0, 2.5q) (reduce_hi) or [0, q); the other ranges are
+// already below 4q.
+template <int AR>
+__device__ __forceinline__ uint64_t inv_row_out(uint64_t v, uint64_t q, uint64_t inv1) {
+  if (AR != AR_LAZY) return v;
+  return q > kReduceHiMin ? reduce_hi(v, q, (uint32_t)inv1) : reduce64(v, q, inv1);
+}
+
 // Inverse row pass of one limb on the tile: src holds canonical (or below
 // 4q) words, dst receives the pass's output for the column pass that follows
-// ([0, q) for AR_LAZY, reduced once at the end; the range of AR otherwise).  Rounds on
+// (below 4q: inv_row_out).  Rounds on
 // row bits 0-2 (8 consecutive words per thread, 16-byte loads), then 3.. and
 // 6.. through the LDS tile; the last round's stores cover consecutive rows
 // across the wave.
@@ -191,7 +201,7 @@ __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* d
     ip_inv_butterflies<G::R2, LOGB, AR, 3>(y, b, 3, c, twl, q);
 #pragma unroll
     for (int i = 0; i < (1 << G::R2); ++i) {
-      if constexpr (G::R1 == 0) dst[ip_word<LOGB>(tile, b + (i << 3), c)] = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
+      if constexpr (G::R1 == 0) dst[ip_word<LOGB>(tile, b + (i << 3), c)] = inv_row_out<AR>(y[i], q, inv1);
       else lds[ip_lds<LOGB>(b + (i << 3), c)] = y[i];
     }
   }
@@ -209,7 +219,7 @@ __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* d
       ip_inv_butterflies<G::R1, LOGB, AR, P1>(y, b, P1, c, twl, q);
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i)
-        dst[ip_word<LOGB>(tile, b + (i << P1), c)] = AR == AR_LAZY ? reduce64(y[i], q, inv1) : y[i];
+        dst[ip_word<LOGB>(tile, b + (i << P1), c)] = inv_row_out<AR>(y[i], q, inv1);
     }
   }
 }
