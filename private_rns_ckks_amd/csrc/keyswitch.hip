@@ -187,7 +187,7 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
 // inverse column pass (scaled for ModDown) completes it.
 //
 // The inverse row pass of one component: the thread's 8 words (rows
-// base..base+7 of its column, canonical) go through the Gentleman-Sande stages
+// base..base+7 of its column, below 4q, below 2q for AR_STRICT) go through the Gentleman-Sande stages
 // of row bits 0-2 in registers, then of row bits 3.. and 6.. through the LDS
 // tile, and are stored below 4q for the column pass (inv_row_out).
 template <int LOGB, int AR>
@@ -278,14 +278,24 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
       ip_accumulate<LOGB, LOGN, AR_HARVEY>(a, lds, twl, pc, keyl, gp, accb, acca);
     else
       ip_accumulate<LOGB, LOGN, AR_STRICT>(a, lds, twl, pc, keyl, gp, accb, acca);
+    // remove the 2^-64: [0, 4q), the range the lazy and Harvey inverse
+    // butterflies take; the exact-quotient ones take [0, 2q)
+    const int iar = inv_ar(pc.q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // remove the 2^-64: canonical accumulators
-      accb[i] = reduce_4q(mul_shoup_lazy(accb[i], pc.r64, pc.r64p, pc.q), pc.q);
-      acca[i] = reduce_4q(mul_shoup_lazy(acca[i], pc.r64, pc.r64p, pc.q), pc.q);
+    for (int i = 0; i < 8; ++i) {
+      accb[i] = mul_shoup_lazy(accb[i], pc.r64, pc.r64p, pc.q);
+      acca[i] = mul_shoup_lazy(acca[i], pc.r64, pc.r64p, pc.q);
+    }
+    if (iar == AR_STRICT) {
+      const uint64_t two_q = 2 * pc.q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        accb[i] = accb[i] >= two_q ? accb[i] - two_q : accb[i];
+        acca[i] = acca[i] >= two_q ? acca[i] - two_q : acca[i];
+      }
     }
     uint64_t* ob = a.acc + gp.item * a.acc_bstride + ((uint64_t)(t - a.level - 1) << log_n);
     uint64_t* oa = ob + ((uint64_t)a.K << log_n);
-    const int iar = inv_ar(pc.q);
     if (iar == AR_LAZY) {
       ip_inverse_row_store<LOGB, AR_LAZY>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
       ip_inverse_row_store<LOGB, AR_LAZY>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
@@ -345,10 +355,18 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
   uint64_t acc[2][8];
   ip_accumulate<LOGB, LOGN, AR>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
   const uint64_t cw = a.pinv64[2 * i], cwp = a.pinv64[2 * i + 1];
+  // Lazy primes in (2^33, 2^56): the row pass leaves NTT(w) below 65q < 2^63,
+  // which reduce_hi takes to [0, 2q); with acc*P^-1 in [0, 4q) and canonical
+  // add and accum terms, acc + 2q - w + add + accum lies below 8q and is
+  // reduced once.  Otherwise every term is made canonical first.
+  const bool fast = AR == AR_LAZY && q > kReduceHiMin && q < (1ull << 56);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[c][r] = reduce_4q(mul_shoup_lazy(acc[c][r], cw, cwp, q), q);
+    for (int r = 0; r < 8; ++r) {
+      acc[c][r] = mul_shoup_lazy(acc[c][r], cw, cwp, q);
+      if (!fast) acc[c][r] = reduce_4q(acc[c][r], q);
+    }
   int col, base;
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(gp.tile, base, col);
@@ -378,14 +396,27 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
     }
     ulonglong2* o = reinterpret_cast<ulonglong2*>(a.out + item * a.out_bstride +
                                                   ((uint64_t)(c * a.out_comp_limbs + i) << log_n) + w0);
+    if (fast) {
+      const uint64_t two_q = 2 * q, four_q = 4 * q;
+      const uint32_t m = (uint32_t)pc.inv1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ulonglong2 v;
-      uint64_t e0 = sub_mod(acc[c][2 * r], reduce64(x[2 * r], q, pc.inv1), q);
-      uint64_t e1 = sub_mod(acc[c][2 * r + 1], reduce64(x[2 * r + 1], q, pc.inv1), q);
-      v.x = add_mod(add_mod(e0, add[2 * r], q), accum[2 * r], q);
-      v.y = add_mod(add_mod(e1, add[2 * r + 1], q), accum[2 * r + 1], q);
-      o[r] = v;
+      for (int r = 0; r < 4; ++r) {
+        uint64_t e0 = acc[c][2 * r] + two_q - reduce_hi(x[2 * r], q, m) + add[2 * r] + accum[2 * r];
+        uint64_t e1 = acc[c][2 * r + 1] + two_q - reduce_hi(x[2 * r + 1], q, m) + add[2 * r + 1] + accum[2 * r + 1];
+        e0 = reduce_4q(e0 >= four_q ? e0 - four_q : e0, q);
+        e1 = reduce_4q(e1 >= four_q ? e1 - four_q : e1, q);
+        o[r] = make_ulonglong2(e0, e1);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ulonglong2 v;
+        uint64_t e0 = sub_mod(acc[c][2 * r], reduce64(x[2 * r], q, pc.inv1), q);
+        uint64_t e1 = sub_mod(acc[c][2 * r + 1], reduce64(x[2 * r + 1], q, pc.inv1), q);
+        v.x = add_mod(add_mod(e0, add[2 * r], q), accum[2 * r], q);
+        v.y = add_mod(add_mod(e1, add[2 * r + 1], q), accum[2 * r + 1], q);
+        o[r] = v;
+      }
     }
   }
 }
