@@ -31,8 +31,9 @@ int ckks_probe_list(char* buf, int len);
  *               median of 9 timed launches of 8 waves per SIMD, each lane
  *               running 16 independent chains;
  *   "copy"      bytes read plus bytes written per second of a device copy of
- *               copy_bytes (a multiple of 16, at least 4096; two buffers of
- *               that size are allocated and freed), median of 15 copies.
+ *               copy_bytes (a positive multiple of 4096; two buffers of that
+ *               size are allocated and freed), median of 15 copies; one
+ *               16-byte word per thread and one 4 KiB block per workgroup.
  * *ms (optional) receives the median launch time.  copy_bytes is ignored by
  * the ALU probes.  Returns CKKS_OK, CKKS_EINVAL (unknown probe, bad size),
  * CKKS_ENOMEM or CKKS_EHIP. */
