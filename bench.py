@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -406,22 +407,27 @@ def summarize_counters(root, traffic_out=None, command=""):
         w_b = avg[(dom, "WRITE_SIZE")] * wscale * 1024
         n_f = len(per[(dom, "FETCH_SIZE")])
         items = DOMINANT_ITEMS_PER_LAUNCH
-        alg = items * KERNEL_IO_LIMBS[lib.DOMINANT_KERNEL] * (1 << 16) * 8
+        kio = items * KERNEL_IO_LIMBS[lib.DOMINANT_KERNEL] * (1 << 16) * 8
+        kname = re.sub(r"\(anonymous namespace\)::|^void |ckks::", "", dom).split("(")[0]
         with open(traffic_out, "w") as f:
-            f.write("# HBM traffic per launch of %s on the HRot batch (N=2^16, L=24 + K=8, dnum=3,\n" % dom[:60])
+            f.write("# HBM traffic per launch of %s on the HRot batch (N=2^16, L=24 + K=8, dnum=3,\n" % kname)
             f.write("# level 23, 32 ciphertexts; launches of %d ciphertexts), %d dispatches averaged.\n" % (items, n_f))
             f.write("# Command (MI355X, repository root; FETCH_SIZE and WRITE_SIZE each in its own run):\n")
             f.write("#   %s\n" % command)
             f.write("# Scale: the probe copy of 1 GiB reads FETCH_SIZE x %.4f and writes WRITE_SIZE x %.4f\n"
                     % (fscale, wscale))
-            f.write("# of its size, so the counters are multiplied by those factors.  Algorithmic bytes\n")
-            f.write("# per launch: %d items x %d limbs x 2^16 words x 8 B (the kernel's own reads and\n"
+            f.write("# of its size, so the counters are multiplied by those factors.  Kernel I/O bytes\n")
+            f.write("# per launch: %d items x %d limbs x 2^16 words x 8 B (every limb the kernel reads\n"
                     % (items, KERNEL_IO_LIMBS[lib.DOMINANT_KERNEL]))
-            f.write("# writes).  bench.py reports traffic while the sources hash to sources_sha256.\n")
+            f.write("# or writes, once); algorithmic bytes per launch: %d HRots x %d B (ciphertext in,\n"
+                    % (items, BYTES_PER_HROT))
+            f.write("# key, ciphertext out).  bench.py reports traffic while the sources hash to\n")
+            f.write("# sources_sha256.\n")
             f.write("sources_sha256: %s\n" % kernel_sources_sha256())
             f.write("fetch_bytes_per_launch: %d\n" % round(f_b))
             f.write("write_bytes_per_launch: %d\n" % round(w_b))
-            f.write("algorithmic_bytes_per_launch: %d\n" % alg)
+            f.write("kernel_io_bytes_per_launch: %d\n" % kio)
+            f.write("algorithmic_bytes_per_launch: %d\n" % (items * BYTES_PER_HROT))
     return "\n".join(lines)
 
 
