@@ -155,20 +155,28 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
       ip_row_pass<LOGB, AR>(x, src, lds, twl, tile, log_n, q);
     }
+    // one key component at a time: 16 registers of key words live, not 32
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
-    ulonglong2 vb[4], va[4];
+    {
+      ulonglong2 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vb[i] = kb[i];
-      va[i] = ka[i];
+      for (int i = 0; i < 4; ++i) v[i] = kb[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accb[2 * i] += mont_mul_lazy(x[2 * i], v[i].x, q, mp);
+        accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], v[i].y, q, mp);
+      }
     }
+    {
+      ulonglong2 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      accb[2 * i] += mont_mul_lazy(x[2 * i], vb[i].x, q, mp);
-      accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], vb[i].y, q, mp);
-      acca[2 * i] += mont_mul_lazy(x[2 * i], va[i].x, q, mp);
-      acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], va[i].y, q, mp);
+      for (int i = 0; i < 4; ++i) v[i] = ka[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acca[2 * i] += mont_mul_lazy(x[2 * i], v[i].x, q, mp);
+        acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], v[i].y, q, mp);
+      }
     }
     if (++since == fold) {
       since = 0;
