@@ -217,6 +217,20 @@ struct Finish {
 __host__ __device__ constexpr int logb_col(int log_n) { return (log_n + 1) / 2; }
 __host__ __device__ constexpr int logb_row(int log_n) { return log_n - logb_col(log_n); }
 
+// Tile word (column-major) handled by thread tid in step k of a staging loop:
+// the workgroup sweeps the tile (WAVE = false), or each wave sweeps its own
+// 64 * PER words (WAVE = true); either way consecutive lanes take
+// consecutive words.
+template <bool WAVE, int PER>
+__device__ __forceinline__ int stage_index(int tid, int k) {
+  return WAVE ? (tid >> 6) * (64 * PER) + k * 64 + (tid & 63) : tid + k * kThreads;
+}
+
+// The wave's LDS reads and writes so far are complete; the memory clobber
+// keeps the compiler from moving LDS accesses across.  A wave runs in
+// lockstep, so its lanes then see each other's writes without a barrier.
+__device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // LOGN > 0 fixes log N at compile time (index arithmetic folds to constants);
 // LOGN = 0 takes it from log_n_rt.
 template <int RA, int RB, bool INV, bool COLFAST, int AR, int LOGN, class IO>
@@ -236,6 +250,12 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
   constexpr bool stage_in = INV && !COLFAST;   // inverse row pass: first round strided in memory
   constexpr bool stage_out = !INV && !COLFAST; // forward row pass: last round strided in memory
   constexpr int PER = TILE / kThreads;  // words per thread in the staging loops
+  // When every thread takes part in the last round of the forward row pass,
+  // wave w's threads hold exactly tile words [64 w PER, 64 (w+1) PER)
+  // (column-major: e = col * ROWS + row), so each wave stores its own words
+  // in coalesced order after waiting only for its own LDS writes, not for a
+  // workgroup barrier (C2 forward row pass 123 against 127-129 us).
+  constexpr bool wave_out = stage_out && kCols * (ROWS >> R2) == kThreads;
   if (stage_in) {
     // all loads first, then the LDS and side stores: keeps the loads in flight together
     uint64_t v[PER];
@@ -314,17 +334,20 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
     }
   }
   if (stage_out) {
-    __syncthreads();
+    if constexpr (wave_out)
+      wave_lds_wait();
+    else
+      __syncthreads();
     // fetch every operand of the epilogue before the first store
     typename IO::Ops ops[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      const int e = stage_index<wave_out, PER>(tid, k), row = e % ROWS, col = e / ROWS;
       ops[k] = io.fetch(tile_index<COLFAST>(tile, row, col, LOGB, log_n));
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int e = tid + k * kThreads, row = e % ROWS, col = e / ROWS;
+      const int e = stage_index<wave_out, PER>(tid, k), row = e % ROWS, col = e / ROWS;
       io.store(tile_index<COLFAST>(tile, row, col, LOGB, log_n), lds[lds_index<COLFAST, RB, ROWS>(row, col)], ops[k]);
     }
   }
