@@ -205,21 +205,21 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
   constexpr int T = G::THREADS;
   const uint32_t s0 = (uint32_t)logb_col(log_n);
   int col, base;
-  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  ip_item<3, LOGB>(0, 0, col, base);
   {
     const uint32_t blk = tile * G::KC + col;
     round_regs<3, true, AR, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
   }
-  __syncthreads();  // every thread has read the tile's previous contents
+  wave_lds_wait();  // the wave has read its columns' previous contents
 #pragma unroll
   for (int i = 0; i < 8; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
-  __syncthreads();
+  wave_lds_wait();
   // row bits [3, 3 + R2)
   constexpr int N2 = 8 >> G::R2;
 #pragma unroll
   for (int k = 0; k < N2; ++k) {
     int c, b;
-    item_coords<false, G::R2, LOGB>(threadIdx.x + k * T, 3, c, b);
+    ip_item<G::R2, LOGB>(k, 3, c, b);
     uint64_t y[1 << G::R2];
 #pragma unroll
     for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
@@ -237,13 +237,13 @@ __device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t*
     }
   }
   if constexpr (G::R1 > 0) {
-    __syncthreads();
+    wave_lds_wait();
     constexpr int N1 = 8 >> G::R1;
     constexpr int P1 = 3 + G::R2;
 #pragma unroll
     for (int k = 0; k < N1; ++k) {
       int c, b;
-      item_coords<false, G::R1, LOGB>(threadIdx.x + k * T, P1, c, b);
+      ip_item<G::R1, LOGB>(k, P1, c, b);
       uint64_t y[1 << G::R1];
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
@@ -272,6 +272,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
   const uint32_t s0 = (uint32_t)logb_col(log_n);
   const uint64_t* tw_i = twi + ((uint64_t)keyl << (log_n + 1));
   ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)keyl << (log_n + 1)), g0.tile, s0);
+  __syncthreads();  // every wave reads the twiddles every thread staged
   int col, base;
   item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
   for (int k = 0; k < a.items_per_wg; ++k) {
@@ -439,6 +440,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
   const PrimeConst& pc = a.ip.prime[i];
   const int log_n = LOGN ? LOGN : a.ip.log_n;
   ip_stage_twiddles<LOGB>(twl, a.ip.tw + ((uint64_t)i << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  __syncthreads();  // every wave reads the twiddles every thread staged
   for (int k = 0; k < a.ip.items_per_wg; ++k) {
     GridPos gp = g0;
     gp.item = g0.item * a.ip.items_per_wg + k;

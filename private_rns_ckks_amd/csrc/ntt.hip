@@ -76,7 +76,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_inv_kernel(Pa
   const int p = a.prime_idx[job];
   const PrimeConst& pc = a.prime[p];
   ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)p << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
-  __syncthreads();  // the first round reads the staged twiddles before any other barrier
+  __syncthreads();  // every wave reads the twiddles every thread staged
   for (int k = 0; k < items; ++k) {
     const int item = g0.item * items + k;
     if (item >= n_items) break;

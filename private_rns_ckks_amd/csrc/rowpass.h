@@ -27,6 +27,21 @@ struct IPRounds {
   static constexpr int THREADS = KC << (LOGB - 3);
 };
 
+// Work item k (k < 8 >> R) of the calling thread in a register round of R
+// stages at row bit pos.  Wave w takes the items of its own 2^(9-LOGB)
+// columns (KC columns over THREADS / 64 waves), consecutive lanes taking
+// consecutive items; for R = 3 this is the thread's column in every other
+// round too, so each wave touches only its own columns of the LDS tile in
+// every round of a pass, and the rounds need no workgroup barrier.
+template <int R, int LOGB>
+__device__ __forceinline__ void ip_item(int k, int pos, int& col, int& base) {
+  constexpr int NB = 1 << (LOGB - R);  // items per column
+  const int u = k * 64 + ((int)threadIdx.x & 63);
+  col = ((int)threadIdx.x >> 6) * (1 << (9 - LOGB)) + u / NB;
+  const int b = u % NB;
+  base = ((b >> pos) << (pos + R)) | (b & ((1 << pos) - 1));
+}
+
 // global word index (within the limb) of tile element (row, col)
 template <int LOGB>
 __device__ __forceinline__ uint32_t ip_word(uint32_t tile, int row, int col) {
@@ -91,7 +106,7 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
   int col[NI], base[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    item_coords<false, R, LOGB>(threadIdx.x + k * T, POS, col[k], base[k]);
+    ip_item<R, LOGB>(k, POS, col[k], base[k]);
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       const int row = base[k] + (i << POS);
@@ -115,15 +130,15 @@ template <int LOGB, int AR>
 __device__ __forceinline__ void ip_row_pass(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
                                             uint32_t tile, int log_n, uint64_t q) {
   typedef IPRounds<LOGB> G;
-  __syncthreads();  // every thread has read the tile's previous contents
+  wave_lds_wait();  // the wave has read its columns' previous contents
   if constexpr (G::R1 > 0) {
     ip_round<G::R1, LOGB - G::R1, LOGB, AR, true, true>(x, src, lds, twl, tile, log_n, q);
-    __syncthreads();
+    wave_lds_wait();
     ip_round<G::R2, G::R3, LOGB, AR, false, true>(x, src, lds, twl, tile, log_n, q);
   } else {
     ip_round<G::R2, G::R3, LOGB, AR, true, true>(x, src, lds, twl, tile, log_n, q);
   }
-  __syncthreads();
+  wave_lds_wait();
   ip_round<G::R3, 0, LOGB, AR, false, false>(x, src, lds, twl, tile, log_n, q);
 }
 
@@ -174,7 +189,7 @@ __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* d
   typedef IPRounds<LOGB> G;
   constexpr int T = G::THREADS;
   int col, base;
-  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  ip_item<3, LOGB>(0, 0, col, base);
   uint64_t x[8];
   {
     const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(src + ip_word<LOGB>(tile, base, col));
@@ -186,15 +201,15 @@ __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* d
     }
   }
   ip_inv_butterflies<3, LOGB, AR, 0>(x, base, 0, col, twl, q);
-  __syncthreads();  // every thread has read the tile's previous contents
+  wave_lds_wait();  // the wave has read its columns' previous contents
 #pragma unroll
   for (int i = 0; i < 8; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
-  __syncthreads();
+  wave_lds_wait();
   constexpr int N2 = 8 >> G::R2;
 #pragma unroll
   for (int k = 0; k < N2; ++k) {
     int c, b;
-    item_coords<false, G::R2, LOGB>(threadIdx.x + k * T, 3, c, b);
+    ip_item<G::R2, LOGB>(k, 3, c, b);
     uint64_t y[1 << G::R2];
 #pragma unroll
     for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
@@ -206,13 +221,13 @@ __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* d
     }
   }
   if constexpr (G::R1 > 0) {
-    __syncthreads();
+    wave_lds_wait();
     constexpr int N1 = 8 >> G::R1;
     constexpr int P1 = 3 + G::R2;
 #pragma unroll
     for (int k = 0; k < N1; ++k) {
       int c, b;
-      item_coords<false, G::R1, LOGB>(threadIdx.x + k * T, P1, c, b);
+      ip_item<G::R1, LOGB>(k, P1, c, b);
       uint64_t y[1 << G::R1];
 #pragma unroll
       for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
