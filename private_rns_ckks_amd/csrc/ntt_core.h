@@ -287,7 +287,13 @@ __device__ __forceinline__ void pass_body(const IO& io, uint64_t* lds, uint32_t 
 #pragma unroll
     for (int i = 0; i < (1 << R1); ++i) lds[lds_index<COLFAST, RB, ROWS>(base + (i << pos1), col)] = x[i];
   }
-  __syncthreads();
+  // A row pass whose two rounds have the same radix and use every thread
+  // keeps each thread on column tid / (ROWS >> R1) in both rounds, so the
+  // exchange stays inside the wave's own columns.
+  if constexpr (!COLFAST && R1 == R2 && kCols * (ROWS >> R1) == kThreads)
+    wave_lds_wait();
+  else
+    __syncthreads();
   if (tid < kCols * (ROWS >> R2)) {
     int col, base;
     item_coords<COLFAST, R2, LOGB>(tid, pos2, col, base);
