@@ -45,18 +45,6 @@ using namespace nttc;
 
 // ---------------------------------------------------------------------------
 // A: inverse row pass with optional automorphism gather
-struct GatherIO {
-  typedef NoOps Ops;
-  const uint64_t* src;
-  uint64_t* dst;
-  uint32_t g;
-  int log_n;
-  __device__ __forceinline__ uint64_t load(uint32_t j) const { return g ? src[automorph_src(j, g, log_n)] : src[j]; }
-  __device__ __forceinline__ void after_load(uint32_t, uint64_t) const {}
-  __device__ __forceinline__ Ops fetch(uint32_t) const { return Ops(); }
-  __device__ __forceinline__ void store(uint32_t j, uint64_t v, const Ops&) const { dst[j] = v; }
-};
-
 struct GatherArgs {
   const uint64_t* src;  // item b: src + b*src_bstride, limb i at + i*N
   uint64_t* dst;
@@ -67,22 +55,58 @@ struct GatherArgs {
   int log_n;
 };
 
-template <int RA, int RB, int LOGN>
-__global__ __launch_bounds__(kThreads) void intt_row_gather_kernel(GatherArgs a) {
-  constexpr int ROWS = 1 << (RA + RB);
-  __shared__ uint64_t lds[lds_words<false, RB, ROWS>()];
-  const GridPos gp = row_grid_pos();
-  const int limb = gp.job, item = gp.item;
-  const uint64_t off = (uint64_t)limb << a.log_n;
-  GatherIO io;
-  io.src = a.src + item * a.src_bstride + off;
-  io.dst = a.dst + item * a.dst_bstride + off;
-  io.g = a.g[item];
-  io.log_n = a.log_n;
+// A: the first pass (the row pass) of the inverse NTT of c1's limbs, read
+// through tau_g, for up to 8 batch items per workgroup that share the tile's
+// inverse twiddles staged in LDS (as the batched inverse NTT); the output
+// (below 4q) goes to the scaled inverse column pass.
+template <int LOGB, int LOGN>
+__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void intt_row_gather_kernel(GatherArgs a, int items,
+                                                                                 int n_items) {
+  typedef IPRounds<LOGB> G;
+  __shared__ uint64_t lds[(1 << LOGB) * G::KC];
+  __shared__ ulonglong2 twl[G::KC * ((1 << LOGB) - 1)];
+  const GridPos g0 = row_grid_pos();
+  const int limb = g0.job;
+  const int log_n = LOGN ? LOGN : a.log_n;
   const PrimeConst& pc = a.prime[limb];
-  Finish fin{0, 0, 0, pc.inv1};
-  run_pass<RA, RB, true, false, LOGN>(io, lds, gp.tile, a.log_n, a.tw + ((uint64_t)limb << (a.log_n + 1)), pc.q,
-                                      fin);
+  ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)limb << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  __syncthreads();  // every wave reads the twiddles every thread staged
+  const int iar = inv_ar(pc.q);
+  const uint64_t off = (uint64_t)limb << log_n;
+  for (int k = 0; k < items; ++k) {
+    const int item = g0.item * items + k;
+    if (item >= n_items) break;
+    const uint64_t* src = a.src + item * a.src_bstride + off;
+    uint64_t* dst = a.dst + item * a.dst_bstride + off;
+    const uint32_t g = a.g[item];
+    if (iar == AR_LAZY)
+      ip_inv_row_pass<LOGB, AR_LAZY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+    else if (iar == AR_HARVEY)
+      ip_inv_row_pass<LOGB, AR_HARVEY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+    else
+      ip_inv_row_pass<LOGB, AR_STRICT>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+  }
+}
+
+typedef void (*GatherFn)(GatherArgs, int, int);
+
+// Step A over n_items items of nq limbs.
+int launch_gather(Ctx* c, hipStream_t s, const GatherArgs& ga, int nq, int n_items) {
+  const int log_n = (int)c->log_n, logb = logb_row(log_n);
+  GatherFn fn = nullptr;
+  if (log_n == 16 && logb == 8) fn = intt_row_gather_kernel<8, 16>;
+  else if (logb == 5) fn = intt_row_gather_kernel<5, 0>;
+  else if (logb == 6) fn = intt_row_gather_kernel<6, 0>;
+  else if (logb == 7) fn = intt_row_gather_kernel<7, 0>;
+  else if (logb == 8) fn = intt_row_gather_kernel<8, 0>;
+  if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
+  const int items = std::max(1, std::min(8, n_items / 2));
+  const uint32_t tiles = c->N >> (ip_logkc(logb) + logb);
+  const int threads = (1 << ip_logkc(logb)) << (logb - 3);  // IPRounds<logb>::THREADS
+  TraceScope ts(c, s, "intt_row_gather", (double)n_items * nq * (c->N / 2) * logb);
+  hipLaunchKernelGGL(fn, dim3(tiles, nq, (n_items + items - 1) / items), dim3(threads), 0, s, ga, items, n_items);
+  CKKS_HIP_CHECK(hipGetLastError());
+  return CKKS_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -872,11 +896,7 @@ int ks_decompose(Ctx* c, hipStream_t s, int level, int n_in, const uint64_t* c1,
     ga.tw = c->d_tw_inv;
     ga.prime = c->d_prime;
     ga.log_n = log_n;
-    auto fn = CKKS_PICK_PASS(intt_row_gather_kernel, log_n, lr);
-    if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
-    TraceScope ts(c, s, "intt_row_gather", (double)n_in * nq * (N / 2) * lr);
-    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_in), dim3(kThreads), 0, s, ga);
-    CKKS_HIP_CHECK(hipGetLastError());
+    if ((rc = launch_gather(c, s, ga, nq, n_in))) return rc;
   }
   // inverse column pass, times [qhat_i^-1 N^-1]: the ModUp inputs y_i
   {
@@ -998,11 +1018,7 @@ int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* 
     ga.prime = c->d_prime;
     for (int i = 0; i < n_items; ++i) ga.g[i] = it[i].g;
     ga.log_n = log_n;
-    auto fn = CKKS_PICK_PASS(intt_row_gather_kernel, log_n, lr);
-    if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
-    TraceScope ts(c, s, "intt_row_gather", (double)n_items * nq * (N / 2) * lr);
-    hipLaunchKernelGGL(fn, dim3(pass_tiles(N, lr), nq, n_items), dim3(kThreads), 0, s, ga);
-    CKKS_HIP_CHECK(hipGetLastError());
+    if ((rc = launch_gather(c, s, ga, nq, n_items))) return rc;
   }
   if ((rc = modup_steps(c, s, level, n_items, Y, per, E, per))) return rc;
   RowIPArgs ip;

@@ -5,6 +5,7 @@
 // needs, KC * (2^LOGB - 1) Shoup pairs, are read from the table once per
 // workgroup instead of once per butterfly group and item.
 #pragma once
+#include "automorph.h"
 #include "ntt_core.h"
 
 namespace ckks {
@@ -179,20 +180,26 @@ __device__ __forceinline__ uint64_t inv_row_out(uint64_t v, uint64_t q, uint64_t
 
 // Inverse row pass of one limb on the tile: src holds canonical (or below
 // 4q) words, dst receives the pass's output for the column pass that follows
-// (below 4q: inv_row_out).  Rounds on
-// row bits 0-2 (8 consecutive words per thread, 16-byte loads), then 3.. and
+// (below 4q: inv_row_out); with g nonzero the input is read through tau_g.
+// Rounds on row bits 0-2 (8 consecutive words per thread, 16-byte loads, or
+// word by word through tau_g), then 3.. and
 // 6.. through the LDS tile; the last round's stores cover consecutive rows
 // across the wave.
 template <int LOGB, int AR>
 __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* dst, uint64_t* lds,
-                                                const ulonglong2* twl, uint32_t tile, uint64_t q, uint64_t inv1) {
+                                                const ulonglong2* twl, uint32_t tile, uint64_t q, uint64_t inv1,
+                                                uint32_t g = 0, int log_n = 0) {
   typedef IPRounds<LOGB> G;
   constexpr int T = G::THREADS;
   int col, base;
   ip_item<3, LOGB>(0, 0, col, base);
   uint64_t x[8];
-  {
-    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(src + ip_word<LOGB>(tile, base, col));
+  const uint32_t w0 = ip_word<LOGB>(tile, base, col);
+  if (g) {  // the input through tau_g (automorph.h): word j comes from word automorph_src(j, g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = src[automorph_src(w0 + i, g, log_n)];
+  } else {
+    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(src + w0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const ulonglong2 v = s2[i];
