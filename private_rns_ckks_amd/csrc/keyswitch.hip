@@ -175,21 +175,27 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
           x[2 * i + 1] = v.y;
         }
       }
-    } else {  // forward row pass of the converted limb; outputs stay lazy (< 70q, or < 8q)
-      const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
-      ip_row_pass<LOGB, AR>(x, src, lds, twl, tile, log_n, q);
     }
-    // one key component at a time: 16 registers of key words live, not 32
+    // one key component at a time: 16 registers of key words live, not 32;
+    // the first component's words load during the row pass's later rounds
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
-    {
-      ulonglong2 v[4];
+    ulonglong2 vb[4];
+    if (!in_digit) {  // forward row pass of the converted limb; outputs stay lazy (< 70q, or < 8q)
+      const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
+      ip_row_pass_first<LOGB, AR>(src, lds, twl, tile, log_n, q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = kb[i];
+      for (int i = 0; i < 4; ++i) vb[i] = kb[i];
+      ip_row_pass_rest<LOGB, AR>(x, lds, twl, tile, log_n, q);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[i] = kb[i];
+    }
+    {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        accb[2 * i] += mont_mul_lazy(x[2 * i], v[i].x, q, mp);
-        accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], v[i].y, q, mp);
+        accb[2 * i] += mont_mul_lazy(x[2 * i], vb[i].x, q, mp);
+        accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], vb[i].y, q, mp);
       }
     }
     {
@@ -406,9 +412,9 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
   const uint32_t ag = a.add_g[item];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    uint64_t x[8];
-    ip_row_pass<LOGB, AR>(x, a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds, twl,
-                            gp.tile, log_n, q);
+    // the additive terms load during the row pass's later rounds
+    ip_row_pass_first<LOGB, AR>(a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds,
+                                twl, gp.tile, log_n, q);
     uint64_t add[8], accum[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) add[r] = accum[r] = 0;
@@ -427,6 +433,8 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
         accum[2 * r + 1] = v.y;
       }
     }
+    uint64_t x[8];
+    ip_row_pass_rest<LOGB, AR>(x, lds, twl, gp.tile, log_n, q);
     ulonglong2* o = reinterpret_cast<ulonglong2*>(a.out + item * a.out_bstride +
                                                   ((uint64_t)(c * a.out_comp_limbs + i) << log_n) + w0);
     if (fast) {

@@ -125,22 +125,40 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
   }
 }
 
-// Forward row pass of one limb (src, lazy column-pass output) on the tile:
-// the thread ends with rows base..base+7 of its column in x[] (lazy).
+// Forward row pass of one limb (src, lazy column-pass output) on the tile,
+// in two calls: ip_row_pass_first reads the limb and runs the first register
+// round into the LDS tile; ip_row_pass_rest runs the other rounds and leaves
+// the thread rows base..base+7 of its column in x[] (lazy).  Loads issued
+// between the two calls (the key words of the inner product) are in flight
+// during the other rounds without holding up the first round's wait for its
+// own loads.
+template <int LOGB, int AR>
+__device__ __forceinline__ void ip_row_pass_first(const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
+                                                  uint32_t tile, int log_n, uint64_t q) {
+  typedef IPRounds<LOGB> G;
+  uint64_t unused[8];
+  wave_lds_wait();  // the wave has read its columns' previous contents
+  if constexpr (G::R1 > 0)
+    ip_round<G::R1, LOGB - G::R1, LOGB, AR, true, true>(unused, src, lds, twl, tile, log_n, q);
+  else
+    ip_round<G::R2, G::R3, LOGB, AR, true, true>(unused, src, lds, twl, tile, log_n, q);
+}
+template <int LOGB, int AR>
+__device__ __forceinline__ void ip_row_pass_rest(uint64_t (&x)[8], uint64_t* lds, const ulonglong2* twl,
+                                                 uint32_t tile, int log_n, uint64_t q) {
+  typedef IPRounds<LOGB> G;
+  if constexpr (G::R1 > 0) {
+    wave_lds_wait();
+    ip_round<G::R2, G::R3, LOGB, AR, false, true>(x, nullptr, lds, twl, tile, log_n, q);
+  }
+  wave_lds_wait();
+  ip_round<G::R3, 0, LOGB, AR, false, false>(x, nullptr, lds, twl, tile, log_n, q);
+}
 template <int LOGB, int AR>
 __device__ __forceinline__ void ip_row_pass(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
                                             uint32_t tile, int log_n, uint64_t q) {
-  typedef IPRounds<LOGB> G;
-  wave_lds_wait();  // the wave has read its columns' previous contents
-  if constexpr (G::R1 > 0) {
-    ip_round<G::R1, LOGB - G::R1, LOGB, AR, true, true>(x, src, lds, twl, tile, log_n, q);
-    wave_lds_wait();
-    ip_round<G::R2, G::R3, LOGB, AR, false, true>(x, src, lds, twl, tile, log_n, q);
-  } else {
-    ip_round<G::R2, G::R3, LOGB, AR, true, true>(x, src, lds, twl, tile, log_n, q);
-  }
-  wave_lds_wait();
-  ip_round<G::R3, 0, LOGB, AR, false, false>(x, src, lds, twl, tile, log_n, q);
+  ip_row_pass_first<LOGB, AR>(src, lds, twl, tile, log_n, q);
+  ip_row_pass_rest<LOGB, AR>(x, lds, twl, tile, log_n, q);
 }
 
 // R inverse (Gentleman-Sande) stages on the 2^R words of one item (rows
