@@ -150,7 +150,7 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
   const uint64_t q = pc.q, mp = pc.mprime;
   const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
   int col, base;
-  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  ip_item<3, LOGB>(0, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
 #pragma unroll
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
   ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)keyl << (log_n + 1)), g0.tile, s0);
   __syncthreads();  // every wave reads the twiddles every thread staged
   int col, base;
-  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  ip_item<3, LOGB>(0, 0, col, base);
   for (int k = 0; k < a.items_per_wg; ++k) {
     GridPos gp = g0;
     gp.item = g0.item * a.items_per_wg + k;
@@ -407,7 +407,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
       if (!fast) acc[c][r] = reduce_4q(acc[c][r], q);
     }
   int col, base;
-  item_coords<false, 3, LOGB>(threadIdx.x, 0, col, base);
+  ip_item<3, LOGB>(0, 0, col, base);
   const uint32_t w0 = ip_word<LOGB>(gp.tile, base, col);
   const uint32_t ag = a.add_g[item];
 #pragma unroll

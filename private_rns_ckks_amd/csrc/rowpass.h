@@ -1,9 +1,12 @@
 // Row passes with the tile's twiddles staged in LDS, for kernels that run the
 // row pass of several limbs or items on one tile: the key-switch inner
-// products (a forward row pass per digit) and the batched inverse NTT's row
-// pass (one per item of the workgroup).  The twiddles a tile of KC columns
-// needs, KC * (2^LOGB - 1) Shoup pairs, are read from the table once per
-// workgroup instead of once per butterfly group and item.
+// products (a forward row pass per digit), the batched inverse NTT's row pass
+// and the key switch's first inverse pass of c1 (one per item of the
+// workgroup).  The twiddles a tile of KC columns needs, KC * (2^LOGB - 1)
+// Shoup pairs, are read from the table once per workgroup instead of once per
+// butterfly group and item.  Every wave works on its own columns of the tile
+// in every round (ip_item), so only the twiddle staging needs a workgroup
+// barrier.
 #pragma once
 #include "automorph.h"
 #include "ntt_core.h"
@@ -153,12 +156,6 @@ __device__ __forceinline__ void ip_row_pass_rest(uint64_t (&x)[8], uint64_t* lds
   }
   wave_lds_wait();
   ip_round<G::R3, 0, LOGB, AR, false, false>(x, nullptr, lds, twl, tile, log_n, q);
-}
-template <int LOGB, int AR>
-__device__ __forceinline__ void ip_row_pass(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
-                                            uint32_t tile, int log_n, uint64_t q) {
-  ip_row_pass_first<LOGB, AR>(src, lds, twl, tile, log_n, q);
-  ip_row_pass_rest<LOGB, AR>(x, lds, twl, tile, log_n, q);
 }
 
 // R inverse (Gentleman-Sande) stages on the 2^R words of one item (rows
