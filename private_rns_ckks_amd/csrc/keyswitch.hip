@@ -139,37 +139,37 @@ struct RowIPArgs {
 // converted limb E[j][t] or, for t inside digit j, the NTT-form input limb
 // (through tau_g when rotating).  Sums of Montgomery products, reduced every
 // mont_fold(m) digits (below 9m); the factor 2^-64 is left in them.
-template <int LOGB, int LOGN, int AR>
+template <int LOGB, int LOGN, int AR, int W = 8>
 __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds, const ulonglong2* twl,
-                                              const PrimeConst& pc, int keyl, const GridPos& gp, uint64_t (&accb)[8],
-                                              uint64_t (&acca)[8]) {
-  typedef IPRounds<LOGB> G;
+                                              const PrimeConst& pc, int keyl, const GridPos& gp, uint64_t (&accb)[W],
+                                              uint64_t (&acca)[W]) {
+  constexpr int H = W / 2;  // 16-byte words per thread
   const int log_n = LOGN ? LOGN : a.log_n;
   const int t = gp.job + a.t0, item = gp.item;
   const uint32_t tile = gp.tile;
   const uint64_t q = pc.q, mp = pc.mprime;
   const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
   int col, base;
-  ip_item<3, LOGB>(0, 0, col, base);
-  const uint32_t w0 = ip_word<LOGB>(tile, base, col);
+  ip_item<IPRounds<LOGB, W>::RW, LOGB, W>(0, 0, col, base);
+  const uint32_t w0 = ip_word<LOGB, W>(tile, base, col);
   const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accb[i] = acca[i] = 0;
+  for (int i = 0; i < W; ++i) accb[i] = acca[i] = 0;
   const int fold = mont_fold(q);
   int since = 0;
   for (int j = 0; j < a.beta; ++j) {
     const bool in_digit = t >= j * a.alpha && t < (j + 1) * a.alpha && t <= a.level;
-    uint64_t x[8];
+    uint64_t x[W];
     if (in_digit) {  // NTT-form input limb, in [0, q); a rotation gathers tau_g of it here
       const uint64_t* limb = a.T + item * a.T_bstride + ((uint64_t)t << log_n);
       const uint32_t g = a.g[item];
       if (g) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = limb[automorph_src(w0 + i, g, log_n)];
+        for (int i = 0; i < W; ++i) x[i] = limb[automorph_src(w0 + i, g, log_n)];
       } else {
         const ulonglong2* src = reinterpret_cast<const ulonglong2*>(limb + w0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < H; ++i) {
           const ulonglong2 v = src[i];
           x[2 * i] = v.x;
           x[2 * i + 1] = v.y;
@@ -180,30 +180,30 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
     // the first component's words load during the row pass's later rounds
     const ulonglong2* kb = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j) * LKN);
     const ulonglong2* ka = reinterpret_cast<const ulonglong2*>(evk + (uint64_t)(2 * j + 1) * LKN);
-    ulonglong2 vb[4];
+    ulonglong2 vb[H];
     if (!in_digit) {  // forward row pass of the converted limb; outputs stay lazy (< 70q, or < 8q)
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
-      ip_row_pass_first<LOGB, AR>(src, lds, twl, tile, log_n, q);
+      ip_row_pass_first<LOGB, AR, W>(src, lds, twl, tile, log_n, q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = kb[i];
-      ip_row_pass_rest<LOGB, AR>(x, lds, twl, tile, log_n, q);
+      for (int i = 0; i < H; ++i) vb[i] = kb[i];
+      ip_row_pass_rest<LOGB, AR, W>(x, lds, twl, tile, log_n, q);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = kb[i];
+      for (int i = 0; i < H; ++i) vb[i] = kb[i];
     }
     {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < H; ++i) {
         accb[2 * i] += mont_mul_lazy(x[2 * i], vb[i].x, q, mp);
         accb[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], vb[i].y, q, mp);
       }
     }
     {
-      ulonglong2 v[4];
+      ulonglong2 v[H];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = ka[i];
+      for (int i = 0; i < H; ++i) v[i] = ka[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < H; ++i) {
         acca[2 * i] += mont_mul_lazy(x[2 * i], v[i].x, q, mp);
         acca[2 * i + 1] += mont_mul_lazy(x[2 * i + 1], v[i].y, q, mp);
       }
@@ -211,7 +211,7 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
     if (++since == fold) {
       since = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < W; ++i) {
         accb[i] = reduce64(accb[i], q, pc.inv1);
         acca[i] = reduce64(acca[i], q, pc.inv1);
       }
@@ -224,76 +224,62 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
 // on the same tile by the first pass of their inverse NTT (the row pass); the
 // inverse column pass (scaled for ModDown) completes it.
 //
-// The inverse row pass of one component: the thread's 8 words (rows
-// base..base+7 of its column, below 4q, below 2q for AR_STRICT) go through the Gentleman-Sande stages
-// of row bits 0-2 in registers, then of row bits 3.. and 6.. through the LDS
-// tile, and are stored below 4q for the column pass (inv_row_out).
-template <int LOGB, int AR>
-__device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[8], uint64_t* lds, uint32_t tile, int log_n,
+// The inverse row pass of one component: the thread's W words (rows
+// base..base+W-1 of its column, below 4q, below 2q for AR_STRICT) go through
+// the Gentleman-Sande stages of the low row bits in registers, then of the
+// higher row bits in rounds through the LDS tile (the rounds of the forward
+// pass in reverse order), and are stored below 4q for the column pass
+// (inv_row_out).  Twiddles come from the inverse table in global memory.
+template <int LOGB, int AR, int W, int POS>
+__device__ __forceinline__ void ip_inv_rounds_up(uint64_t* lds, uint32_t tile, int log_n, uint32_t s0,
+                                                 const uint64_t* twi, uint64_t q, uint64_t inv1, uint64_t* dst) {
+  typedef IPRounds<LOGB, W> G;
+  constexpr bool LAST = POS + G::RW >= LOGB;
+  constexpr int R = LAST ? LOGB - POS : G::RW;
+#pragma unroll
+  for (int k = 0; k < (W >> R); ++k) {
+    int c, b;
+    ip_item<R, LOGB, W>(k, POS, c, b);
+    uint64_t y[1 << R];
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << POS), c)];
+    const uint32_t blk = tile * G::KC + c;
+    round_regs<R, true, AR, false, false, POS>(y, b, POS, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) {
+      if constexpr (LAST) dst[ip_word<LOGB, W>(tile, b + (i << POS), c)] = inv_row_out<AR>(y[i], q, inv1);
+      else lds[ip_lds<LOGB>(b + (i << POS), c)] = y[i];
+    }
+  }
+  if constexpr (!LAST) {
+    wave_lds_wait();
+    ip_inv_rounds_up<LOGB, AR, W, POS + R>(lds, tile, log_n, s0, twi, q, inv1, dst);
+  }
+}
+template <int LOGB, int AR, int W>
+__device__ __forceinline__ void ip_inverse_row_store(uint64_t (&x)[W], uint64_t* lds, uint32_t tile, int log_n,
                                                      const uint64_t* twi, uint64_t q, uint64_t inv1, uint64_t* dst) {
-  typedef IPRounds<LOGB> G;
-  constexpr int T = G::THREADS;
+  typedef IPRounds<LOGB, W> G;
   const uint32_t s0 = (uint32_t)logb_col(log_n);
   int col, base;
-  ip_item<3, LOGB>(0, 0, col, base);
+  ip_item<G::RW, LOGB, W>(0, 0, col, base);
   {
     const uint32_t blk = tile * G::KC + col;
-    round_regs<3, true, AR, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
+    round_regs<G::RW, true, AR, false, false, 0>(x, base, 0, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
   }
   wave_lds_wait();  // the wave has read its columns' previous contents
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
+  for (int i = 0; i < W; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
   wave_lds_wait();
-  // row bits [3, 3 + R2)
-  constexpr int N2 = 8 >> G::R2;
-#pragma unroll
-  for (int k = 0; k < N2; ++k) {
-    int c, b;
-    ip_item<G::R2, LOGB>(k, 3, c, b);
-    uint64_t y[1 << G::R2];
-#pragma unroll
-    for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
-    const uint32_t blk = tile * G::KC + c;
-    round_regs<G::R2, true, AR, false, false, 3>(y, b, 3, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
-    if constexpr (G::R1 == 0) {
-#pragma unroll
-      for (int i = 0; i < (1 << G::R2); ++i) {
-        const uint64_t v = inv_row_out<AR>(y[i], q, inv1);
-        dst[ip_word<LOGB>(tile, b + (i << 3), c)] = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < (1 << G::R2); ++i) lds[ip_lds<LOGB>(b + (i << 3), c)] = y[i];
-    }
-  }
-  if constexpr (G::R1 > 0) {
-    wave_lds_wait();
-    constexpr int N1 = 8 >> G::R1;
-    constexpr int P1 = 3 + G::R2;
-#pragma unroll
-    for (int k = 0; k < N1; ++k) {
-      int c, b;
-      ip_item<G::R1, LOGB>(k, P1, c, b);
-      uint64_t y[1 << G::R1];
-#pragma unroll
-      for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
-      const uint32_t blk = tile * G::KC + c;
-      round_regs<G::R1, true, AR, false, false, P1>(y, b, P1, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
-#pragma unroll
-      for (int i = 0; i < (1 << G::R1); ++i) {
-        const uint64_t v = inv_row_out<AR>(y[i], q, inv1);
-        dst[ip_word<LOGB>(tile, b + (i << P1), c)] = v;
-      }
-    }
-  }
+  ip_inv_rounds_up<LOGB, AR, W, G::RW>(lds, tile, log_n, s0, twi, q, inv1, dst);
 }
 
 // acc: item b at acc + b*acc_bstride, [2][K][N] (special limbs only).
-template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void ip_special_kernel(
+template <int LOGB, int LOGN, int W = 8>
+__global__ __launch_bounds__((IPRounds<LOGB, W>::THREADS)) __attribute__((amdgpu_waves_per_eu(W == 8 ? 2 : (LOGN ? 4 : 3)))) void ip_special_kernel(
     RowIPArgs a, const uint64_t* twi) {
-  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
-  __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
+  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB, W>::KC];
+  __shared__ ulonglong2 twl[IPRounds<LOGB, W>::KC * ((1 << LOGB) - 1)];
   const GridPos g0 = a.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
   const int t = g0.job + a.t0;  // a special limb
   const int keyl = a.L + (t - a.level - 1);
@@ -301,34 +287,32 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
   const int log_n = LOGN ? LOGN : a.log_n;
   const uint32_t s0 = (uint32_t)logb_col(log_n);
   const uint64_t* tw_i = twi + ((uint64_t)keyl << (log_n + 1));
-  ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)keyl << (log_n + 1)), g0.tile, s0);
+  ip_stage_twiddles<LOGB, W>(twl, a.tw + ((uint64_t)keyl << (log_n + 1)), g0.tile, s0);
   __syncthreads();  // every wave reads the twiddles every thread staged
-  int col, base;
-  ip_item<3, LOGB>(0, 0, col, base);
   for (int k = 0; k < a.items_per_wg; ++k) {
     GridPos gp = g0;
     gp.item = g0.item * a.items_per_wg + k;
     if (gp.item >= a.n_items) break;
-    uint64_t accb[8], acca[8];
+    uint64_t accb[W], acca[W];
     const int far = fwd_ar(pc.q);
     if (far == AR_LAZY)
-      ip_accumulate<LOGB, LOGN, AR_LAZY>(a, lds, twl, pc, keyl, gp, accb, acca);
+      ip_accumulate<LOGB, LOGN, AR_LAZY, W>(a, lds, twl, pc, keyl, gp, accb, acca);
     else if (far == AR_HARVEY)
-      ip_accumulate<LOGB, LOGN, AR_HARVEY>(a, lds, twl, pc, keyl, gp, accb, acca);
+      ip_accumulate<LOGB, LOGN, AR_HARVEY, W>(a, lds, twl, pc, keyl, gp, accb, acca);
     else
-      ip_accumulate<LOGB, LOGN, AR_STRICT>(a, lds, twl, pc, keyl, gp, accb, acca);
+      ip_accumulate<LOGB, LOGN, AR_STRICT, W>(a, lds, twl, pc, keyl, gp, accb, acca);
     // remove the 2^-64: [0, 4q), the range the lazy and Harvey inverse
     // butterflies take; the exact-quotient ones take [0, 2q)
     const int iar = inv_ar(pc.q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < W; ++i) {
       accb[i] = mul_shoup_lazy(accb[i], pc.r64, pc.r64p, pc.q);
       acca[i] = mul_shoup_lazy(acca[i], pc.r64, pc.r64p, pc.q);
     }
     if (iar == AR_STRICT) {
       const uint64_t two_q = 2 * pc.q;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < W; ++i) {
         accb[i] = accb[i] >= two_q ? accb[i] - two_q : accb[i];
         acca[i] = acca[i] >= two_q ? acca[i] - two_q : acca[i];
       }
@@ -336,27 +320,32 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     uint64_t* ob = a.acc + gp.item * a.acc_bstride + ((uint64_t)(t - a.level - 1) << log_n);
     uint64_t* oa = ob + ((uint64_t)a.K << log_n);
     if (iar == AR_LAZY) {
-      ip_inverse_row_store<LOGB, AR_LAZY>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
-      ip_inverse_row_store<LOGB, AR_LAZY>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+      ip_inverse_row_store<LOGB, AR_LAZY, W>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_LAZY, W>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
     } else if (iar == AR_HARVEY) {
-      ip_inverse_row_store<LOGB, AR_HARVEY>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
-      ip_inverse_row_store<LOGB, AR_HARVEY>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+      ip_inverse_row_store<LOGB, AR_HARVEY, W>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_HARVEY, W>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
     } else {
-      ip_inverse_row_store<LOGB, AR_STRICT>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
-      ip_inverse_row_store<LOGB, AR_STRICT>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
+      ip_inverse_row_store<LOGB, AR_STRICT, W>(accb, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, ob);
+      ip_inverse_row_store<LOGB, AR_STRICT, W>(acca, lds, gp.tile, log_n, tw_i, pc.q, pc.inv1, oa);
     }
   }
 }
 
 typedef void (*IPSpecialFn)(RowIPArgs, const uint64_t*);
 
+// Words per thread of the special-limb inner product (IPRounds): 8 measured
+// faster than 4 here (the extra inverse round and its twiddle loads cost more
+// than the added waves gain).
+constexpr int kSpecialW = 8;
+
 IPSpecialFn pick_ip_special(int log_n, int logb) {
-  if (log_n == 16 && logb == 8) return ip_special_kernel<8, 16>;
+  if (log_n == 16 && logb == 8) return ip_special_kernel<8, 16, kSpecialW>;
   switch (logb) {
-    case 5: return ip_special_kernel<5, 0>;
-    case 6: return ip_special_kernel<6, 0>;
-    case 7: return ip_special_kernel<7, 0>;
-    case 8: return ip_special_kernel<8, 0>;
+    case 5: return ip_special_kernel<5, 0, kSpecialW>;
+    case 6: return ip_special_kernel<6, 0, kSpecialW>;
+    case 7: return ip_special_kernel<7, 0, kSpecialW>;
+    case 8: return ip_special_kernel<8, 0, kSpecialW>;
   }
   return nullptr;
 }
@@ -385,14 +374,15 @@ struct CombIPArgs {
   const uint64_t* pinv64;  // [L][2]: {[2^64 P^-1]_{q_i}, Shoup}
 };
 
-template <int LOGB, int LOGN, int AR>
+template <int LOGB, int LOGN, int AR, int W>
 __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds, const ulonglong2* twl,
                                              const PrimeConst& pc, int i, const GridPos& gp) {
+  constexpr int H = W / 2;
   const int log_n = LOGN ? LOGN : a.ip.log_n;
   const int item = gp.item;
   const uint64_t q = pc.q;
-  uint64_t acc[2][8];
-  ip_accumulate<LOGB, LOGN, AR>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
+  uint64_t acc[2][W];
+  ip_accumulate<LOGB, LOGN, AR, W>(a.ip, lds, twl, pc, i, gp, acc[0], acc[1]);
   const uint64_t cw = a.pinv64[2 * i], cwp = a.pinv64[2 * i + 1];
   // Lazy primes in (2^33, 2^56): the row pass leaves NTT(w) below 65q < 2^63,
   // which reduce_hi takes to [0, 2q); with acc*P^-1 in [0, 4q) and canonical
@@ -402,46 +392,46 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < W; ++r) {
       acc[c][r] = mul_shoup_lazy(acc[c][r], cw, cwp, q);
       if (!fast) acc[c][r] = reduce_4q(acc[c][r], q);
     }
   int col, base;
-  ip_item<3, LOGB>(0, 0, col, base);
-  const uint32_t w0 = ip_word<LOGB>(gp.tile, base, col);
+  ip_item<IPRounds<LOGB, W>::RW, LOGB, W>(0, 0, col, base);
+  const uint32_t w0 = ip_word<LOGB, W>(gp.tile, base, col);
   const uint32_t ag = a.add_g[item];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     // the additive terms load during the row pass's later rounds
-    ip_row_pass_first<LOGB, AR>(a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds,
-                                twl, gp.tile, log_n, q);
-    uint64_t add[8], accum[8];
+    ip_row_pass_first<LOGB, AR, W>(a.W + item * a.W_bstride + ((uint64_t)(c * a.ip.level + c + i) << log_n), lds,
+                                   twl, gp.tile, log_n, q);
+    uint64_t add[W], accum[W];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) add[r] = accum[r] = 0;
+    for (int r = 0; r < W; ++r) add[r] = accum[r] = 0;
     if (a.add[c]) {
       const uint64_t* ad = a.add[c] + item * a.add_bstride + ((uint64_t)i << log_n);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) add[r] = ad[ag ? automorph_src(w0 + r, ag, log_n) : w0 + r];
+      for (int r = 0; r < W; ++r) add[r] = ad[ag ? automorph_src(w0 + r, ag, log_n) : w0 + r];
     }
     if (a.accum) {
       const ulonglong2* ac =
           reinterpret_cast<const ulonglong2*>(a.accum + item * a.accum_bstride + ((uint64_t)(c * (a.ip.level + 1) + i) << log_n) + w0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < H; ++r) {
         const ulonglong2 v = ac[r];
         accum[2 * r] = v.x;
         accum[2 * r + 1] = v.y;
       }
     }
-    uint64_t x[8];
-    ip_row_pass_rest<LOGB, AR>(x, lds, twl, gp.tile, log_n, q);
+    uint64_t x[W];
+    ip_row_pass_rest<LOGB, AR, W>(x, lds, twl, gp.tile, log_n, q);
     ulonglong2* o = reinterpret_cast<ulonglong2*>(a.out + item * a.out_bstride +
                                                   ((uint64_t)(c * a.out_comp_limbs + i) << log_n) + w0);
     if (fast) {
       const uint64_t two_q = 2 * q, four_q = 4 * q;
       const uint32_t m = (uint32_t)pc.inv1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < H; ++r) {
         uint64_t e0 = acc[c][2 * r] + two_q - reduce_hi(x[2 * r], q, m) + add[2 * r] + accum[2 * r];
         uint64_t e1 = acc[c][2 * r + 1] + two_q - reduce_hi(x[2 * r + 1], q, m) + add[2 * r + 1] + accum[2 * r + 1];
         e0 = reduce_4q(e0 >= four_q ? e0 - four_q : e0, q);
@@ -450,7 +440,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < H; ++r) {
         ulonglong2 v;
         uint64_t e0 = sub_mod(acc[c][2 * r], reduce64(x[2 * r], q, pc.inv1), q);
         uint64_t e1 = sub_mod(acc[c][2 * r + 1], reduce64(x[2 * r + 1], q, pc.inv1), q);
@@ -462,16 +452,16 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
   }
 }
 
-template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void comb_ip_kernel(
+template <int LOGB, int LOGN, int W = 8>
+__global__ __launch_bounds__((IPRounds<LOGB, W>::THREADS)) __attribute__((amdgpu_waves_per_eu(W == 8 ? 2 : (LOGN ? 4 : 3)))) void comb_ip_kernel(
     CombIPArgs a) {
-  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB>::KC];
-  __shared__ ulonglong2 twl[IPRounds<LOGB>::KC * ((1 << LOGB) - 1)];
+  __shared__ uint64_t lds[(1 << LOGB) * IPRounds<LOGB, W>::KC];
+  __shared__ ulonglong2 twl[IPRounds<LOGB, W>::KC * ((1 << LOGB) - 1)];
   const GridPos g0 = a.ip.shared_key ? row_grid_pos<true>() : row_grid_pos<false>();
   const int i = g0.job;  // a ciphertext limb
   const PrimeConst& pc = a.ip.prime[i];
   const int log_n = LOGN ? LOGN : a.ip.log_n;
-  ip_stage_twiddles<LOGB>(twl, a.ip.tw + ((uint64_t)i << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  ip_stage_twiddles<LOGB, W>(twl, a.ip.tw + ((uint64_t)i << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
   __syncthreads();  // every wave reads the twiddles every thread staged
   for (int k = 0; k < a.ip.items_per_wg; ++k) {
     GridPos gp = g0;
@@ -479,23 +469,27 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) __attribute__((amdgpu_wave
     if (gp.item >= a.ip.n_items) break;
     const int far = fwd_ar(pc.q);
     if (far == AR_LAZY)
-      comb_ip_body<LOGB, LOGN, AR_LAZY>(a, lds, twl, pc, i, gp);
+      comb_ip_body<LOGB, LOGN, AR_LAZY, W>(a, lds, twl, pc, i, gp);
     else if (far == AR_HARVEY)
-      comb_ip_body<LOGB, LOGN, AR_HARVEY>(a, lds, twl, pc, i, gp);
+      comb_ip_body<LOGB, LOGN, AR_HARVEY, W>(a, lds, twl, pc, i, gp);
     else
-      comb_ip_body<LOGB, LOGN, AR_STRICT>(a, lds, twl, pc, i, gp);
+      comb_ip_body<LOGB, LOGN, AR_STRICT, W>(a, lds, twl, pc, i, gp);
   }
 }
 
 typedef void (*CombIPFn)(CombIPArgs);
 
+// Words per thread of the combining kernel (IPRounds): 4, at 4 waves per
+// SIMD for N = 2^16, measured faster than 8 at 2 waves.
+constexpr int kCombW = 4;
+
 CombIPFn pick_comb_ip(int log_n, int logb) {
-  if (log_n == 16 && logb == 8) return comb_ip_kernel<8, 16>;
+  if (log_n == 16 && logb == 8) return comb_ip_kernel<8, 16, kCombW>;
   switch (logb) {
-    case 5: return comb_ip_kernel<5, 0>;
-    case 6: return comb_ip_kernel<6, 0>;
-    case 7: return comb_ip_kernel<7, 0>;
-    case 8: return comb_ip_kernel<8, 0>;
+    case 5: return comb_ip_kernel<5, 0, kCombW>;
+    case 6: return comb_ip_kernel<6, 0, kCombW>;
+    case 7: return comb_ip_kernel<7, 0, kCombW>;
+    case 8: return comb_ip_kernel<8, 0, kCombW>;
   }
   return nullptr;
 }
@@ -1051,8 +1045,6 @@ int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* 
   ip.L = (int)c->L;
   ip.K = K;
   ip.n_items = n_items;
-  const int logkc = ip_logkc(lr);
-  const dim3 block(1u << (lr - 3 + logkc));
   {
     RowIPArgs sp = ip;
     sp.acc = A;
@@ -1063,7 +1055,9 @@ int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* 
     if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
     const double units = (double)K * ((double)beta * (N / 2) * lr + N * (2.0 * beta + 2) + 2.0 * (N / 2) * lr);
     TraceScope ts(c, s, "ip_special", units * n_items);
-    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), K, (n_items + 1) / 2), block, 0, s, sp, c->d_tw_inv);
+    const int logkc = ip_logkc(lr, kSpecialW);
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), K, (n_items + 1) / 2), dim3((1u << (lr + logkc)) / kSpecialW), 0, s,
+                       sp, c->d_tw_inv);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   if ((rc = moddown_steps(c, s, level, n_items, A, per, W, per))) return rc;
@@ -1094,7 +1088,9 @@ int ks_chunk_fused(Ctx* c, hipStream_t s, int level, int n_items, const KSItem* 
     }
     units += (double)nq * (N * (2.0 * beta + 2) + 2.0 * ((N / 2) * lr + N));
     TraceScope ts(c, s, "comb_ip", units * n_items);
-    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), nq, (n_items + 1) / 2), block, 0, s, ca);
+    const int logkc = ip_logkc(lr, kCombW);
+    hipLaunchKernelGGL(fn, dim3(N >> (lr + logkc), nq, (n_items + 1) / 2), dim3((1u << (lr + logkc)) / kCombW), 0,
+                       s, ca);
     CKKS_HIP_CHECK(hipGetLastError());
   }
   return CKKS_OK;

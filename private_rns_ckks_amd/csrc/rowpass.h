@@ -14,42 +14,50 @@
 namespace ckks {
 namespace nttc {
 
-// A workgroup's tile is KC columns of 2^LOGB rows (8 columns from 2^7 rows
-// on, so several workgroups share a CU).  The row pass's LOGB stages run as
-// register rounds of at most 3 stages, the last of exactly 3, so every thread
-// holds 8 words in every round and ends with 8 consecutive words of one
-// column: the layout the multiply phase reads the key digits in.
-__host__ __device__ constexpr int ip_logkc(int logb) { return logb >= 7 ? 3 : 4; }
+// A workgroup's tile is KC columns of 2^LOGB rows.  Every thread holds W
+// words (8, or 4 for more waves per SIMD at half the registers) in every
+// register round and ends the forward pass with W consecutive words of one
+// column: the layout the multiply phase reads the key digits in.  The LOGB
+// stages run as rounds of log2(W) stages, the first round taking what is
+// left (W = 8 at 2^8 rows: 2, 3, 3; W = 4: 2, 2, 2, 2).  KC is 8 (W = 8) or 4
+// (W = 4) from 2^7 rows on, twice that below, so that several workgroups
+// share a CU.
+__host__ __device__ constexpr int ip_logkc(int logb, int w = 8) { return (logb >= 7 ? 3 : 4) - (w == 4 ? 1 : 0); }
 
-template <int LOGB>
+template <int LOGB, int W = 8>
 struct IPRounds {
-  static constexpr int R3 = 3;
-  static constexpr int R2 = LOGB >= 6 ? 3 : LOGB - 3;
-  static constexpr int R1 = LOGB - R2 - R3;  // 0 when two rounds suffice
-  static constexpr int LOGKC = ip_logkc(LOGB);
+  static_assert(W == 8 || W == 4, "words per thread");
+  static constexpr int RW = W == 8 ? 3 : 2;                    // stages per full round
+  static constexpr int NR = (LOGB + RW - 1) / RW;              // rounds
+  static constexpr int R0 = LOGB - RW * (NR - 1);              // stages of the first round
+  static constexpr int R3 = 3;                                 // W = 8 names: the last round,
+  static constexpr int R2 = LOGB >= 6 ? 3 : LOGB - 3;          // the one before it,
+  static constexpr int R1 = LOGB - R2 - R3;                    // the first (0 when two suffice)
+  static constexpr int LOGKC = ip_logkc(LOGB, W);
   static constexpr int KC = 1 << LOGKC;
-  static constexpr int THREADS = KC << (LOGB - 3);
+  static constexpr int THREADS = (KC << LOGB) / W;
+  static constexpr int CPW = (64 * W) >> LOGB;                 // columns per wave
 };
 
-// Work item k (k < 8 >> R) of the calling thread in a register round of R
-// stages at row bit pos.  Wave w takes the items of its own 2^(9-LOGB)
-// columns (KC columns over THREADS / 64 waves), consecutive lanes taking
-// consecutive items; for R = 3 this is the thread's column in every other
-// round too, so each wave touches only its own columns of the LDS tile in
-// every round of a pass, and the rounds need no workgroup barrier.
-template <int R, int LOGB>
+// Work item k (k < W >> R) of the calling thread in a register round of R
+// stages at row bit pos.  Wave w takes the items of its own CPW columns
+// (KC columns over THREADS / 64 waves), consecutive lanes taking consecutive
+// items; for R = log2(W) this is the thread's column in every other round
+// too, so each wave touches only its own columns of the LDS tile in every
+// round of a pass, and the rounds need no workgroup barrier.
+template <int R, int LOGB, int W = 8>
 __device__ __forceinline__ void ip_item(int k, int pos, int& col, int& base) {
   constexpr int NB = 1 << (LOGB - R);  // items per column
   const int u = k * 64 + ((int)threadIdx.x & 63);
-  col = ((int)threadIdx.x >> 6) * (1 << (9 - LOGB)) + u / NB;
+  col = ((int)threadIdx.x >> 6) * IPRounds<LOGB, W>::CPW + u / NB;
   const int b = u % NB;
   base = ((b >> pos) << (pos + R)) | (b & ((1 << pos) - 1));
 }
 
 // global word index (within the limb) of tile element (row, col)
-template <int LOGB>
+template <int LOGB, int W = 8>
 __device__ __forceinline__ uint32_t ip_word(uint32_t tile, int row, int col) {
-  return ((tile * IPRounds<LOGB>::KC + col) << LOGB) + row;
+  return ((tile * IPRounds<LOGB, W>::KC + col) << LOGB) + row;
 }
 
 // LDS position of row-pass tile element (row, col): column-major, with row
@@ -65,9 +73,9 @@ __device__ __forceinline__ int ip_lds(int row, int col) {
 // used by every digit: relative stage d (global stage s0 + d) of column col
 // needs entries col * 2^d .. col * 2^d + 2^d - 1 of a run of KC * 2^d
 // consecutive table entries, stored from LDS entry KC * (2^d - 1) on.
-template <int LOGB>
+template <int LOGB, int W = 8>
 __device__ __forceinline__ void ip_stage_twiddles(ulonglong2* twl, const uint64_t* tw, uint32_t tile, uint32_t s0) {
-  typedef IPRounds<LOGB> G;
+  typedef IPRounds<LOGB, W> G;
   constexpr int ENTRIES = G::KC * ((1 << LOGB) - 1);
   for (int e = threadIdx.x; e < ENTRIES; e += G::THREADS) {
     const int d = 31 - __clz((e >> G::LOGKC) + 1);
@@ -78,7 +86,7 @@ __device__ __forceinline__ void ip_stage_twiddles(ulonglong2* twl, const uint64_
 
 // R forward stages on the 2^R words of one item (rows base + (i << pos) of
 // column col), twiddles from the LDS copy.
-template <int R, int LOGB, int AR>
+template <int R, int LOGB, int AR, int W = 8>
 __device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, int pos, int col, const ulonglong2* twl,
                                                uint64_t q) {
   constexpr int E = 1 << R;
@@ -90,7 +98,7 @@ __device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, 
     for (int g = 0; g < (1 << s); ++g) {
       const int i0 = g * 2 * half;
       const int row = base + (i0 << pos);
-      const ulonglong2 w = twl[IPRounds<LOGB>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
+      const ulonglong2 w = twl[IPRounds<LOGB, W>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
 #pragma unroll
       for (int m = 0; m < half; ++m) ct_butterfly<AR>(x[i0 + m], x[i0 + m + half], w.x, w.y, q);
     }
@@ -98,28 +106,26 @@ __device__ __forceinline__ void ip_butterflies(uint64_t (&x)[1 << R], int base, 
 }
 
 // One register round of R forward stages on row bits [POS, POS+R): item k of
-// the thread (k < 8 >> R) is tid + k * THREADS; its words are rows
-// base + (i << POS) of column col, read from global memory (src) or LDS and
-// left in LDS or in x[].
-template <int R, int POS, int LOGB, int AR, bool FROM_GLOBAL, bool TO_LDS>
-__device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
+// the thread (k < W >> R, ip_item); its words are rows base + (i << POS) of
+// column col, read from global memory (src) or LDS and left in LDS or in x[].
+template <int R, int POS, int LOGB, int AR, bool FROM_GLOBAL, bool TO_LDS, int W = 8>
+__device__ __forceinline__ void ip_round(uint64_t (&x)[W], const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
                                          uint32_t tile, int log_n, uint64_t q) {
-  constexpr int T = IPRounds<LOGB>::THREADS;
-  constexpr int NI = 8 >> R;
+  constexpr int NI = W >> R;
   uint64_t y[NI][1 << R];
   int col[NI], base[NI];
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    ip_item<R, LOGB>(k, POS, col[k], base[k]);
+    ip_item<R, LOGB, W>(k, POS, col[k], base[k]);
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       const int row = base[k] + (i << POS);
-      y[k][i] = FROM_GLOBAL ? src[ip_word<LOGB>(tile, row, col[k])] : lds[ip_lds<LOGB>(row, col[k])];
+      y[k][i] = FROM_GLOBAL ? src[ip_word<LOGB, W>(tile, row, col[k])] : lds[ip_lds<LOGB>(row, col[k])];
     }
   }
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
-    ip_butterflies<R, LOGB, AR>(y[k], base[k], POS, col[k], twl, q);
+    ip_butterflies<R, LOGB, AR, W>(y[k], base[k], POS, col[k], twl, q);
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       if (TO_LDS) lds[ip_lds<LOGB>(base[k] + (i << POS), col[k])] = y[k][i];
@@ -135,27 +141,32 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[8], const uint64_t* src, 
 // between the two calls (the key words of the inner product) are in flight
 // during the other rounds without holding up the first round's wait for its
 // own loads.
-template <int LOGB, int AR>
+template <int LOGB, int AR, int W = 8>
 __device__ __forceinline__ void ip_row_pass_first(const uint64_t* src, uint64_t* lds, const ulonglong2* twl,
                                                   uint32_t tile, int log_n, uint64_t q) {
-  typedef IPRounds<LOGB> G;
-  uint64_t unused[8];
+  typedef IPRounds<LOGB, W> G;
+  uint64_t unused[W];
   wave_lds_wait();  // the wave has read its columns' previous contents
-  if constexpr (G::R1 > 0)
-    ip_round<G::R1, LOGB - G::R1, LOGB, AR, true, true>(unused, src, lds, twl, tile, log_n, q);
-  else
-    ip_round<G::R2, G::R3, LOGB, AR, true, true>(unused, src, lds, twl, tile, log_n, q);
+  ip_round<G::R0, LOGB - G::R0, LOGB, AR, true, true, W>(unused, src, lds, twl, tile, log_n, q);
 }
-template <int LOGB, int AR>
-__device__ __forceinline__ void ip_row_pass_rest(uint64_t (&x)[8], uint64_t* lds, const ulonglong2* twl,
-                                                 uint32_t tile, int log_n, uint64_t q) {
-  typedef IPRounds<LOGB> G;
-  if constexpr (G::R1 > 0) {
-    wave_lds_wait();
-    ip_round<G::R2, G::R3, LOGB, AR, false, true>(x, nullptr, lds, twl, tile, log_n, q);
-  }
+// The rounds below row bit POS, through the LDS tile, the last into x[].
+template <int LOGB, int AR, int W, int POS>
+__device__ __forceinline__ void ip_rounds_down(uint64_t (&x)[W], uint64_t* lds, const ulonglong2* twl, uint32_t tile,
+                                               int log_n, uint64_t q) {
+  constexpr int RW = IPRounds<LOGB, W>::RW;
+  constexpr int P = POS - RW;
   wave_lds_wait();
-  ip_round<G::R3, 0, LOGB, AR, false, false>(x, nullptr, lds, twl, tile, log_n, q);
+  if constexpr (P > 0) {
+    ip_round<RW, P, LOGB, AR, false, true, W>(x, nullptr, lds, twl, tile, log_n, q);
+    ip_rounds_down<LOGB, AR, W, P>(x, lds, twl, tile, log_n, q);
+  } else {
+    ip_round<RW, 0, LOGB, AR, false, false, W>(x, nullptr, lds, twl, tile, log_n, q);
+  }
+}
+template <int LOGB, int AR, int W = 8>
+__device__ __forceinline__ void ip_row_pass_rest(uint64_t (&x)[W], uint64_t* lds, const ulonglong2* twl,
+                                                 uint32_t tile, int log_n, uint64_t q) {
+  ip_rounds_down<LOGB, AR, W, LOGB - IPRounds<LOGB, W>::R0>(x, lds, twl, tile, log_n, q);
 }
 
 // R inverse (Gentleman-Sande) stages on the 2^R words of one item (rows
