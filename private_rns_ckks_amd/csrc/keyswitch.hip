@@ -135,7 +135,7 @@ struct RowIPArgs {
 
 // Multiply-accumulate of target limb t (tile gp.tile, item gp.item) over the
 // digits: accb[i] / acca[i] receive sum_j x_j * evk_j.{b,a} for the thread's
-// 8 words (rows base..base+7 of column col), x_j the forward row pass of the
+// W words (rows base..base+W-1 of column col), x_j the forward row pass of the
 // converted limb E[j][t] or, for t inside digit j, the NTT-form input limb
 // (through tau_g when rotating).  Sums of Montgomery products, reduced every
 // mont_fold(m) digits (below 9m); the factor 2^-64 is left in them.
@@ -151,8 +151,8 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
   const uint64_t LKN = (uint64_t)(a.L + a.K) << log_n;
   int col, base;
   ip_item<IPRounds<LOGB, W>::RW, LOGB, W>(0, 0, col, base);
-  const uint32_t w0 = ip_word<LOGB, W>(tile, base, col);
-  const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n) + w0;
+  const uint32_t w0 = ip_word<LOGB, W>(tile, base, col), h0 = w0 >> 1;
+  const uint64_t* evk = a.evk[item] + ((uint64_t)keyl << log_n);
 #pragma unroll
   for (int i = 0; i < W; ++i) accb[i] = acca[i] = 0;
   const int fold = mont_fold(q);
@@ -165,12 +165,12 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
       const uint32_t g = a.g[item];
       if (g) {
 #pragma unroll
-        for (int i = 0; i < W; ++i) x[i] = limb[automorph_src(w0 + i, g, log_n)];
+        for (int i = 0; i < W; ++i) x[i] = at_u32(limb, automorph_src(w0 + i, g, log_n));
       } else {
-        const ulonglong2* src = reinterpret_cast<const ulonglong2*>(limb + w0);
+        const ulonglong2* src = reinterpret_cast<const ulonglong2*>(limb);
 #pragma unroll
         for (int i = 0; i < H; ++i) {
-          const ulonglong2 v = src[i];
+          const ulonglong2 v = at_u32(src, h0 + i);
           x[2 * i] = v.x;
           x[2 * i + 1] = v.y;
         }
@@ -185,11 +185,11 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
       const uint64_t* src = a.E + item * a.E_bstride + ((uint64_t)(j * a.next + t) << log_n);
       ip_row_pass_first<LOGB, AR, W>(src, lds, twl, tile, log_n, q);
 #pragma unroll
-      for (int i = 0; i < H; ++i) vb[i] = kb[i];
+      for (int i = 0; i < H; ++i) vb[i] = at_u32(kb, h0 + i);
       ip_row_pass_rest<LOGB, AR, W>(x, lds, twl, tile, log_n, q);
     } else {
 #pragma unroll
-      for (int i = 0; i < H; ++i) vb[i] = kb[i];
+      for (int i = 0; i < H; ++i) vb[i] = at_u32(kb, h0 + i);
     }
     {
 #pragma unroll
@@ -201,7 +201,7 @@ __device__ __forceinline__ void ip_accumulate(const RowIPArgs& a, uint64_t* lds,
     {
       ulonglong2 v[H];
 #pragma unroll
-      for (int i = 0; i < H; ++i) v[i] = ka[i];
+      for (int i = 0; i < H; ++i) v[i] = at_u32(ka, h0 + i);
 #pragma unroll
       for (int i = 0; i < H; ++i) {
         acca[2 * i] += mont_mul_lazy(x[2 * i], v[i].x, q, mp);
@@ -411,14 +411,14 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
     if (a.add[c]) {
       const uint64_t* ad = a.add[c] + item * a.add_bstride + ((uint64_t)i << log_n);
 #pragma unroll
-      for (int r = 0; r < W; ++r) add[r] = ad[ag ? automorph_src(w0 + r, ag, log_n) : w0 + r];
+      for (int r = 0; r < W; ++r) add[r] = at_u32(ad, ag ? automorph_src(w0 + r, ag, log_n) : w0 + r);
     }
     if (a.accum) {
       const ulonglong2* ac =
-          reinterpret_cast<const ulonglong2*>(a.accum + item * a.accum_bstride + ((uint64_t)(c * (a.ip.level + 1) + i) << log_n) + w0);
+          reinterpret_cast<const ulonglong2*>(a.accum + item * a.accum_bstride + ((uint64_t)(c * (a.ip.level + 1) + i) << log_n));
 #pragma unroll
       for (int r = 0; r < H; ++r) {
-        const ulonglong2 v = ac[r];
+        const ulonglong2 v = at_u32(ac, (w0 >> 1) + r);
         accum[2 * r] = v.x;
         accum[2 * r + 1] = v.y;
       }
@@ -426,7 +426,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
     uint64_t x[W];
     ip_row_pass_rest<LOGB, AR, W>(x, lds, twl, gp.tile, log_n, q);
     ulonglong2* o = reinterpret_cast<ulonglong2*>(a.out + item * a.out_bstride +
-                                                  ((uint64_t)(c * a.out_comp_limbs + i) << log_n) + w0);
+                                                  ((uint64_t)(c * a.out_comp_limbs + i) << log_n));
     if (fast) {
       const uint64_t two_q = 2 * q, four_q = 4 * q;
       const uint32_t m = (uint32_t)pc.inv1;
@@ -436,7 +436,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
         uint64_t e1 = acc[c][2 * r + 1] + two_q - reduce_hi(x[2 * r + 1], q, m) + add[2 * r + 1] + accum[2 * r + 1];
         e0 = reduce_4q(e0 >= four_q ? e0 - four_q : e0, q);
         e1 = reduce_4q(e1 >= four_q ? e1 - four_q : e1, q);
-        o[r] = make_ulonglong2(e0, e1);
+        at_u32(o, (w0 >> 1) + r) = make_ulonglong2(e0, e1);
       }
     } else {
 #pragma unroll
@@ -446,7 +446,7 @@ __device__ __forceinline__ void comb_ip_body(const CombIPArgs& a, uint64_t* lds,
         uint64_t e1 = sub_mod(acc[c][2 * r + 1], reduce64(x[2 * r + 1], q, pc.inv1), q);
         v.x = add_mod(add_mod(e0, add[2 * r], q), accum[2 * r], q);
         v.y = add_mod(add_mod(e1, add[2 * r + 1], q), accum[2 * r + 1], q);
-        o[r] = v;
+        at_u32(o, (w0 >> 1) + r) = v;
       }
     }
   }

@@ -79,6 +79,18 @@ __device__ __forceinline__ void load_tw(const uint64_t* tw, uint32_t ti, uint64_
   wp = v.y;
 }
 
+// Element idx of an array whose base is the same across the wave, addressed
+// as the base plus a 32-bit byte offset (idx * sizeof(T) below 2^32): the
+// global load or store can then take the base from scalar registers and one
+// offset register per lane, instead of a 64-bit address per lane.
+template <class T>
+__device__ __forceinline__ T& at_u32(T* base, uint32_t idx) {
+  typedef typename std::conditional<std::is_const<T>::value, const char, char>::type Byte;
+  uint32_t off = idx * (uint32_t)sizeof(T);
+  asm volatile("" : "+v"(off));
+  return *reinterpret_cast<T*>(reinterpret_cast<Byte*>(base) + off);
+}
+
 enum : int { AR_STRICT = 0, AR_HARVEY = 1, AR_LAZY = 2 };
 __host__ __device__ inline int fwd_ar(uint64_t q) {
   return q < (1ull << 57) ? AR_LAZY : q < (1ull << 61) ? AR_HARVEY : AR_STRICT;

@@ -120,7 +120,7 @@ __device__ __forceinline__ void ip_round(uint64_t (&x)[W], const uint64_t* src, 
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
       const int row = base[k] + (i << POS);
-      y[k][i] = FROM_GLOBAL ? src[ip_word<LOGB, W>(tile, row, col[k])] : lds[ip_lds<LOGB>(row, col[k])];
+      y[k][i] = FROM_GLOBAL ? at_u32(src, ip_word<LOGB, W>(tile, row, col[k])) : lds[ip_lds<LOGB>(row, col[k])];
     }
   }
 #pragma unroll
