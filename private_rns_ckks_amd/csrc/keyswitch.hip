@@ -247,7 +247,7 @@ __device__ __forceinline__ void ip_inv_rounds_up(uint64_t* lds, uint32_t tile, i
     round_regs<R, true, AR, false, false, POS>(y, b, POS, (int)(blk & 15), LOGB, blk >> 4, s0, log_n, twi, q);
 #pragma unroll
     for (int i = 0; i < (1 << R); ++i) {
-      if constexpr (LAST) dst[ip_word<LOGB, W>(tile, b + (i << POS), c)] = inv_row_out<AR>(y[i], q, inv1);
+      if constexpr (LAST) at_u32(dst, ip_word<LOGB, W>(tile, b + (i << POS), c)) = inv_row_out<AR>(y[i], q, inv1);
       else lds[ip_lds<LOGB>(b + (i << POS), c)] = y[i];
     }
   }
