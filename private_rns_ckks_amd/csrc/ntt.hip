@@ -121,14 +121,90 @@ int launch_row_inv(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs) {
   return CKKS_OK;
 }
 
+// Forward row pass (the transform's last pass, output in [0, q)) with the
+// tile's twiddles staged in LDS once per workgroup, over `items` batch items
+// of one (tile, job); 4 words per thread, so that four waves share a SIMD.
+template <int LOGB, int LOGN>
+__global__ __launch_bounds__((IPRounds<LOGB, 4>::THREADS)) void ntt_row_fwd_kernel(PassArgs a, int items,
+                                                                                    int n_items) {
+  typedef IPRounds<LOGB, 4> G;
+  __shared__ uint64_t lds[(1 << LOGB) * G::KC];
+  __shared__ ulonglong2 twl[G::KC * ((1 << LOGB) - 1)];
+  const GridPos g0 = row_grid_pos();
+  const int job = g0.job;
+  const int log_n = LOGN ? LOGN : (int)a.log_n;
+  const int p = a.prime_idx[job];
+  const PrimeConst& pc = a.prime[p];
+  const uint64_t q = pc.q;
+  ip_stage_twiddles<LOGB, 4>(twl, a.tw + ((uint64_t)p << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  __syncthreads();  // every wave reads the twiddles every thread staged
+  int col, base;
+  ip_item<G::RW, LOGB, 4>(0, 0, col, base);
+  const uint32_t h0 = ip_word<LOGB, 4>(g0.tile, base, col) >> 1;
+  const int far = fwd_ar(q);
+  // lazy outputs lie below 70q < 2^63 for q < 2^57: one high-word quotient
+  // leaves [0, 2q) when q is above 2^33 and below 2^56
+  const bool hi_red = far == AR_LAZY && q > kReduceHiMin && q < (1ull << 56);
+  for (int k = 0; k < items; ++k) {
+    const int item = g0.item * items + k;
+    if (item >= n_items) break;
+    const uint64_t* src = a.src + item * a.src_bstride + ((uint64_t)a.src_limb[job] << log_n);
+    ulonglong2* dst =
+        reinterpret_cast<ulonglong2*>(a.dst + item * a.dst_bstride + ((uint64_t)a.dst_limb[job] << log_n));
+    uint64_t x[4];
+    if (far == AR_LAZY) {
+      ip_row_pass_first<LOGB, AR_LAZY, 4>(src, lds, twl, g0.tile, log_n, q);
+      ip_row_pass_rest<LOGB, AR_LAZY, 4>(x, lds, twl, g0.tile, log_n, q);
+    } else if (far == AR_HARVEY) {
+      ip_row_pass_first<LOGB, AR_HARVEY, 4>(src, lds, twl, g0.tile, log_n, q);
+      ip_row_pass_rest<LOGB, AR_HARVEY, 4>(x, lds, twl, g0.tile, log_n, q);
+    } else {
+      ip_row_pass_first<LOGB, AR_STRICT, 4>(src, lds, twl, g0.tile, log_n, q);
+      ip_row_pass_rest<LOGB, AR_STRICT, 4>(x, lds, twl, g0.tile, log_n, q);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = hi_red ? reduce_2q(reduce_hi(x[i], q, (uint32_t)pc.inv1), q) : reduce64(x[i], q, pc.inv1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) at_u32(dst, h0 + i) = make_ulonglong2(x[2 * i], x[2 * i + 1]);
+  }
+}
+
+typedef void (*RowFwdFn)(PassArgs, int, int);
+
+RowFwdFn pick_row_fwd(int log_n, int logb) {
+  if (log_n == 16 && logb == 8) return ntt_row_fwd_kernel<8, 16>;
+  switch (logb) {
+    case 5: return ntt_row_fwd_kernel<5, 0>;
+    case 6: return ntt_row_fwd_kernel<6, 0>;
+    case 7: return ntt_row_fwd_kernel<7, 0>;
+    case 8: return ntt_row_fwd_kernel<8, 0>;
+  }
+  return nullptr;
+}
+
+// The forward transform's row pass over `batch` items (final: output in [0, q)).
+int launch_row_fwd(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs) {
+  const int log_n = (int)c->log_n, logb = logb_row(log_n);
+  RowFwdFn fn = pick_row_fwd(log_n, logb);
+  if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
+  const int items = std::max(1, std::min(8, batch / 2));
+  const int logkc = ip_logkc(logb, 4);
+  TraceScope ts(c, s, "ntt_pass", (double)njobs * batch * (c->N / 2) * logb);
+  hipLaunchKernelGGL(fn, dim3(c->N >> (logkc + logb), njobs, (batch + items - 1) / items),
+                     dim3((1u << (logkc + logb)) / 4), 0, s, a, items, batch);
+  CKKS_HIP_CHECK(hipGetLastError());
+  return CKKS_OK;
+}
+
 typedef void (*PassFn)(PassArgs);
 
-int launch_pass(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs, int logb, bool inv, bool colfast) {
-  const int log_n = (int)c->log_n;
-  // the inverse row pass runs in ntt_row_inv_kernel (launch_row_inv)
-  PassFn fn = inv ? (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, true) : nullptr)
-                  : (colfast ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, true)
-                             : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, false));
+// Column pass (the forward transform's first pass, the inverse's last); the
+// row passes run in ntt_row_fwd_kernel and ntt_row_inv_kernel.
+int launch_col_pass(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs, bool inv) {
+  const int log_n = (int)c->log_n, logb = logb_col(log_n);
+  PassFn fn = inv ? CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, true, true)
+                  : CKKS_PICK_PASS(ntt_pass_kernel, log_n, logb, false, true);
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
   const double limbs = (double)njobs * batch;
   TraceScope ts(c, s, "ntt_pass", limbs * (c->N / 2) * logb + ((inv && a.final_pass && a.scale_mode) ? limbs * c->N : 0));
@@ -165,7 +241,7 @@ int ntt_run_scaled(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, si
   a.final_pass = 0;
   int rc;
   if (!inverse) {
-    rc = launch_pass(c, s, a, batch, jobs.n, logb_col(log_n), false, true);
+    rc = launch_col_pass(c, s, a, batch, jobs.n, false);
   } else {
     rc = launch_row_inv(c, s, a, batch, jobs.n);
   }
@@ -174,10 +250,8 @@ int ntt_run_scaled(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, si
   a.src_bstride = dst_bstride;
   for (int i = 0; i < jobs.n; ++i) a.src_limb[i] = jobs.dst_limb[i];
   a.final_pass = 1;
-  if (!inverse) {
-    return launch_pass(c, s, a, batch, jobs.n, logb_row(log_n), false, false);
-  }
-  return launch_pass(c, s, a, batch, jobs.n, logb_col(log_n), true, true);
+  if (!inverse) return launch_row_fwd(c, s, a, batch, jobs.n);
+  return launch_col_pass(c, s, a, batch, jobs.n, true);
 }
 
 int ntt_pass_only(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, size_t src_bstride, size_t dst_bstride,
@@ -203,9 +277,9 @@ int ntt_pass_only(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, siz
   a.src_bstride = src_bstride;
   a.dst_bstride = dst_bstride;
   a.final_pass = first ? 0 : 1;
-  const bool colpass = (inverse != first);  // forward first / inverse second
-  if (inverse && first) return launch_row_inv(c, s, a, batch, jobs.n);
-  return launch_pass(c, s, a, batch, jobs.n, colpass ? logb_col(log_n) : logb_row(log_n), inverse, colpass);
+  // the column pass is the forward transform's first and the inverse's last
+  if (inverse == first) return inverse ? launch_row_inv(c, s, a, batch, jobs.n) : launch_row_fwd(c, s, a, batch, jobs.n);
+  return launch_col_pass(c, s, a, batch, jobs.n, inverse);
 }
 
 int ntt_run(Ctx* c, hipStream_t s, const uint64_t* src, uint64_t* dst, size_t src_bstride, size_t dst_bstride,
