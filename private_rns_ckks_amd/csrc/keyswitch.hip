@@ -59,17 +59,17 @@ struct GatherArgs {
 // through tau_g, for up to 8 batch items per workgroup that share the tile's
 // inverse twiddles staged in LDS (as the batched inverse NTT); the output
 // (below 4q) goes to the scaled inverse column pass.
-template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void intt_row_gather_kernel(GatherArgs a, int items,
-                                                                                 int n_items) {
-  typedef IPRounds<LOGB> G;
+template <int LOGB, int LOGN, int W>
+__global__ __launch_bounds__((IPRounds<LOGB, W>::THREADS)) void intt_row_gather_kernel(GatherArgs a, int items,
+                                                                                      int n_items) {
+  typedef IPRounds<LOGB, W> G;
   __shared__ uint64_t lds[(1 << LOGB) * G::KC];
   __shared__ ulonglong2 twl[G::KC * ((1 << LOGB) - 1)];
   const GridPos g0 = row_grid_pos();
   const int limb = g0.job;
   const int log_n = LOGN ? LOGN : a.log_n;
   const PrimeConst& pc = a.prime[limb];
-  ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)limb << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  ip_stage_twiddles<LOGB, W>(twl, a.tw + ((uint64_t)limb << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
   __syncthreads();  // every wave reads the twiddles every thread staged
   const int iar = inv_ar(pc.q);
   const uint64_t off = (uint64_t)limb << log_n;
@@ -80,31 +80,34 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void intt_row_gather_kerne
     uint64_t* dst = a.dst + item * a.dst_bstride + off;
     const uint32_t g = a.g[item];
     if (iar == AR_LAZY)
-      ip_inv_row_pass<LOGB, AR_LAZY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+      ip_inv_row_pass<LOGB, AR_LAZY, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
     else if (iar == AR_HARVEY)
-      ip_inv_row_pass<LOGB, AR_HARVEY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+      ip_inv_row_pass<LOGB, AR_HARVEY, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
     else
-      ip_inv_row_pass<LOGB, AR_STRICT>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
+      ip_inv_row_pass<LOGB, AR_STRICT, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1, g, log_n);
   }
 }
 
 typedef void (*GatherFn)(GatherArgs, int, int);
 
+// Words per thread of step A (IPRounds).
+constexpr int kGatherW = 4;
+
 // Step A over n_items items of nq limbs.
 int launch_gather(Ctx* c, hipStream_t s, const GatherArgs& ga, int nq, int n_items) {
   const int log_n = (int)c->log_n, logb = logb_row(log_n);
   GatherFn fn = nullptr;
-  if (log_n == 16 && logb == 8) fn = intt_row_gather_kernel<8, 16>;
-  else if (logb == 5) fn = intt_row_gather_kernel<5, 0>;
-  else if (logb == 6) fn = intt_row_gather_kernel<6, 0>;
-  else if (logb == 7) fn = intt_row_gather_kernel<7, 0>;
-  else if (logb == 8) fn = intt_row_gather_kernel<8, 0>;
+  if (log_n == 16 && logb == 8) fn = intt_row_gather_kernel<8, 16, kGatherW>;
+  else if (logb == 5) fn = intt_row_gather_kernel<5, 0, kGatherW>;
+  else if (logb == 6) fn = intt_row_gather_kernel<6, 0, kGatherW>;
+  else if (logb == 7) fn = intt_row_gather_kernel<7, 0, kGatherW>;
+  else if (logb == 8) fn = intt_row_gather_kernel<8, 0, kGatherW>;
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported N");
   const int items = std::max(1, std::min(8, n_items / 2));
-  const uint32_t tiles = c->N >> (ip_logkc(logb) + logb);
-  const int threads = (1 << ip_logkc(logb)) << (logb - 3);  // IPRounds<logb>::THREADS
+  const int logkc = ip_logkc(logb, kGatherW);
   TraceScope ts(c, s, "intt_row_gather", (double)n_items * nq * (c->N / 2) * logb);
-  hipLaunchKernelGGL(fn, dim3(tiles, nq, (n_items + items - 1) / items), dim3(threads), 0, s, ga, items, n_items);
+  hipLaunchKernelGGL(fn, dim3(c->N >> (logkc + logb), nq, (n_items + items - 1) / items),
+                     dim3((1u << (logkc + logb)) / kGatherW), 0, s, ga, items, n_items);
   CKKS_HIP_CHECK(hipGetLastError());
   return CKKS_OK;
 }

@@ -65,9 +65,10 @@ __global__ __launch_bounds__(kThreads) void ntt_pass_kernel(PassArgs a) {
 // Inverse row pass (the transform's first pass) with the tile's inverse
 // twiddles staged in LDS once per workgroup, over `items` batch items of one
 // (tile, job).
-template <int LOGB, int LOGN>
-__global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_inv_kernel(PassArgs a, int items, int n_items) {
-  typedef IPRounds<LOGB> G;
+template <int LOGB, int LOGN, int W>
+__global__ __launch_bounds__((IPRounds<LOGB, W>::THREADS)) void ntt_row_inv_kernel(PassArgs a, int items,
+                                                                                    int n_items) {
+  typedef IPRounds<LOGB, W> G;
   __shared__ uint64_t lds[(1 << LOGB) * G::KC];
   __shared__ ulonglong2 twl[G::KC * ((1 << LOGB) - 1)];
   const GridPos g0 = row_grid_pos();
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_inv_kernel(Pa
   const int log_n = LOGN ? LOGN : (int)a.log_n;
   const int p = a.prime_idx[job];
   const PrimeConst& pc = a.prime[p];
-  ip_stage_twiddles<LOGB>(twl, a.tw + ((uint64_t)p << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
+  ip_stage_twiddles<LOGB, W>(twl, a.tw + ((uint64_t)p << (log_n + 1)), g0.tile, (uint32_t)logb_col(log_n));
   __syncthreads();  // every wave reads the twiddles every thread staged
   for (int k = 0; k < items; ++k) {
     const int item = g0.item * items + k;
@@ -84,23 +85,26 @@ __global__ __launch_bounds__(IPRounds<LOGB>::THREADS) void ntt_row_inv_kernel(Pa
     uint64_t* dst = a.dst + item * a.dst_bstride + ((uint64_t)a.dst_limb[job] << log_n);
     const int iar = inv_ar(pc.q);
     if (iar == AR_LAZY)
-      ip_inv_row_pass<LOGB, AR_LAZY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
+      ip_inv_row_pass<LOGB, AR_LAZY, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
     else if (iar == AR_HARVEY)
-      ip_inv_row_pass<LOGB, AR_HARVEY>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
+      ip_inv_row_pass<LOGB, AR_HARVEY, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
     else
-      ip_inv_row_pass<LOGB, AR_STRICT>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
+      ip_inv_row_pass<LOGB, AR_STRICT, W>(src, dst, lds, twl, g0.tile, pc.q, pc.inv1);
   }
 }
 
 typedef void (*RowInvFn)(PassArgs, int, int);
 
+// Words per thread of the inverse row pass (IPRounds).
+constexpr int kRowInvW = 4;
+
 RowInvFn pick_row_inv(int log_n, int logb) {
-  if (log_n == 16 && logb == 8) return ntt_row_inv_kernel<8, 16>;
+  if (log_n == 16 && logb == 8) return ntt_row_inv_kernel<8, 16, kRowInvW>;
   switch (logb) {
-    case 5: return ntt_row_inv_kernel<5, 0>;
-    case 6: return ntt_row_inv_kernel<6, 0>;
-    case 7: return ntt_row_inv_kernel<7, 0>;
-    case 8: return ntt_row_inv_kernel<8, 0>;
+    case 5: return ntt_row_inv_kernel<5, 0, kRowInvW>;
+    case 6: return ntt_row_inv_kernel<6, 0, kRowInvW>;
+    case 7: return ntt_row_inv_kernel<7, 0, kRowInvW>;
+    case 8: return ntt_row_inv_kernel<8, 0, kRowInvW>;
   }
   return nullptr;
 }
@@ -113,10 +117,10 @@ int launch_row_inv(Ctx* c, hipStream_t s, PassArgs& a, int batch, int njobs) {
   RowInvFn fn = pick_row_inv(log_n, logb);
   if (!fn) return set_error(CKKS_EINTERNAL, "unsupported NTT pass size");
   const int items = std::max(1, std::min(8, batch / 2));
-  const uint32_t tiles = c->N >> (ip_logkc(logb) + logb);
-  const int threads = (1 << ip_logkc(logb)) << (logb - 3);  // IPRounds<logb>::THREADS
+  const int logkc = ip_logkc(logb, kRowInvW);
   TraceScope ts(c, s, "ntt_pass", (double)njobs * batch * (c->N / 2) * logb);
-  hipLaunchKernelGGL(fn, dim3(tiles, njobs, (batch + items - 1) / items), dim3(threads), 0, s, a, items, batch);
+  hipLaunchKernelGGL(fn, dim3(c->N >> (logkc + logb), njobs, (batch + items - 1) / items),
+                     dim3((1u << (logkc + logb)) / kRowInvW), 0, s, a, items, batch);
   CKKS_HIP_CHECK(hipGetLastError());
   return CKKS_OK;
 }

@@ -173,7 +173,7 @@ __device__ __forceinline__ void ip_row_pass_rest(uint64_t (&x)[W], uint64_t* lds
 // base + (i << pos) of column col), highest stage first, twiddles from the
 // LDS copy of the inverse table.  KDONE: stages of this pass already done
 // (the bound of the lazy butterflies).
-template <int R, int LOGB, int AR, int KDONE>
+template <int R, int LOGB, int AR, int KDONE, int W = 8>
 __device__ __forceinline__ void ip_inv_butterflies(uint64_t (&x)[1 << R], int base, int pos, int col,
                                                    const ulonglong2* twl, uint64_t q) {
   constexpr int E = 1 << R;
@@ -186,7 +186,7 @@ __device__ __forceinline__ void ip_inv_butterflies(uint64_t (&x)[1 << R], int ba
     for (int g = 0; g < (1 << s); ++g) {
       const int i0 = g * 2 * half;
       const int row = base + (i0 << pos);
-      const ulonglong2 w = twl[IPRounds<LOGB>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
+      const ulonglong2 w = twl[IPRounds<LOGB, W>::KC * ((1 << d) - 1) + (col << d) + (row >> (LOGB - d))];
 #pragma unroll
       for (int m = 0; m < half; ++m)
         gs_butterfly_ar<AR>(x[i0 + m], x[i0 + m + half], w.x, w.y, q, (4 * q) << (KDONE + ss));
@@ -204,72 +204,69 @@ __device__ __forceinline__ uint64_t inv_row_out(uint64_t v, uint64_t q, uint64_t
   return q > kReduceHiMin ? reduce_hi(v, q, (uint32_t)inv1) : reduce64(v, q, inv1);
 }
 
+// The inverse row pass's rounds from row bit POS up, through the LDS tile
+// (rounds of log2(W) stages, the last taking what is left); the last round
+// stores the pass's output to dst.
+template <int LOGB, int AR, int W, int POS>
+__device__ __forceinline__ void ip_inv_rounds_up(uint64_t* dst, uint64_t* lds, const ulonglong2* twl, uint32_t tile,
+                                                 uint64_t q, uint64_t inv1) {
+  typedef IPRounds<LOGB, W> G;
+  constexpr bool LAST = POS + G::RW >= LOGB;
+  constexpr int R = LAST ? LOGB - POS : G::RW;
+#pragma unroll
+  for (int k = 0; k < (W >> R); ++k) {
+    int c, b;
+    ip_item<R, LOGB, W>(k, POS, c, b);
+    uint64_t y[1 << R];
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << POS), c)];
+    ip_inv_butterflies<R, LOGB, AR, POS, W>(y, b, POS, c, twl, q);
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) {
+      if constexpr (LAST) at_u32(dst, ip_word<LOGB, W>(tile, b + (i << POS), c)) = inv_row_out<AR>(y[i], q, inv1);
+      else lds[ip_lds<LOGB>(b + (i << POS), c)] = y[i];
+    }
+  }
+  if constexpr (!LAST) {
+    wave_lds_wait();
+    ip_inv_rounds_up<LOGB, AR, W, POS + R>(dst, lds, twl, tile, q, inv1);
+  }
+}
+
 // Inverse row pass of one limb on the tile: src holds canonical (or below
 // 4q) words, dst receives the pass's output for the column pass that follows
 // (below 4q: inv_row_out); with g nonzero the input is read through tau_g.
-// Rounds on row bits 0-2 (8 consecutive words per thread, 16-byte loads, or
-// word by word through tau_g), then 3.. and
-// 6.. through the LDS tile; the last round's stores cover consecutive rows
-// across the wave.
-template <int LOGB, int AR>
+// The first round takes the thread's W consecutive words (16-byte loads, or
+// word by word through tau_g) on the low row bits in registers; the other
+// rounds go up through the LDS tile, and the last one's stores cover
+// consecutive rows across the wave.
+template <int LOGB, int AR, int W = 8>
 __device__ __forceinline__ void ip_inv_row_pass(const uint64_t* src, uint64_t* dst, uint64_t* lds,
                                                 const ulonglong2* twl, uint32_t tile, uint64_t q, uint64_t inv1,
                                                 uint32_t g = 0, int log_n = 0) {
-  typedef IPRounds<LOGB> G;
-  constexpr int T = G::THREADS;
+  typedef IPRounds<LOGB, W> G;
   int col, base;
-  ip_item<3, LOGB>(0, 0, col, base);
-  uint64_t x[8];
-  const uint32_t w0 = ip_word<LOGB>(tile, base, col);
+  ip_item<G::RW, LOGB, W>(0, 0, col, base);
+  uint64_t x[W];
+  const uint32_t w0 = ip_word<LOGB, W>(tile, base, col);
   if (g) {  // the input through tau_g (automorph.h): word j comes from word automorph_src(j, g)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = src[automorph_src(w0 + i, g, log_n)];
+    for (int i = 0; i < W; ++i) x[i] = at_u32(src, automorph_src(w0 + i, g, log_n));
   } else {
-    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(src + w0);
+    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(src);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const ulonglong2 v = s2[i];
+    for (int i = 0; i < W / 2; ++i) {
+      const ulonglong2 v = at_u32(s2, (w0 >> 1) + i);
       x[2 * i] = v.x;
       x[2 * i + 1] = v.y;
     }
   }
-  ip_inv_butterflies<3, LOGB, AR, 0>(x, base, 0, col, twl, q);
+  ip_inv_butterflies<G::RW, LOGB, AR, 0, W>(x, base, 0, col, twl, q);
   wave_lds_wait();  // the wave has read its columns' previous contents
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
+  for (int i = 0; i < W; ++i) lds[ip_lds<LOGB>(base + i, col)] = x[i];
   wave_lds_wait();
-  constexpr int N2 = 8 >> G::R2;
-#pragma unroll
-  for (int k = 0; k < N2; ++k) {
-    int c, b;
-    ip_item<G::R2, LOGB>(k, 3, c, b);
-    uint64_t y[1 << G::R2];
-#pragma unroll
-    for (int i = 0; i < (1 << G::R2); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << 3), c)];
-    ip_inv_butterflies<G::R2, LOGB, AR, 3>(y, b, 3, c, twl, q);
-#pragma unroll
-    for (int i = 0; i < (1 << G::R2); ++i) {
-      if constexpr (G::R1 == 0) dst[ip_word<LOGB>(tile, b + (i << 3), c)] = inv_row_out<AR>(y[i], q, inv1);
-      else lds[ip_lds<LOGB>(b + (i << 3), c)] = y[i];
-    }
-  }
-  if constexpr (G::R1 > 0) {
-    wave_lds_wait();
-    constexpr int N1 = 8 >> G::R1;
-    constexpr int P1 = 3 + G::R2;
-#pragma unroll
-    for (int k = 0; k < N1; ++k) {
-      int c, b;
-      ip_item<G::R1, LOGB>(k, P1, c, b);
-      uint64_t y[1 << G::R1];
-#pragma unroll
-      for (int i = 0; i < (1 << G::R1); ++i) y[i] = lds[ip_lds<LOGB>(b + (i << P1), c)];
-      ip_inv_butterflies<G::R1, LOGB, AR, P1>(y, b, P1, c, twl, q);
-#pragma unroll
-      for (int i = 0; i < (1 << G::R1); ++i)
-        dst[ip_word<LOGB>(tile, b + (i << P1), c)] = inv_row_out<AR>(y[i], q, inv1);
-    }
-  }
+  ip_inv_rounds_up<LOGB, AR, W, G::RW>(dst, lds, twl, tile, q, inv1);
 }
 
 }  // namespace nttc
