@@ -34,12 +34,18 @@ __device__ __forceinline__ RedConst red_const(ConstPrime p, int i) {
 // butterflies start from words below 6q and stay below 70q < 2^64 for
 // q < 2^57; Harvey butterflies accept words below 8q, strict ones below 4q).
 // NS is 8 or 16; sources past the real count have zero constants and words.
-template <int NS, bool WIDE>
-__device__ __forceinline__ uint64_t conv_dot(const Split<WIDE> (&y)[NS], ConstU64 conv, int stride,
-                                             const RedConst& pc) {
-  uint64_t cw[NS];
+// conv_consts reads one target's constants (scalar loads), conv_dot_c forms
+// one coefficient's sum from them, so a thread converting several
+// coefficients loads each constant once.
+template <int NS>
+__device__ __forceinline__ void conv_consts(ConstU64 conv, int stride, uint64_t (&cw)[NS]) {
 #pragma unroll
   for (int i = 0; i < NS; ++i) cw[i] = conv[i * stride];
+}
+
+template <int NS, bool WIDE>
+__device__ __forceinline__ uint64_t conv_dot_c(const Split<WIDE> (&y)[NS], const uint64_t (&cw)[NS],
+                                               const RedConst& pc) {
   uint64_t r = 0;
 #pragma unroll
   for (int g = 0; g < NS; g += 8) {

@@ -43,26 +43,37 @@ __global__ void automorph_coeff_kernel(const uint64_t* in, uint64_t* out, uint64
 // x: the digit limbs already multiplied by [qhat_i^-1]_{q_i} (canonical y_i),
 // [level+1][N] per item.  out: [beta][next][N] per item; for every target limb
 // t outside the digit, out_t = sum_i y_i [qhat_i]_{m_t} mod m_t (exact,
-// left in the range conv_dot gives).
+// left in the range conv_dot_c gives).
 // Constants [qhat_i]_{m_t}: [NS][next], split into 30-bit halves, zero rows
 // past the digit's size.  WIDE: some prime is at least 2^60 (full-width
-// products).
+// products).  Every thread converts two adjacent coefficients (16-byte loads
+// and stores), so each target's constants serve two words; limbs are
+// addressed as a wave-uniform base plus a 32-bit lane offset.
 template <int NS, bool WIDE>
 __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
   const int j = blockIdx.y;
   const int lo = a.lo[j], hi = a.hi[j], na = hi - lo;
   const ConstU64 conv = (ConstU64)(a.tables + a.offset[j] + 2 * na);
   const ConstPrime prime = (ConstPrime)a.prime;
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t* x = a.x + blockIdx.z * a.x_bstride + (uint64_t)lo * a.n + c;
-  uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n + c;
-  Split<WIDE> y[NS];
+  const uint32_t c2 = blockIdx.x * blockDim.x + threadIdx.x;  // coefficients 2*c2, 2*c2+1
+  const uint64_t* x = a.x + blockIdx.z * a.x_bstride + (uint64_t)lo * a.n;
+  uint64_t* out = a.out + blockIdx.z * a.out_bstride + (uint64_t)j * a.next * a.n;
+  Split<WIDE> y0[NS], y1[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) y[i] = split_word<WIDE>(i < na ? x[(uint64_t)i * a.n] : 0);
+  for (int i = 0; i < NS; ++i) {
+    ulonglong2 v = make_ulonglong2(0, 0);
+    if (i < na) v = nttc::at_u32(reinterpret_cast<const ulonglong2*>(x + (uint64_t)i * a.n), c2);
+    y0[i] = split_word<WIDE>(v.x);
+    y1[i] = split_word<WIDE>(v.y);
+  }
   for (int t = 0; t < a.next; ++t) {
     if (t >= lo && t < hi) continue;
     const RedConst pc = red_const(prime, t <= a.level ? t : a.L + (t - a.level - 1));
-    out[(uint64_t)t * a.n] = conv_dot<NS, WIDE>(y, conv + t, a.next, pc);
+    uint64_t cw[NS];
+    conv_consts<NS>(conv + t, a.next, cw);
+    const uint64_t r0 = conv_dot_c<NS, WIDE>(y0, cw, pc);
+    const uint64_t r1 = conv_dot_c<NS, WIDE>(y1, cw, pc);
+    nttc::at_u32(reinterpret_cast<ulonglong2*>(out + (uint64_t)t * a.n), c2) = make_ulonglong2(r0, r1);
   }
 }
 
@@ -71,31 +82,39 @@ __global__ __launch_bounds__(256) void modup_kernel(ModUpArgs a) {
 // coefficient form).  Centred lift: y_k counts as negative when
 // y_k > (p_k-1)/2, and then sum_k ybar_k [phat_k P^-1]_{q_i} =
 // sum_k y_k [1/p_k]_{q_i} - #negative  (mod q_i).  w: [2][level+1][N] per item,
-// in the range conv_dot gives.
+// in the range conv_dot_c gives.
 // Constants [1/p_k]_{q_i}: [NS][L], split into 30-bit halves, zero rows past K.
+// Two adjacent coefficients per thread, as ModUp.
 template <int NS, bool WIDE>
 __global__ __launch_bounds__(256) void moddown_conv_kernel(ModDownArgs a) {
   const int nq = a.level + 1;
   const ConstU64 conv = (ConstU64)a.conv;
   const ConstPrime prime = (ConstPrime)a.prime;
-  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t c2 = blockIdx.x * blockDim.x + threadIdx.x;  // coefficients 2*c2, 2*c2+1
   const int comp = blockIdx.y;
-  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.acc_comp_limbs + a.acc_k0) * a.n + c;
-  Split<WIDE> y[NS];
-  uint32_t neg = 0;
+  const uint64_t* acc = a.acc + blockIdx.z * a.acc_bstride + (uint64_t)(comp * a.acc_comp_limbs + a.acc_k0) * a.n;
+  Split<WIDE> y0[NS], y1[NS];
+  uint32_t neg0 = 0, neg1 = 0;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    uint64_t v = 0;
+    ulonglong2 v = make_ulonglong2(0, 0);
     if (k < a.K) {
-      v = acc[(uint64_t)k * a.n];
-      neg += v > (prime[a.L + k].q >> 1) ? 1u : 0u;
+      v = nttc::at_u32(reinterpret_cast<const ulonglong2*>(acc + (uint64_t)k * a.n), c2);
+      const uint64_t half = prime[a.L + k].q >> 1;
+      neg0 += v.x > half ? 1u : 0u;
+      neg1 += v.y > half ? 1u : 0u;
     }
-    y[k] = split_word<WIDE>(v);
+    y0[k] = split_word<WIDE>(v.x);
+    y1[k] = split_word<WIDE>(v.y);
   }
-  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * nq * a.n + c;
+  uint64_t* w = a.w + blockIdx.z * a.w_bstride + (uint64_t)comp * nq * a.n;
   for (int i = 0; i < nq; ++i) {
     const RedConst pc = red_const(prime, i);
-    w[(uint64_t)i * a.n] = sub_mod(conv_dot<NS, WIDE>(y, conv + i, a.L, pc), neg, pc.q);
+    uint64_t cw[NS];
+    conv_consts<NS>(conv + i, a.L, cw);
+    const uint64_t r0 = sub_mod(conv_dot_c<NS, WIDE>(y0, cw, pc), neg0, pc.q);
+    const uint64_t r1 = sub_mod(conv_dot_c<NS, WIDE>(y1, cw, pc), neg1, pc.q);
+    nttc::at_u32(reinterpret_cast<ulonglong2*>(w + (uint64_t)i * a.n), c2) = make_ulonglong2(r0, r1);
   }
 }
 
@@ -440,7 +459,7 @@ int launch_modup(Ctx* c, hipStream_t s, ModUpArgs& a, int beta, int batch) {
   TraceScope ts(c, s, "modup", units * batch * c->N);
   auto fn = conv_rows(c->alpha) == 8 ? (c->wide ? modup_kernel<8, true> : modup_kernel<8, false>)
                                      : (c->wide ? modup_kernel<16, true> : modup_kernel<16, false>);
-  hipLaunchKernelGGL(fn, dim3(c->N / 256, beta, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(c->N / 512, beta, batch), dim3(256), 0, s, a);  // two coefficients per thread
   LAUNCH_CHECK();
   return CKKS_OK;
 }
@@ -449,7 +468,7 @@ int launch_moddown_conv(Ctx* c, hipStream_t s, ModDownArgs& a, int batch) {
   TraceScope ts(c, s, "moddown_conv", (double)batch * 2 * (a.K + (double)(a.level + 1) * (a.K + 1)) * c->N);
   auto fn = conv_rows(c->K) == 8 ? (c->wide ? moddown_conv_kernel<8, true> : moddown_conv_kernel<8, false>)
                                  : (c->wide ? moddown_conv_kernel<16, true> : moddown_conv_kernel<16, false>);
-  hipLaunchKernelGGL(fn, dim3(c->N / 256, 2, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(c->N / 512, 2, batch), dim3(256), 0, s, a);  // two coefficients per thread
   LAUNCH_CHECK();
   return CKKS_OK;
 }
