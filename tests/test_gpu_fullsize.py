@@ -5,11 +5,12 @@ C3: the 32-ciphertext rotation batch (N=2^16, L=24, K=8, dnum=3), with item 0
     a real encryption under a real Galois key (decrypt = shifted slots).
 C5: 48 ciphertext pairs: multiply + relinearise + rescale, then rotate-and-sum
     over the 15 power-of-two offsets, with pair 0 real (decrypt = slot sum).
-C4: the BSGS matvec at level 12 with 12 x 3 x 8 x 8 diagonals (15.7 GB).
+C4: the BSGS matvec at level 12 with 12 x 3 x 8 x 8 diagonals (15.7 GB),
+    outputs 0 and 11 checked.
 Polynomial evaluation: degree 7 on the 48 ciphertexts of a C5 batch at level
     23 (scale 2^54), with item 0 a real encryption (decrypts to p(slots)).
 A x V: the encrypted-weight BSGS matvec at level 12 with 3 x 3 x 8 x 8
-    ciphertext diagonals (7.9 GB).
+    ciphertext diagonals (7.9 GB), outputs 0 and 2 checked.
 """
 import numpy as np
 import pytest
@@ -110,12 +111,12 @@ def test_c4_full_ptmatvec(lib, orc, full):
     x = S.uniform_limbs(S.stream(4, "full/x"), P.q[:nq], P.N, lead=(n_in, 2))
     # 15.7 GB of diagonals: generated and uploaded one output block at a time
     d_diags = torch.empty((n_out, n_in, n2, n1, nq, P.N), dtype=torch.int64, device="cuda")
-    diag0 = None
+    kept = {}  # the first and last output blocks' diagonals, for the oracle
     for o in range(n_out):
         blk = S.uniform_limbs(S.stream(o, "full/diag"), P.q[:nq], P.N, lead=(n_in, n2, n1))
         d_diags[o].copy_(torch.from_numpy(blk.view(np.int64)))
-        if o == 0:
-            diag0 = blk
+        if o in (0, n_out - 1):
+            kept[o] = blk
         del blk
     gb = [P.galois(bb) for bb in range(1, n1)]
     gg = [P.galois(n1 * g) for g in range(1, n2)]
@@ -129,8 +130,11 @@ def test_c4_full_ptmatvec(lib, orc, full):
     torch.cuda.empty_cache()
     for t, m in enumerate(P.q[:level]):
         assert (got[:, :, t, :] < m).all()
-    ref = orc.ptmatvec(P, level, x, diag0[None], gb, kb, gg, kg)
+    # outputs 0 and n_out-1: the first and last diagonal blocks, output slots
+    # at both ends of the result buffer
+    ref = orc.ptmatvec(P, level, x, np.stack([kept[0], kept[n_out - 1]]), gb, kb, gg, kg)
     assert np.array_equal(got[0], ref[0])
+    assert np.array_equal(got[n_out - 1], ref[1])
 
 
 def test_poly_eval_full(lib, orc, full):
@@ -165,12 +169,12 @@ def test_av_full_ctmatvec(lib, orc, full):
     torch = torch_cuda()
     x = S.uniform_limbs(S.stream(7, "full/av/x"), P.q[:nq], P.N, lead=(n_in, 2))
     d_diags = torch.empty((n_out, n_in, n2, n1, 2, nq, P.N), dtype=torch.int64, device="cuda")
-    diag0 = None
+    kept = {}  # the first and last output blocks' diagonals, for the oracle
     for o in range(n_out):
         blk = S.uniform_limbs(S.stream(o, "full/av/diag"), P.q[:nq], P.N, lead=(n_in, n2, n1, 2))
         d_diags[o].copy_(torch.from_numpy(blk.view(np.int64)))
-        if o == 0:
-            diag0 = blk
+        if o in (0, n_out - 1):
+            kept[o] = blk
         del blk
     rlk = S.uniform_limbs(S.stream(7, "full/av/rlk"), P.mods, P.N, lead=(P.dnum, 2))
     gb = [P.galois(bb) for bb in range(1, n1)]
@@ -185,5 +189,6 @@ def test_av_full_ctmatvec(lib, orc, full):
     torch.cuda.empty_cache()
     for t, m in enumerate(P.q[:level]):
         assert (got[:, :, t, :] < m).all()
-    ref = orc.ctmatvec(P, level, x, diag0[None], rlk, gb, kb, gg, kg)
+    ref = orc.ctmatvec(P, level, x, np.stack([kept[0], kept[n_out - 1]]), rlk, gb, kb, gg, kg)
     assert np.array_equal(got[0], ref[0])
+    assert np.array_equal(got[n_out - 1], ref[1])
