@@ -277,7 +277,7 @@ def main():
     if kstat["launches"]:
         avg_s = kstat["total_ms"] / kstat["launches"] / 1e3
         items_per_launch = B * args.steps / kstat["launches"]
-        alg_bytes = items_per_launch * BYTES_PER_HROT      # the survey's per-HRot bytes x HRots per launch
+        alg_bytes = items_per_launch * BYTES_PER_HROT      # algorithmic bytes per HRot x HRots per launch
         ops = kstat["alg_units"] / kstat["launches"]       # modmul-class operations per launch
         hbm_gbps = alg_bytes / avg_s / 1e9
         alu_frac = ops / avg_s / r_mm if r_mm else None
