@@ -199,8 +199,8 @@ def main():
     if args.serial:
         os.environ["CKKS_LANES"] = "1"  # read by the library at its first batched call
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rotation batches shard by ciphertext with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a rotation batch would shard by ciphertext, with no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
